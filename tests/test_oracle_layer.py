@@ -1,0 +1,117 @@
+"""Pins of the oracle's whole layer: torch library reductions of the
+projection/normalisation steps, finite differences of the backward,
+layer-level invariants of the mask, and the probe score helper."""
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from mtgr_inputs import config_inputs, make_batch_from_lengths, make_layer_params
+from oracle import mtgr_oracle as orc
+
+EPS = 1e-5
+
+
+def _tiny(seed=0, bias=True, d=16, H=2, lengths=((2, 5, 3, 3), (1, 4, 2, 2))):
+    rng = np.random.default_rng(seed)
+    batch = make_batch_from_lengths(list(lengths), rng, ts_max=10)
+    p = make_layer_params(d, H, rng, "normal0.02", bias)
+    for name in ("W_uqkv", "b_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o", "b_o"):
+        if getattr(p, name) is not None:
+            setattr(p, name, getattr(p, name).astype(np.float64))
+    p.W_uqkv *= 20  # larger weights so that every term carries weight
+    p.W_o *= 20
+    x = rng.normal(0, 1, size=(batch.T, d))
+    return batch, p, x
+
+
+def test_projection_steps_match_torch_functional():
+    batch, p, x = _tiny()
+    _, saved = orc.layer_fwd(p, x, batch.offsets, batch.group_ids, batch.timestamps, 1.0, 0.1, EPS)
+    xt = torch.from_numpy(x)
+    g = torch.from_numpy(batch.group_ids.astype(np.int64))
+    xhat = torch.stack([F.layer_norm(xt[i], (x.shape[1],), torch.from_numpy(p.gamma1[g[i]]).double(),
+                                     torch.from_numpy(p.beta1[g[i]]).double(), eps=EPS)
+                        for i in range(batch.T)])
+    np.testing.assert_allclose(saved["xhat"], xhat.numpy(), rtol=1e-12, atol=1e-13)
+    z = F.linear(xhat, torch.from_numpy(p.W_uqkv).double(), torch.from_numpy(p.b_uqkv).double())
+    np.testing.assert_allclose(saved["z"], z.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(saved["uqkv"], F.silu(z).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_layer_bwd_matches_finite_differences():
+    batch, p, x = _tiny(seed=1)
+    args = (batch.offsets, batch.group_ids, batch.timestamps, 1.0, 0.1)
+    R = np.random.default_rng(2).normal(size=x.shape)
+    x_out, saved = orc.layer_fwd(p, x, *args, EPS)
+    dx, grads = orc.layer_bwd(p, x, saved, R, *args)
+
+    def loss(pp, xx):
+        return float((orc.layer_fwd(pp, xx, *args, EPS)[0] * R).sum())
+
+    h = 1e-6
+    pick = np.random.default_rng(3)
+    # input coordinates
+    for _ in range(40):
+        i, j = pick.integers(batch.T), pick.integers(x.shape[1])
+        xa, xb = x.copy(), x.copy()
+        xa[i, j] += h
+        xb[i, j] -= h
+        fd = (loss(p, xa) - loss(p, xb)) / (2 * h)
+        assert abs(fd - dx[i, j]) <= 1e-6 * max(1.0, abs(fd)), ("x", i, j, fd, dx[i, j])
+    # parameter coordinates
+    for name in ("W_uqkv", "b_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o", "b_o"):
+        arr = getattr(p, name)
+        for _ in range(20):
+            idx = tuple(int(pick.integers(s)) for s in arr.shape)
+            orig = arr[idx]
+            arr[idx] = orig + h
+            lp = loss(p, x)
+            arr[idx] = orig - h
+            lm = loss(p, x)
+            arr[idx] = orig
+            fd = (lp - lm) / (2 * h)
+            got = grads[name][idx]
+            assert abs(fd - got) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, got)
+
+
+def test_layer_candidate_and_static_invariants():
+    batch, p, x = _tiny(seed=4, lengths=((2, 6, 4, 4),))
+    args = (batch.offsets, batch.group_ids, batch.timestamps, 1.0, 0.1)
+    y, _ = orc.layer_fwd(p, x, *args, EPS)
+    c0 = 12
+    x2 = x.copy()
+    x2[c0 + 1:] += np.random.default_rng(5).normal(size=x2[c0 + 1:].shape)
+    y2, _ = orc.layer_fwd(p, x2, *args, EPS)
+    np.testing.assert_allclose(y2[c0], y[c0], rtol=1e-13, atol=1e-14)
+    x3 = x.copy()
+    x3[8:] = 0.3
+    y3, _ = orc.layer_fwd(p, x3, *args, EPS)
+    np.testing.assert_array_equal(y3[:8], y[:8])
+
+
+def test_stack_is_repeated_layers_and_scores():
+    batch, params, x = config_inputs(1)
+    params = params * 2
+    ref = x.astype(np.float64)
+    for pp in params:
+        ref, _ = orc.layer_fwd(pp, ref, batch.offsets, batch.group_ids, batch.timestamps, 1.0,
+                               1.0 / batch.max_len)
+    got = orc.stack_fwd(params, x, batch.offsets, batch.group_ids, batch.timestamps, 1.0,
+                        1.0 / batch.max_len)
+    np.testing.assert_array_equal(got, ref)
+    w = np.random.default_rng(0).normal(size=x.shape[1])
+    s = orc.candidate_scores(got, batch.group_ids, w)
+    want = torch.sigmoid(torch.from_numpy(got[batch.group_ids == 3]) @ torch.from_numpy(w)).numpy()
+    np.testing.assert_allclose(s, want, rtol=1e-14)
+
+
+def test_selected_users_match_full_batch():
+    batch, params, x = config_inputs(1)
+    p = params[0]
+    args = (1.0, 1.0 / batch.max_len)
+    full, _ = orc.layer_fwd(p, x, batch.offsets, batch.group_ids, batch.timestamps, *args)
+    off, g, t, xs, rows = orc.select_users(batch.offsets, batch.group_ids, batch.timestamps, x, [3, 1])
+    part, _ = orc.layer_fwd(p, xs, off, g, t, *args)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-13, atol=1e-15)
