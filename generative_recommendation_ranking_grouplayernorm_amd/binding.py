@@ -1,0 +1,250 @@
+"""ctypes binding of libmtgr.so: the C ABI of include/mtgr.h, same names.
+
+Argument marshalling only: tensors are passed as device pointers plus sizes,
+every computation runs in the library's HIP kernels.  PyTorch provides device
+memory and streams.  There is no fallback: if the library is missing or was
+not built, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmtgr.so")
+
+MTGR_F32, MTGR_BF16, MTGR_F16 = 0, 1, 2
+OP_PREP, OP_GLN_FWD, OP_GLN_BWD, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD = range(7)
+
+_DT = {torch.float32: MTGR_F32, torch.bfloat16: MTGR_BF16, torch.float16: MTGR_F16}
+
+EXPORTED = (
+    "mtgr_version", "mtgr_status_string", "mtgr_workspace_size", "mtgr_jagged_prep",
+    "mtgr_group_layernorm", "mtgr_group_layernorm_bwd", "mtgr_hstu_attn_fwd", "mtgr_hstu_attn_bwd",
+    "mtgr_hstu_layer_fwd", "mtgr_hstu_layer_bwd",
+)
+
+
+class MtgrError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({_status_text(status)})")
+
+
+class LayerParams(ctypes.Structure):
+    _fields_ = [("W_uqkv", ctypes.c_void_p), ("b_uqkv", ctypes.c_void_p),
+                ("gamma1", ctypes.c_void_p), ("beta1", ctypes.c_void_p),
+                ("gamma2", ctypes.c_void_p), ("beta2", ctypes.c_void_p),
+                ("W_o", ctypes.c_void_p), ("b_o", ctypes.c_void_p),
+                ("d", ctypes.c_int32), ("H", ctypes.c_int32), ("dh", ctypes.c_int32),
+                ("G", ctypes.c_int32), ("eps", ctypes.c_float), ("alpha", ctypes.c_float)]
+
+
+class LayerSaved(ctypes.Structure):
+    _fields_ = [("xhat", ctypes.c_void_p), ("mean1", ctypes.c_void_p), ("rstd1", ctypes.c_void_p),
+                ("z", ctypes.c_void_p), ("uqkv", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("mean2", ctypes.c_void_p), ("rstd2", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [("W_uqkv", ctypes.c_void_p), ("b_uqkv", ctypes.c_void_p),
+                ("gamma1", ctypes.c_void_p), ("beta1", ctypes.c_void_p),
+                ("gamma2", ctypes.c_void_p), ("beta2", ctypes.c_void_p),
+                ("W_o", ctypes.c_void_p), ("b_o", ctypes.c_void_p)]
+
+
+class LayerBwdExtras(ctypes.Structure):
+    _fields_ = [("d_uqkv", ctypes.c_void_p), ("d_o", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmtgr.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"{path} not found: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "mtgr_version": ([], ctypes.c_char_p),
+        "mtgr_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "mtgr_workspace_size": ([ctypes.c_int, I32, I64, I32, I32, ctypes.c_int], SZ),
+        "mtgr_jagged_prep": ([P, P, I32, I64, P, P, SZ, P], ctypes.c_int),
+        "mtgr_group_layernorm": ([P, P, P, P, P, I64, I32, I32, F, ctypes.c_int, P, P, P], ctypes.c_int),
+        "mtgr_group_layernorm_bwd": ([P, P, P, P, P, P, I64, I32, I32, ctypes.c_int, P, P, P, P, SZ, P],
+                                     ctypes.c_int),
+        "mtgr_hstu_attn_fwd": ([P, P, P, I64, P, I64, P, P, P, I32, I64, I32, I32, F, F, ctypes.c_int, P, SZ, P],
+                               ctypes.c_int),
+        "mtgr_hstu_attn_bwd": ([P, P, P, I64, P, I64, P, P, P, I64, P, P, P, I32, I64, I32, I32, F, F,
+                                ctypes.c_int, P, SZ, P], ctypes.c_int),
+        "mtgr_hstu_layer_fwd": ([ctypes.POINTER(LayerParams), P, P, ctypes.POINTER(LayerSaved), P, P, P, I32,
+                                 I64, F, ctypes.c_int, P, SZ, P], ctypes.c_int),
+        "mtgr_hstu_layer_bwd": ([ctypes.POINTER(LayerParams), P, ctypes.POINTER(LayerSaved), P, P,
+                                 ctypes.POINTER(LayerGrads), ctypes.POINTER(LayerBwdExtras), P, P, P, I32, I64,
+                                 F, ctypes.c_int, P, SZ, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load_library().mtgr_status_string(status).decode()
+    except OSError:
+        return "library not loaded"
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MtgrError(fn, status)
+
+
+def _p(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    return _DT[dtype]
+
+
+def _ld(t: torch.Tensor) -> int:
+    assert t.dim() == 2 and t.stride(1) == 1, "row-major [rows, cols] view expected"
+    return t.stride(0)
+
+
+# ---------------------------------------------------------------------------
+def mtgr_version() -> str:
+    return load_library().mtgr_version().decode()
+
+
+def mtgr_status_string(status: int) -> str:
+    return load_library().mtgr_status_string(status).decode()
+
+
+def mtgr_workspace_size(op: int, B: int, T: int, d: int, H: int, dtype: torch.dtype) -> int:
+    return int(load_library().mtgr_workspace_size(op, B, T, d, H, dtype_code(dtype)))
+
+
+def workspace(op: int, B: int, T: int, d: int, H: int, dtype: torch.dtype, device="cuda") -> torch.Tensor:
+    """A byte buffer of the size ``op`` needs (allocation through torch)."""
+    n = mtgr_workspace_size(op, B, T, d, H, dtype)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mtgr_jagged_prep(offsets, group_ids, seg, stream=None) -> None:
+    B = offsets.numel() - 1
+    T = group_ids.numel()
+    _check("mtgr_jagged_prep", load_library().mtgr_jagged_prep(
+        _p(offsets), _p(group_ids), B, T, _p(seg), None, 0, _stream(stream)))
+
+
+def mtgr_group_layernorm(x, y, gamma, beta, group_ids, eps, mean_out=None, rstd_out=None, stream=None) -> None:
+    T, d = x.shape
+    G = gamma.shape[0]
+    _check("mtgr_group_layernorm", load_library().mtgr_group_layernorm(
+        _p(x), _p(y), _p(gamma), _p(beta), _p(group_ids), T, d, G, eps, dtype_code(x.dtype),
+        _p(mean_out), _p(rstd_out), _stream(stream)))
+
+
+def mtgr_group_layernorm_bwd(dy, x, mean, rstd, gamma, group_ids, dx, dgamma, dbeta, ws, stream=None) -> None:
+    T, d = x.shape
+    G = gamma.shape[0]
+    _check("mtgr_group_layernorm_bwd", load_library().mtgr_group_layernorm_bwd(
+        _p(dy), _p(x), _p(mean), _p(rstd), _p(gamma), _p(group_ids), T, d, G, dtype_code(x.dtype),
+        _p(dx), _p(dgamma), _p(dbeta), _p(ws), ws.numel(), _stream(stream)))
+
+
+def mtgr_hstu_attn_fwd(q, k, v, o, offsets, group_ids, timestamps, H, dh, alpha, attn_scale, ws,
+                       stream=None) -> None:
+    B = offsets.numel() - 1
+    T = q.shape[0]
+    assert _ld(q) == _ld(k) == _ld(v)
+    _check("mtgr_hstu_attn_fwd", load_library().mtgr_hstu_attn_fwd(
+        _p(q), _p(k), _p(v), _ld(q), _p(o), _ld(o), _p(offsets), _p(group_ids), _p(timestamps), B, T, H, dh,
+        alpha, attn_scale, dtype_code(q.dtype), _p(ws), ws.numel(), _stream(stream)))
+
+
+def mtgr_hstu_attn_bwd(q, k, v, d_o, dq, dk, dv, offsets, group_ids, timestamps, H, dh, alpha, attn_scale, ws,
+                       stream=None) -> None:
+    B = offsets.numel() - 1
+    T = q.shape[0]
+    assert _ld(q) == _ld(k) == _ld(v) and _ld(dq) == _ld(dk) == _ld(dv)
+    _check("mtgr_hstu_attn_bwd", load_library().mtgr_hstu_attn_bwd(
+        _p(q), _p(k), _p(v), _ld(q), _p(d_o), _ld(d_o), _p(dq), _p(dk), _p(dv), _ld(dq), _p(offsets),
+        _p(group_ids), _p(timestamps), B, T, H, dh, alpha, attn_scale, dtype_code(q.dtype), _p(ws), ws.numel(),
+        _stream(stream)))
+
+
+def make_params(p: Dict[str, torch.Tensor], H: int, eps: float = 1e-5, alpha: float = 1.0) -> LayerParams:
+    d = p["W_o"].shape[0]
+    return LayerParams(_p(p["W_uqkv"]), _p(p.get("b_uqkv")), _p(p["gamma1"]), _p(p["beta1"]),
+                       _p(p["gamma2"]), _p(p["beta2"]), _p(p["W_o"]), _p(p.get("b_o")),
+                       d, H, d // H, p["gamma1"].shape[0], eps, alpha)
+
+
+def make_saved(s: Dict[str, torch.Tensor]) -> LayerSaved:
+    return LayerSaved(*(_p(s[k]) for k in ("xhat", "mean1", "rstd1", "z", "uqkv", "o", "mean2", "rstd2", "y")))
+
+
+def alloc_saved(T: int, d: int, dtype: torch.dtype, device="cuda") -> Dict[str, torch.Tensor]:
+    f = dict(dtype=dtype, device=device)
+    s = dict(dtype=torch.float32, device=device)
+    return dict(xhat=torch.empty(T, d, **f), mean1=torch.empty(T, **s), rstd1=torch.empty(T, **s),
+                z=torch.empty(T, 4 * d, **f), uqkv=torch.empty(T, 4 * d, **f), o=torch.empty(T, d, **f),
+                mean2=torch.empty(T, **s), rstd2=torch.empty(T, **s), y=torch.empty(T, d, **f))
+
+
+def alloc_grads(d: int, G: int, bias: bool, device="cuda") -> Dict[str, torch.Tensor]:
+    f = dict(dtype=torch.float32, device=device)
+    g = dict(W_uqkv=torch.empty(4 * d, d, **f), gamma1=torch.empty(G, d, **f), beta1=torch.empty(G, d, **f),
+             gamma2=torch.empty(G, d, **f), beta2=torch.empty(G, d, **f), W_o=torch.empty(d, d, **f))
+    if bias:
+        g["b_uqkv"] = torch.empty(4 * d, **f)
+        g["b_o"] = torch.empty(d, **f)
+    return g
+
+
+def mtgr_hstu_layer_fwd(params: LayerParams, x_in, x_out, saved: Optional[LayerSaved], offsets, group_ids,
+                        timestamps, attn_scale, ws, stream=None) -> None:
+    B = offsets.numel() - 1
+    T = x_in.shape[0]
+    _check("mtgr_hstu_layer_fwd", load_library().mtgr_hstu_layer_fwd(
+        ctypes.byref(params), _p(x_in), _p(x_out), ctypes.byref(saved) if saved is not None else None,
+        _p(offsets), _p(group_ids), _p(timestamps), B, T, attn_scale, dtype_code(x_in.dtype), _p(ws),
+        ws.numel(), _stream(stream)))
+
+
+def mtgr_hstu_layer_bwd(params: LayerParams, x_in, saved: LayerSaved, dx_out, dx_in, grads: Dict[str, torch.Tensor],
+                        offsets, group_ids, timestamps, attn_scale, ws, extras: Optional[Dict] = None,
+                        stream=None) -> None:
+    B = offsets.numel() - 1
+    T = x_in.shape[0]
+    g = LayerGrads(_p(grads["W_uqkv"]), _p(grads.get("b_uqkv")), _p(grads["gamma1"]), _p(grads["beta1"]),
+                   _p(grads["gamma2"]), _p(grads["beta2"]), _p(grads["W_o"]), _p(grads.get("b_o")))
+    ex = None
+    if extras is not None:
+        ex = ctypes.byref(LayerBwdExtras(_p(extras.get("d_uqkv")), _p(extras.get("d_o"))))
+    _check("mtgr_hstu_layer_bwd", load_library().mtgr_hstu_layer_bwd(
+        ctypes.byref(params), _p(x_in), ctypes.byref(saved), _p(dx_out), _p(dx_in), ctypes.byref(g), ex,
+        _p(offsets), _p(group_ids), _p(timestamps), B, T, attn_scale, dtype_code(x_in.dtype), _p(ws),
+        ws.numel(), _stream(stream)))

@@ -1,0 +1,397 @@
+// C ABI of the library: argument validation, workspace carving and the
+// launch sequence of each entry point (declared in include/mtgr.h).
+#include <stdlib.h>
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace mtgr;
+
+namespace {
+
+constexpr int kMaxG = 8;
+
+inline hipStream_t S(mtgr_stream_t s) { return (hipStream_t)s; }
+
+inline size_t elt(int dt) { return dt == MTGR_F32 ? 4 : 2; }
+
+inline bool dt_ok(int dt) { return dt == MTGR_F32 || dt == MTGR_BF16 || dt == MTGR_F16; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Row strides and base pointers must allow 16-byte vector access.
+inline bool vec_ok(const void* p, int64_t ld, int dt) {
+  if (!p) return true;
+  return aligned16(p) && (ld * (int64_t)elt(dt)) % 16 == 0;
+}
+
+bool attn_shape_ok(int dt, int dh) {
+  if (dt == MTGR_F32) return dh == 16 || dh == 32 || dh == 64 || dh == 128;
+  return dh == 64 || dh == 128;
+}
+
+size_t attn_ws(int B, int64_t T) { return prep_workspace_bytes(B, T, ATTN_TILE_ROWS); }
+
+// Carve a workspace sequentially.
+struct Carver {
+  char* p;
+  size_t left;
+  bool ok = true;
+  void* take(size_t n) {
+    n = align_up(n, 256);
+    if (n > left) { ok = false; return nullptr; }
+    void* r = p;
+    p += n;
+    left -= n;
+    return r;
+  }
+};
+
+size_t layer_fwd_ws(int B, int64_t T, int d, int dt) {
+  const size_t e = elt(dt);
+  size_t n = align_up(attn_ws(B, T), 256);
+  n += align_up((size_t)T * d * e, 256);       // xhat, then y
+  n += align_up((size_t)T * 4 * d * e, 256);   // uqkv
+  n += align_up((size_t)T * d * e, 256);       // o
+  return n;
+}
+
+size_t layer_bwd_ws(int B, int64_t T, int d, int dt) {
+  const size_t e = elt(dt);
+  size_t n = align_up(attn_ws(B, T), 256);
+  n += align_up((size_t)T * d * e, 256);       // dy, then dxhat
+  n += align_up((size_t)T * d * e, 256);       // d_o
+  n += align_up((size_t)T * 4 * d * e, 256);   // dz
+  size_t r = gln_bwd_workspace_bytes(T, d, kMaxG);
+  size_t c = colsum_workspace_bytes(T, 4 * d);
+  n += align_up(r > c ? r : c, 256);
+  return n;
+}
+
+bool jagged_ok(const int32_t* offsets, const uint8_t* g, const int64_t* ts, int32_t B, int64_t T) {
+  if (B < 0 || T < 0 || T > INT32_MAX) return false;
+  if (B > 0 && !offsets) return false;
+  if (T > 0 && (!g || !ts)) return false;
+  return true;
+}
+
+int splits_for(int M, int N, int K) {
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int s = (512 + tiles - 1) / tiles;
+  const int maxs = K / 512 > 0 ? K / 512 : 1;
+  if (s > maxs) s = maxs;
+  return s < 1 ? 1 : s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mtgr_version(void) { return "mtgr-hstu 0.1.0 gfx950"; }
+
+const char* mtgr_status_string(int status) {
+  switch (status) {
+    case MTGR_OK: return "ok";
+    case MTGR_ERR_INVALID_ARG: return "invalid argument";
+    case MTGR_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case MTGR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MTGR_ERR_HIP: return "HIP launch error";
+    case MTGR_ERR_VALIDATION: return "jagged metadata failed validation";
+    default: return "unknown status";
+  }
+}
+
+size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t d, int32_t H, int dt) {
+  (void)H;
+  if (B < 0 || T < 0 || d < 0 || !dt_ok(dt)) return 0;
+  switch (op) {
+    case MTGR_OP_PREP: return 0;
+    case MTGR_OP_GLN_FWD: return 0;
+    case MTGR_OP_GLN_BWD: return gln_bwd_workspace_bytes(T, d, kMaxG);
+    case MTGR_OP_ATTN_FWD: return attn_ws(B, T);
+    case MTGR_OP_ATTN_BWD: return attn_ws(B, T);
+    case MTGR_OP_LAYER_FWD: return layer_fwd_ws(B, T, d, dt);
+    case MTGR_OP_LAYER_BWD: return layer_bwd_ws(B, T, d, dt);
+    default: return 0;
+  }
+}
+
+int mtgr_jagged_prep(const int32_t* offsets, const uint8_t* group_ids, int32_t B, int64_t T,
+                     int32_t* seg, void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (B < 0 || T < 0) return MTGR_ERR_INVALID_ARG;
+  if (B == 0) return MTGR_OK;
+  if (!offsets || !seg || (T > 0 && !group_ids)) return MTGR_ERR_INVALID_ARG;
+  return launch_seg_only(offsets, group_ids, B, seg, S(stream));
+}
+
+int mtgr_group_layernorm(const void* x, void* y, const void* gamma, const void* beta,
+                         const uint8_t* group_ids, int64_t T, int32_t d, int32_t G, float eps, int dt,
+                         float* mean_out, float* rstd_out, mtgr_stream_t stream) {
+  if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
+  if (T < 0 || d < 8 || d > 8192 || d % 8 != 0 || G < 1 || G > kMaxG) return MTGR_ERR_INVALID_ARG;
+  if (T == 0) return MTGR_OK;
+  if (!x || !y || !gamma || !beta || !group_ids) return MTGR_ERR_INVALID_ARG;
+  if ((mean_out == nullptr) != (rstd_out == nullptr)) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(x, d, dt) || !vec_ok(y, d, dt) || !vec_ok(gamma, d, dt) || !vec_ok(beta, d, dt))
+    return MTGR_ERR_INVALID_ARG;
+  return launch_gln_fwd(dt, x, d, y, d, gamma, beta, group_ids, T, d, eps, mean_out, rstd_out, nullptr, 0,
+                        S(stream));
+}
+
+int mtgr_group_layernorm_bwd(const void* dy, const void* x, const float* mean, const float* rstd,
+                             const void* gamma, const uint8_t* group_ids, int64_t T, int32_t d, int32_t G,
+                             int dt, void* dx, float* dgamma, float* dbeta, void* workspace,
+                             size_t ws_bytes, mtgr_stream_t stream) {
+  if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
+  if (T < 0 || d < 8 || d > 8192 || d % 8 != 0 || G < 1 || G > kMaxG || G * d > 8192)
+    return MTGR_ERR_INVALID_ARG;
+  if (!dgamma || !dbeta || !gamma) return MTGR_ERR_INVALID_ARG;
+  if (T > 0 && (!dy || !x || !mean || !rstd || !group_ids || !dx)) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(dy, d, dt) || !vec_ok(x, d, dt) || !vec_ok(dx, d, dt) || !vec_ok(gamma, d, dt))
+    return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < gln_bwd_workspace_bytes(T, d, G) || (T > 0 && !workspace))
+    return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  return launch_gln_bwd(dt, dy, d, x, d, mean, rstd, gamma, nullptr, group_ids, T, d, G, dx, d, nullptr, 0,
+                        nullptr, 0, nullptr, 0, nullptr, 0, dgamma, dbeta, workspace, S(stream));
+}
+
+static int attn_common_checks(const void* q, const void* k, const void* v, int64_t ldqkv,
+                              const int32_t* offsets, const uint8_t* g, const int64_t* ts, int32_t B,
+                              int64_t T, int32_t H, int32_t dh, int dt, void* workspace, size_t ws_bytes) {
+  if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
+  if (!attn_shape_ok(dt, dh)) return MTGR_ERR_UNSUPPORTED;
+  if (H < 1 || !jagged_ok(offsets, g, ts, B, T)) return MTGR_ERR_INVALID_ARG;
+  if (ldqkv < (int64_t)H * dh) return MTGR_ERR_INVALID_ARG;
+  if (T > 0 && (!q || !k || !v)) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(q, ldqkv, dt) || !vec_ok(k, ldqkv, dt) || !vec_ok(v, ldqkv, dt)) return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < attn_ws(B, T) || (B > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  return MTGR_OK;
+}
+
+int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv, void* o, int64_t ld_o,
+                       const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
+                       int32_t B, int64_t T, int32_t H, int32_t dh, float alpha, float attn_scale, int dt,
+                       void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
+  int r = attn_common_checks(q, k, v, ld_qkv, offsets, group_ids, timestamps, B, T, H, dh, dt, workspace,
+                             ws_bytes);
+  if (r) return r;
+  if (ld_o < (int64_t)H * dh || (T > 0 && !o) || !vec_ok(o, ld_o, dt)) return MTGR_ERR_INVALID_ARG;
+  if (B == 0 || T == 0) return MTGR_OK;
+  PrepView pv;
+  r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, workspace, S(stream), &pv);
+  if (r) return r;
+  AttnArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.ldqkv = ld_qkv;
+  a.o = o; a.ldo = ld_o;
+  a.ts = timestamps; a.B = B; a.T = T; a.H = H; a.dh = dh; a.alpha = alpha; a.scale = attn_scale;
+  return launch_attn_fwd(dt, a, pv, S(stream));
+}
+
+int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_qkv, const void* d_o,
+                       int64_t ld_do, void* dq, void* dk, void* dv, int64_t ld_dqkv, const int32_t* offsets,
+                       const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T, int32_t H,
+                       int32_t dh, float alpha, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                       mtgr_stream_t stream) {
+  int r = attn_common_checks(q, k, v, ld_qkv, offsets, group_ids, timestamps, B, T, H, dh, dt, workspace,
+                             ws_bytes);
+  if (r) return r;
+  if (ld_do < (int64_t)H * dh || ld_dqkv < (int64_t)H * dh) return MTGR_ERR_INVALID_ARG;
+  if (T > 0 && (!d_o || !dq || !dk || !dv)) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(d_o, ld_do, dt) || !vec_ok(dq, ld_dqkv, dt) || !vec_ok(dk, ld_dqkv, dt) ||
+      !vec_ok(dv, ld_dqkv, dt))
+    return MTGR_ERR_INVALID_ARG;
+  if (B == 0 || T == 0) return MTGR_OK;
+  PrepView pv;
+  r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, workspace, S(stream), &pv);
+  if (r) return r;
+  AttnArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.ldqkv = ld_qkv;
+  a.d_o = d_o; a.lddo = ld_do;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.lddqkv = ld_dqkv;
+  a.ts = timestamps; a.B = B; a.T = T; a.H = H; a.dh = dh; a.alpha = alpha; a.scale = attn_scale;
+  return launch_attn_bwd(dt, a, pv, S(stream));
+}
+
+static int layer_param_checks(const mtgr_layer_params* p, int dt) {
+  if (!p) return MTGR_ERR_INVALID_ARG;
+  if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
+  if (p->H < 1 || p->dh < 1 || p->d != p->H * p->dh || p->G < 1 || p->G > kMaxG) return MTGR_ERR_INVALID_ARG;
+  if (!attn_shape_ok(dt, p->dh)) return MTGR_ERR_UNSUPPORTED;
+  if (p->d % 8 != 0 || p->d > 8192 || p->G * p->d > 8192) return MTGR_ERR_UNSUPPORTED;
+  if (dt != MTGR_F32 && p->d % 64 != 0) return MTGR_ERR_UNSUPPORTED;
+  if (!p->W_uqkv || !p->gamma1 || !p->beta1 || !p->gamma2 || !p->beta2 || !p->W_o) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(p->gamma1, p->d, dt) || !vec_ok(p->beta1, p->d, dt) || !vec_ok(p->gamma2, p->d, dt) ||
+      !vec_ok(p->beta2, p->d, dt) || !vec_ok(p->W_uqkv, p->d, dt) || !vec_ok(p->W_o, p->d, dt))
+    return MTGR_ERR_INVALID_ARG;
+  return MTGR_OK;
+}
+
+int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_out, const mtgr_layer_saved* saved,
+                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                        int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                        mtgr_stream_t stream) {
+  int r = layer_param_checks(p, dt);
+  if (r) return r;
+  if (!jagged_ok(offsets, group_ids, timestamps, B, T)) return MTGR_ERR_INVALID_ARG;
+  const int d = p->d;
+  if (T > 0 && (!x_in || !x_out)) return MTGR_ERR_INVALID_ARG;
+  if (x_in == x_out && T > 0) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(x_in, d, dt) || !vec_ok(x_out, d, dt)) return MTGR_ERR_INVALID_ARG;
+  if (saved && (!saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->z || !saved->uqkv || !saved->o ||
+                !saved->mean2 || !saved->rstd2 || !saved->y))
+    return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < layer_fwd_ws(B, T, d, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  if (T == 0 || B == 0) return MTGR_OK;
+  hipStream_t st = S(stream);
+  const size_t e = elt(dt);
+  Carver cv{(char*)workspace, ws_bytes};
+  void* ws_prep = cv.take(attn_ws(B, T));
+  void* ws_xhat = cv.take((size_t)T * d * e);
+  void* ws_uqkv = cv.take((size_t)T * 4 * d * e);
+  void* ws_o = cv.take((size_t)T * d * e);
+  if (!cv.ok) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  void* xhat = saved ? saved->xhat : ws_xhat;
+  void* uqkv = saved ? saved->uqkv : ws_uqkv;
+  void* o = saved ? saved->o : ws_o;
+  void* y = saved ? saved->y : ws_xhat;  // xhat is dead once the projection has run
+  PrepView pv;
+  r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, ws_prep, st, &pv);
+  if (r) return r;
+  // a2: input group norm
+  r = launch_gln_fwd(dt, x_in, d, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->eps,
+                     saved ? saved->mean1 : nullptr, saved ? saved->rstd1 : nullptr, nullptr, 0, st);
+  if (r) return r;
+  // a3: [U|Q|K|V] = SiLU(xhat W^T + b)
+  GemmEpiArgs ep = {};
+  ep.kind = EPI_BIAS_SILU;
+  ep.C = uqkv; ep.ldc = 4 * d; ep.bias = p->b_uqkv;
+  ep.Z = saved ? saved->z : nullptr; ep.ldz = 4 * d;
+  r = launch_gemm(dt, xhat, d, true, p->W_uqkv, d, true, (int)T, 4 * d, d, ep, 1, st);
+  if (r) return r;
+  // a4: attention
+  const char* base = (const char*)uqkv;
+  AttnArgs a = {};
+  a.q = base + (size_t)d * e; a.k = base + (size_t)2 * d * e; a.v = base + (size_t)3 * d * e;
+  a.ldqkv = 4 * d; a.o = o; a.ldo = d;
+  a.ts = timestamps; a.B = B; a.T = T; a.H = p->H; a.dh = p->dh; a.alpha = p->alpha; a.scale = attn_scale;
+  r = launch_attn_fwd(dt, a, pv, st);
+  if (r) return r;
+  // a5: y = GLN2(o) * U
+  r = launch_gln_fwd(dt, o, d, y, d, p->gamma2, p->beta2, group_ids, T, d, p->eps,
+                     saved ? saved->mean2 : nullptr, saved ? saved->rstd2 : nullptr, uqkv, 4 * d, st);
+  if (r) return r;
+  // a6: x_out = x + y W_o^T + b_o
+  GemmEpiArgs eo = {};
+  eo.kind = EPI_BIAS_RESID;
+  eo.C = x_out; eo.ldc = d; eo.bias = p->b_o; eo.R = x_in; eo.ldr = d;
+  return launch_gemm(dt, y, d, true, p->W_o, d, true, (int)T, d, d, eo, 1, st);
+}
+
+int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr_layer_saved* saved,
+                        const void* dx_out, void* dx_in, const mtgr_layer_grads* grads,
+                        const mtgr_layer_bwd_extras* extras, const int32_t* offsets, const uint8_t* group_ids,
+                        const int64_t* timestamps, int32_t B, int64_t T, float attn_scale, int dt,
+                        void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
+  int r = layer_param_checks(p, dt);
+  if (r) return r;
+  if (!jagged_ok(offsets, group_ids, timestamps, B, T)) return MTGR_ERR_INVALID_ARG;
+  if (!saved || !grads) return MTGR_ERR_INVALID_ARG;
+  if (!grads->W_uqkv || !grads->gamma1 || !grads->beta1 || !grads->gamma2 || !grads->beta2 || !grads->W_o)
+    return MTGR_ERR_INVALID_ARG;
+  const int d = p->d;
+  if (T > 0 && (!x_in || !dx_out || !dx_in || !saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->z ||
+                !saved->uqkv || !saved->o || !saved->mean2 || !saved->rstd2 || !saved->y))
+    return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(x_in, d, dt) || !vec_ok(dx_out, d, dt) || !vec_ok(dx_in, d, dt)) return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < layer_bwd_ws(B, T, d, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = S(stream);
+  const int G = p->G;
+  if (T == 0 || B == 0) {
+    r = launch_fill_f32(grads->W_uqkv, (int64_t)4 * d * d, 0.f, st);
+    if (!r) r = launch_fill_f32(grads->W_o, (int64_t)d * d, 0.f, st);
+    if (!r) r = launch_fill_f32(grads->gamma1, (int64_t)G * d, 0.f, st);
+    if (!r) r = launch_fill_f32(grads->beta1, (int64_t)G * d, 0.f, st);
+    if (!r) r = launch_fill_f32(grads->gamma2, (int64_t)G * d, 0.f, st);
+    if (!r) r = launch_fill_f32(grads->beta2, (int64_t)G * d, 0.f, st);
+    if (!r && grads->b_uqkv) r = launch_fill_f32(grads->b_uqkv, (int64_t)4 * d, 0.f, st);
+    if (!r && grads->b_o) r = launch_fill_f32(grads->b_o, (int64_t)d, 0.f, st);
+    return r;
+  }
+  const size_t e = elt(dt);
+  Carver cv{(char*)workspace, ws_bytes};
+  void* ws_prep = cv.take(attn_ws(B, T));
+  void* ws_dy = cv.take((size_t)T * d * e);
+  void* ws_do = cv.take((size_t)T * d * e);
+  void* ws_dz = cv.take((size_t)T * 4 * d * e);
+  size_t rbytes = gln_bwd_workspace_bytes(T, d, kMaxG), cbytes = colsum_workspace_bytes(T, 4 * d);
+  void* ws_red = cv.take(rbytes > cbytes ? rbytes : cbytes);
+  if (!cv.ok) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  PrepView pv;
+  r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, ws_prep, st, &pv);
+  if (r) return r;
+  const bool want_dact = extras && extras->d_uqkv;
+  void* dO = (extras && extras->d_o) ? extras->d_o : ws_do;
+  // gradients w.r.t. SiLU(z) go to the caller's buffer when asked for,
+  // otherwise straight into dz with SiLU' applied by the producers
+  void* dact = want_dact ? extras->d_uqkv : ws_dz;
+  const char* zb = (const char*)saved->z;
+  const char* ub = (const char*)saved->uqkv;
+  char* db = (char*)dact;
+  // a6 backward: dy = dx_out W_o ; dW_o = dx_out^T y ; db_o = colsum(dx_out)
+  GemmEpiArgs ep = {};
+  ep.kind = EPI_STORE; ep.C = ws_dy; ep.ldc = d;
+  r = launch_gemm(dt, dx_out, d, true, p->W_o, d, false, (int)T, d, d, ep, 1, st);
+  if (r) return r;
+  GemmEpiArgs ew = {};
+  ew.kind = EPI_F32_ATOMIC; ew.C = grads->W_o; ew.ldc = d;
+  r = launch_gemm(dt, dx_out, d, false, saved->y, d, false, d, d, (int)T, ew, splits_for(d, d, (int)T), st);
+  if (r) return r;
+  if (grads->b_o) {
+    r = launch_colsum(dt, dx_out, d, T, d, grads->b_o, ws_red, st);
+    if (r) return r;
+  }
+  // a5 backward: dU = dy * GLN2(o) [* SiLU'(z_u)], dO = GLN2'(dy * U)
+  r = launch_gln_bwd(dt, ws_dy, d, saved->o, d, saved->mean2, saved->rstd2, p->gamma2, p->beta2, group_ids, T,
+                     d, G, dO, d, nullptr, 0, ub, 4 * d, db, 4 * d, want_dact ? nullptr : zb, 4 * d,
+                     grads->gamma2, grads->beta2, ws_red, st);
+  if (r) return r;
+  // a7: attention backward into the Q, K, V blocks
+  AttnArgs a = {};
+  a.q = ub + (size_t)d * e; a.k = ub + (size_t)2 * d * e; a.v = ub + (size_t)3 * d * e; a.ldqkv = 4 * d;
+  a.d_o = dO; a.lddo = d;
+  a.dq = db + (size_t)d * e; a.dk = db + (size_t)2 * d * e; a.dv = db + (size_t)3 * d * e; a.lddqkv = 4 * d;
+  if (!want_dact) {
+    a.zq = zb + (size_t)d * e; a.zk = zb + (size_t)2 * d * e; a.zv = zb + (size_t)3 * d * e; a.ldz = 4 * d;
+  }
+  a.ts = timestamps; a.B = B; a.T = T; a.H = p->H; a.dh = p->dh; a.alpha = p->alpha; a.scale = attn_scale;
+  r = launch_attn_bwd(dt, a, pv, st);
+  if (r) return r;
+  if (want_dact) {
+    if (hipMemcpyAsync(ws_dz, dact, (size_t)T * 4 * d * e, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return MTGR_ERR_HIP;
+    r = launch_silu_grad_mul(dt, ws_dz, 4 * d, saved->z, 4 * d, T, 4 * d, st);
+    if (r) return r;
+  }
+  // a3 backward: dxhat = dz W_uqkv ; dW_uqkv = dz^T xhat ; db_uqkv = colsum(dz)
+  GemmEpiArgs ex = {};
+  ex.kind = EPI_STORE; ex.C = ws_dy; ex.ldc = d;
+  r = launch_gemm(dt, ws_dz, 4 * d, true, p->W_uqkv, d, false, (int)T, d, 4 * d, ex, 1, st);
+  if (r) return r;
+  GemmEpiArgs eu = {};
+  eu.kind = EPI_F32_ATOMIC; eu.C = grads->W_uqkv; eu.ldc = d;
+  r = launch_gemm(dt, ws_dz, 4 * d, false, saved->xhat, d, false, 4 * d, d, (int)T, eu,
+                  splits_for(4 * d, d, (int)T), st);
+  if (r) return r;
+  if (grads->b_uqkv) {
+    r = launch_colsum(dt, ws_dz, 4 * d, T, 4 * d, grads->b_uqkv, ws_red, st);
+    if (r) return r;
+  }
+  // a2 backward with the residual: dx = GLN1'(dxhat) + dx_out
+  return launch_gln_bwd(dt, ws_dy, d, x_in, d, saved->mean1, saved->rstd1, p->gamma1, p->beta1, group_ids, T, d,
+                        G, dx_in, d, dx_out, d, nullptr, 0, nullptr, 0, nullptr, 0, grads->gamma1, grads->beta1,
+                        ws_red, st);
+}
+
+}  // extern "C"

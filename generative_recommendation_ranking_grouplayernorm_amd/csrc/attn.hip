@@ -1,0 +1,689 @@
+// a4 / a7: jagged SiLU attention under MTGR's dynamic mask, forward and
+// backward.
+//
+// Per user b and head h:  O_i = c * sum_j M_ij * SiLU(alpha <q_i, k_j>) v_j,
+// no softmax (marovi summary, Métodos; paper-daily 模型怎么搭).  Mask rules
+// (fun-rec 7.3.4 rules 1-3; blog section 9): U/S keys are visible to every
+// token; a real-time key j is visible to a real-time or candidate query i
+// when t_j < t_i, and to itself; a candidate key is visible only to itself.
+//
+// With the row laid out [U | S | R | C], the mask needs only the segment
+// starts and the timestamps: key tiles entirely inside U+S are full (no
+// per-element test), static-only query tiles stop at the end of S
+// (history -> real-time blocks skipped), candidate keys are visited only by
+// query tiles that contain candidates (candidate x candidate blocks skipped
+// except for the diagonal), and the per-element test runs in registers.
+//
+// bf16 / f16 kernels use MFMA 32x32x16.  The score tile is computed
+// transposed, S^T = K Q^T, so that each lane holds one query and 16 keys:
+// that register layout is directly the A operand of P V (with the K index
+// permuted identically on both operands), so P never leaves registers.
+// V (and K, Q, dO in the backward) are read as B operands with the LDS
+// transpose load.  The backward recomputes S; dK/dV are accumulated per
+// key tile (key-major kernel) and dQ per query tile (query-major kernel), so
+// no atomics are needed.
+#include "kernels.h"
+
+namespace mtgr {
+
+__device__ __forceinline__ float silu_grad_from(float s, float sg) { return sg * (1.0f + s * (1.0f - sg)); }
+
+// Visibility of key kj for query qi inside one user, both absolute token
+// indices; s_end = start of R, r_end = start of C, hi = end of the row.
+__device__ __forceinline__ bool mask_visible(int qi, int kj, int s_end, int r_end, int hi, int64_t tq,
+                                             const int64_t* __restrict__ ts) {
+  if (kj < s_end) return true;                                   // U / S key
+  if (kj < r_end) return qi >= s_end && (ts[kj] < tq || kj == qi);  // real-time key
+  return kj == qi && kj < hi;                                    // candidate key
+}
+
+// Key range a query tile [q0, q_last] needs: static queries stop at the end
+// of S, real-time queries at the end of R, candidates at themselves.
+__device__ __forceinline__ int key_end_for(int q_last, int s_end, int r_end) {
+  if (q_last < s_end) return s_end;
+  if (q_last < r_end) return r_end;
+  return q_last + 1;
+}
+
+constexpr int A_BQ = 128;  // queries per forward / dQ workgroup (4 waves x 32)
+constexpr int A_BK = 64;   // keys per LDS tile (forward / dQ)
+constexpr int A_BKW = 128; // keys per dK/dV workgroup (4 waves x 32)
+constexpr int A_BQB = 64;  // queries per LDS tile (dK/dV)
+
+template <int DH> struct AttnPitch {
+  static constexpr int B128 = DH + 8;   // rows read 16 bytes per lane
+  static constexpr int TR = DH + 16;    // rows read with the transpose load
+};
+
+// Load a [64 x DH] tile (rows r0.., columns col0..) into registers; rows at or
+// beyond rlim read as zero.
+template <int DH>
+__device__ __forceinline__ void tile_gload(uint4* r, const uint16_t* __restrict__ P, int64_t ld, int r0,
+                                           int rlim, int col0, int tid) {
+  constexpr int CPR = DH / 8;                 // 16-byte chunks per row
+  constexpr int CH = 64 * CPR / 256;          // chunks per thread
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c / CPR, col = (c % CPR) * 8;
+    const int gr = r0 + row;
+    r[i] = gr < rlim ? *(const uint4*)(P + (int64_t)gr * ld + col0 + col) : make_uint4(0, 0, 0, 0);
+  }
+}
+template <int DH, int PITCH>
+__device__ __forceinline__ void tile_swrite(uint16_t* s, const uint4* r, int tid) {
+  constexpr int CPR = DH / 8;
+  constexpr int CH = 64 * CPR / 256;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c / CPR, col = (c % CPR) * 8;
+    *(uint4*)(s + row * PITCH + col) = r[i];
+  }
+}
+
+// B operand (column = l32 of a 32-wide column block at col0, 16 K rows
+// starting at k16 with the permuted order) read with the transpose load
+// from a row-major [rows][PITCH] tile.
+template <int PITCH>
+__device__ __forceinline__ op8 tr_operand(const uint16_t* s, int k16, int col0, int lane) {
+  const int G = lane >> 4, i = lane & 15, g = lane >> 5;
+  const int row = k16 + 4 * g + (i >> 2);
+  const int col = col0 + 16 * (G & 1) + 4 * (i & 3);
+  uint2 lo = lds_read_tr16(s + row * PITCH + col);
+  uint2 hi = lds_read_tr16(s + (row + 8) * PITCH + col);
+  op8 o;
+  o.v[0] = lo.x; o.v[1] = lo.y; o.v[2] = hi.x; o.v[3] = hi.y;
+  return o;
+}
+
+// A operand: row r0 + l32 of a row-major tile, 8 columns at 16*ks + 8*g.
+template <int PITCH>
+__device__ __forceinline__ op8 row_operand(const uint16_t* s, int r0, int ks, int lane) {
+  op8 o;
+  o.v = *(const u32x4_t*)(s + (r0 + (lane & 31)) * PITCH + 16 * ks + 8 * (lane >> 5));
+  return o;
+}
+
+// Pack accumulator values v[t][j] (t = 32-row subtile, j = MFMA output index)
+// into the A operand of k-step u (16 rows 16u..16u+15 of the 64).
+template <typename T>
+__device__ __forceinline__ op8 pack_kstep(const float (&v)[2][16], int u) {
+  const int t = u >> 1, j0 = (u & 1) * 8;
+  op8 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o.v[e] = pack2<T>(v[t][j0 + 2 * e], v[t][j0 + 2 * e + 1]);
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void attn_fwd_mfma(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    int64_t ldqkv, uint16_t* __restrict__ O, int64_t ldo, const int32_t* __restrict__ seg,
+    const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+    float alpha, float scale) {
+  constexpr int KP = AttnPitch<DH>::B128, VP = AttnPitch<DH>::TR;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][A_BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][A_BK * VP];
+  if ((int)blockIdx.x >= *ntiles) return;
+  const int h = blockIdx.y;
+  const int2 te = tiles[blockIdx.x];
+  const int b = te.x, q0 = te.y;
+  const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int q_last = min(q0 + A_BQ, hi) - 1;
+  const int kv_end = key_end_for(q_last, s_end, r_end);
+  const int qi = q0 + wave * 32 + l32;
+  const bool qv = qi < hi;
+  const int64_t tq = qv ? ts[qi] : 0;
+  const int hc = h * DH;
+
+  op8 qop[DH / 16];
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s) {
+    if (qv) qop[s].v = *(const u32x4_t*)(Q + (int64_t)qi * ldqkv + hc + 16 * s + 8 * g);
+    else qop[s].v = u32x4_t{0, 0, 0, 0};
+  }
+  f32x16_t oacc[DH / 32];
+#pragma unroll
+  for (int c = 0; c < DH / 32; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[c][j] = 0.f;
+
+  constexpr int CH = 64 * (DH / 8) / 256;
+  uint4 rk[CH], rv[CH];
+  const int nkt = (kv_end - lo + A_BK - 1) / A_BK;
+  if (nkt > 0) {
+    tile_gload<DH>(rk, K, ldqkv, lo, hi, hc, tid);
+    tile_gload<DH>(rv, V, ldqkv, lo, hi, hc, tid);
+    tile_swrite<DH, KP>(Ks[0], rk, tid);
+    tile_swrite<DH, VP>(Vs[0], rv, tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < nkt; ++it) {
+    const int buf = it & 1, k0 = lo + it * A_BK;
+    const bool more = it + 1 < nkt;
+    if (more) {
+      tile_gload<DH>(rk, K, ldqkv, k0 + A_BK, hi, hc, tid);
+      tile_gload<DH>(rv, V, ldqkv, k0 + A_BK, hi, hc, tid);
+    }
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[t][j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(row_operand<KP>(Ks[buf], t * 32, s, lane), qop[s], sacc[t]);
+    float p[2][16];
+    const bool full = k0 + A_BK <= s_end;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float sv = alpha * sacc[t][j];
+        float pv = sv * fast_sigmoid(sv);
+        if (!full) {
+          const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) pv = 0.f;
+        }
+        p[t][j] = pv;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const op8 pa = pack_kstep<T>(p, u);
+#pragma unroll
+      for (int c = 0; c < DH / 32; ++c) oacc[c] = mfma32<T>(pa, tr_operand<VP>(Vs[buf], 16 * u, c * 32, lane), oacc[c]);
+    }
+    if (more) {
+      tile_swrite<DH, KP>(Ks[buf ^ 1], rk, tid);
+      tile_swrite<DH, VP>(Vs[buf ^ 1], rv, tid);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = 0; c < DH / 32; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = q0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+      if (row < hi) O[(int64_t)row * ldo + hc + c * 32 + l32] = bits16<T>(oacc[c][j] * scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward, query-major: dQ = alpha * c * sum_j [M SiLU'(S) (dO v_j)] k_j
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void attn_bwd_dq_mfma(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dQ,
+    int64_t lddq, const uint16_t* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
+    const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+    float alpha, float scale) {
+  constexpr int KP = AttnPitch<DH>::B128;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][A_BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][A_BK * KP];
+  if ((int)blockIdx.x >= *ntiles) return;
+  const int h = blockIdx.y;
+  const int2 te = tiles[blockIdx.x];
+  const int b = te.x, q0 = te.y;
+  const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int q_last = min(q0 + A_BQ, hi) - 1;
+  const int kv_end = key_end_for(q_last, s_end, r_end);
+  const int qi = q0 + wave * 32 + l32;
+  const bool qv = qi < hi;
+  const int64_t tq = qv ? ts[qi] : 0;
+  const int hc = h * DH;
+
+  op8 qop[DH / 16], dop[DH / 16];
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s) {
+    if (qv) {
+      qop[s].v = *(const u32x4_t*)(Q + (int64_t)qi * ldqkv + hc + 16 * s + 8 * g);
+      dop[s].v = *(const u32x4_t*)(dO + (int64_t)qi * lddo + hc + 16 * s + 8 * g);
+    } else {
+      qop[s].v = u32x4_t{0, 0, 0, 0};
+      dop[s].v = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  f32x16_t acc[DH / 32];
+#pragma unroll
+  for (int c = 0; c < DH / 32; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
+
+  constexpr int CH = 64 * (DH / 8) / 256;
+  uint4 rk[CH], rv[CH];
+  const int nkt = (kv_end - lo + A_BK - 1) / A_BK;
+  if (nkt > 0) {
+    tile_gload<DH>(rk, K, ldqkv, lo, hi, hc, tid);
+    tile_gload<DH>(rv, V, ldqkv, lo, hi, hc, tid);
+    tile_swrite<DH, KP>(Ks[0], rk, tid);
+    tile_swrite<DH, KP>(Vs[0], rv, tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < nkt; ++it) {
+    const int buf = it & 1, k0 = lo + it * A_BK;
+    const bool more = it + 1 < nkt;
+    if (more) {
+      tile_gload<DH>(rk, K, ldqkv, k0 + A_BK, hi, hc, tid);
+      tile_gload<DH>(rv, V, ldqkv, k0 + A_BK, hi, hc, tid);
+    }
+    f32x16_t sacc[2], dacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[t][j] = dacc[t][j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sacc[t] = mfma32<T>(row_operand<KP>(Ks[buf], t * 32, s, lane), qop[s], sacc[t]);
+        dacc[t] = mfma32<T>(row_operand<KP>(Vs[buf], t * 32, s, lane), dop[s], dacc[t]);
+      }
+    float ds[2][16];
+    const bool full = k0 + A_BK <= s_end;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float sv = alpha * sacc[t][j];
+        const float sg = fast_sigmoid(sv);
+        float v = dacc[t][j] * silu_grad_from(sv, sg);
+        if (!full) {
+          const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) v = 0.f;
+        }
+        ds[t][j] = v;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const op8 da = pack_kstep<T>(ds, u);
+#pragma unroll
+      for (int c = 0; c < DH / 32; ++c) acc[c] = mfma32<T>(da, tr_operand<KP>(Ks[buf], 16 * u, c * 32, lane), acc[c]);
+    }
+    if (more) {
+      tile_swrite<DH, KP>(Ks[buf ^ 1], rk, tid);
+      tile_swrite<DH, KP>(Vs[buf ^ 1], rv, tid);
+    }
+    __syncthreads();
+  }
+  const float f = alpha * scale;
+#pragma unroll
+  for (int c = 0; c < DH / 32; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = q0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+      if (row < hi) {
+        float v = acc[c][j] * f;
+        const int col = hc + c * 32 + l32;
+        if (zq) {
+          const float z = from_bits16<T>(zq[(int64_t)row * ldz + col]);
+          v *= silu_grad_from(z, 1.0f / (1.0f + __expf(-z)));
+        }
+        dQ[(int64_t)row * lddq + col] = bits16<T>(v);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward, key-major: dV = c P^T dO, dK = alpha c dS^T Q for 128 keys
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int64_t lddkv, const uint16_t* __restrict__ zk,
+    const uint16_t* __restrict__ zv, int64_t ldz, const int32_t* __restrict__ seg,
+    const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+    float alpha, float scale) {
+  constexpr int QP = AttnPitch<DH>::B128;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][A_BQB * QP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][A_BQB * QP];
+  if ((int)blockIdx.x >= *ntiles) return;
+  const int h = blockIdx.y;
+  const int2 te = tiles[blockIdx.x];
+  const int b = te.x, k0 = te.y;
+  const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int k_last = min(k0 + A_BKW, hi) - 1;
+  int qlo, qhi;
+  if (k0 < s_end) { qlo = lo; qhi = hi; }            // static keys: every query
+  else if (k0 < r_end) { qlo = s_end; qhi = hi; }    // real-time keys: R and C queries
+  else { qlo = k0; qhi = k_last + 1; }               // candidate keys: themselves
+  const int kj = k0 + wave * 32 + l32;
+  const bool kv = kj < hi;
+  const int64_t tk = kv ? ts[kj] : 0;
+  const int hc = h * DH;
+
+  op8 kop[DH / 16], vop[DH / 16];
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s) {
+    if (kv) {
+      kop[s].v = *(const u32x4_t*)(K + (int64_t)kj * ldqkv + hc + 16 * s + 8 * g);
+      vop[s].v = *(const u32x4_t*)(V + (int64_t)kj * ldqkv + hc + 16 * s + 8 * g);
+    } else {
+      kop[s].v = u32x4_t{0, 0, 0, 0};
+      vop[s].v = u32x4_t{0, 0, 0, 0};
+    }
+  }
+  f32x16_t dk[DH / 32], dv[DH / 32];
+#pragma unroll
+  for (int c = 0; c < DH / 32; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dk[c][j] = dv[c][j] = 0.f;
+
+  constexpr int CH = 64 * (DH / 8) / 256;
+  uint4 rq[CH], rd[CH];
+  const int nqt = (qhi - qlo + A_BQB - 1) / A_BQB;
+  if (nqt > 0) {
+    tile_gload<DH>(rq, Q, ldqkv, qlo, qhi, hc, tid);
+    tile_gload<DH>(rd, dO, lddo, qlo, qhi, hc, tid);
+    tile_swrite<DH, QP>(Qs[0], rq, tid);
+    tile_swrite<DH, QP>(Ds[0], rd, tid);
+  }
+  __syncthreads();
+  const bool full = k0 + A_BKW <= s_end;
+  for (int it = 0; it < nqt; ++it) {
+    const int buf = it & 1, q0 = qlo + it * A_BQB;
+    const bool more = it + 1 < nqt;
+    if (more) {
+      tile_gload<DH>(rq, Q, ldqkv, q0 + A_BQB, qhi, hc, tid);
+      tile_gload<DH>(rd, dO, lddo, q0 + A_BQB, qhi, hc, tid);
+    }
+    f32x16_t sacc[2], dacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[t][j] = dacc[t][j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sacc[t] = mfma32<T>(row_operand<QP>(Qs[buf], t * 32, s, lane), kop[s], sacc[t]);
+        dacc[t] = mfma32<T>(row_operand<QP>(Ds[buf], t * 32, s, lane), vop[s], dacc[t]);
+      }
+    float p[2][16], ds[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float sv = alpha * sacc[t][j];
+        const float sg = fast_sigmoid(sv);
+        float pv = sv * sg;
+        float dsv = dacc[t][j] * silu_grad_from(sv, sg);
+        if (!full) {
+          const int qi = q0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          bool vis = qi < qhi && kv;
+          if (vis) {
+            const int64_t tq = ts[qi];
+            if (kj < s_end) vis = true;
+            else if (kj < r_end) vis = qi >= s_end && (tk < tq || kj == qi);
+            else vis = kj == qi;
+          }
+          if (!vis) { pv = 0.f; dsv = 0.f; }
+        }
+        p[t][j] = pv;
+        ds[t][j] = dsv;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const op8 pa = pack_kstep<T>(p, u);
+      const op8 da = pack_kstep<T>(ds, u);
+#pragma unroll
+      for (int c = 0; c < DH / 32; ++c) {
+        dv[c] = mfma32<T>(pa, tr_operand<QP>(Ds[buf], 16 * u, c * 32, lane), dv[c]);
+        dk[c] = mfma32<T>(da, tr_operand<QP>(Qs[buf], 16 * u, c * 32, lane), dk[c]);
+      }
+    }
+    if (more) {
+      tile_swrite<DH, QP>(Qs[buf ^ 1], rq, tid);
+      tile_swrite<DH, QP>(Ds[buf ^ 1], rd, tid);
+    }
+    __syncthreads();
+  }
+  const float fk = alpha * scale, fv = scale;
+#pragma unroll
+  for (int c = 0; c < DH / 32; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = k0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+      if (row < hi) {
+        const int col = hc + c * 32 + l32;
+        float a = dk[c][j] * fk, bv = dv[c][j] * fv;
+        if (zk) {
+          const float z1 = from_bits16<T>(zk[(int64_t)row * ldz + col]);
+          const float z2 = from_bits16<T>(zv[(int64_t)row * ldz + col]);
+          a *= silu_grad_from(z1, 1.0f / (1.0f + __expf(-z1)));
+          bv *= silu_grad_from(z2, 1.0f / (1.0f + __expf(-z2)));
+        }
+        dK[(int64_t)row * lddkv + col] = bits16<T>(a);
+        dV[(int64_t)row * lddkv + col] = bits16<T>(bv);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// f32 kernels: one thread per (token, head), plain loops (parity workloads).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int find_user(const int32_t* __restrict__ seg, int B, int tok) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {  // last user whose start <= tok (skips empty users)
+    int mid = (lo + hi + 1) >> 1;
+    if (seg[mid * 5] <= tok) lo = mid; else hi = mid - 1;
+  }
+  while (lo > 0 && seg[lo * 5 + 4] <= tok) --lo;
+  return lo;
+}
+
+__device__ __forceinline__ float sigmoid_precise(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+template <int DH>
+__global__ void attn_fwd_f32(const float* __restrict__ Q, const float* __restrict__ K,
+                             const float* __restrict__ V, int64_t ldqkv, float* __restrict__ O,
+                             int64_t ldo, const int32_t* __restrict__ seg, int B, int64_t T,
+                             const int64_t* __restrict__ ts, float alpha, float scale) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  const int h = blockIdx.y, hc = h * DH;
+  const int b = find_user(seg, B, (int)i);
+  const int lo = seg[b * 5], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
+  const int qi = (int)i;
+  const int kend = key_end_for(qi, s_end, r_end);
+  const int64_t tq = ts[qi];
+  float q[DH], acc[DH];
+  for (int e = 0; e < DH; ++e) { q[e] = Q[i * ldqkv + hc + e]; acc[e] = 0.f; }
+  for (int kj = lo; kj < kend; ++kj) {
+    if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) continue;
+    float s = 0.f;
+    for (int e = 0; e < DH; ++e) s += q[e] * K[(int64_t)kj * ldqkv + hc + e];
+    s *= alpha;
+    const float p = s * sigmoid_precise(s);
+    for (int e = 0; e < DH; ++e) acc[e] += p * V[(int64_t)kj * ldqkv + hc + e];
+  }
+  for (int e = 0; e < DH; ++e) O[i * ldo + hc + e] = acc[e] * scale;
+}
+
+template <int DH>
+__global__ void attn_bwd_dq_f32(const float* __restrict__ Q, const float* __restrict__ K,
+                                const float* __restrict__ V, int64_t ldqkv, const float* __restrict__ dO,
+                                int64_t lddo, float* __restrict__ dQ, int64_t lddq,
+                                const float* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
+                                int B, int64_t T, const int64_t* __restrict__ ts, float alpha, float scale) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  const int h = blockIdx.y, hc = h * DH;
+  const int b = find_user(seg, B, (int)i);
+  const int lo = seg[b * 5], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
+  const int qi = (int)i;
+  const int kend = key_end_for(qi, s_end, r_end);
+  const int64_t tq = ts[qi];
+  float q[DH], d[DH], acc[DH];
+  for (int e = 0; e < DH; ++e) { q[e] = Q[i * ldqkv + hc + e]; d[e] = dO[i * lddo + hc + e]; acc[e] = 0.f; }
+  for (int kj = lo; kj < kend; ++kj) {
+    if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) continue;
+    float s = 0.f, da = 0.f;
+    for (int e = 0; e < DH; ++e) {
+      s += q[e] * K[(int64_t)kj * ldqkv + hc + e];
+      da += d[e] * V[(int64_t)kj * ldqkv + hc + e];
+    }
+    s *= alpha;
+    const float w = da * silu_grad_from(s, sigmoid_precise(s));
+    for (int e = 0; e < DH; ++e) acc[e] += w * K[(int64_t)kj * ldqkv + hc + e];
+  }
+  for (int e = 0; e < DH; ++e) {
+    float v = acc[e] * alpha * scale;
+    if (zq) {
+      const float z = zq[i * ldz + hc + e];
+      v *= silu_grad_from(z, sigmoid_precise(z));
+    }
+    dQ[i * lddq + hc + e] = v;
+  }
+}
+
+template <int DH>
+__global__ void attn_bwd_dkdv_f32(const float* __restrict__ Q, const float* __restrict__ K,
+                                  const float* __restrict__ V, int64_t ldqkv,
+                                  const float* __restrict__ dO, int64_t lddo, float* __restrict__ dK,
+                                  float* __restrict__ dV, int64_t lddkv, const float* __restrict__ zk,
+                                  const float* __restrict__ zv, int64_t ldz,
+                                  const int32_t* __restrict__ seg, int B, int64_t T,
+                                  const int64_t* __restrict__ ts, float alpha, float scale) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  const int h = blockIdx.y, hc = h * DH;
+  const int b = find_user(seg, B, (int)i);
+  const int lo = seg[b * 5], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
+  const int kj = (int)i;
+  float k[DH], v[DH], ak[DH], av[DH];
+  for (int e = 0; e < DH; ++e) {
+    k[e] = K[i * ldqkv + hc + e];
+    v[e] = V[i * ldqkv + hc + e];
+    ak[e] = av[e] = 0.f;
+  }
+  for (int qi = lo; qi < hi; ++qi) {
+    if (!mask_visible(qi, kj, s_end, r_end, hi, ts[qi], ts)) continue;
+    float s = 0.f, da = 0.f;
+    for (int e = 0; e < DH; ++e) {
+      s += Q[(int64_t)qi * ldqkv + hc + e] * k[e];
+      da += dO[(int64_t)qi * lddo + hc + e] * v[e];
+    }
+    s *= alpha;
+    const float sg = sigmoid_precise(s);
+    const float p = s * sg, w = da * silu_grad_from(s, sg);
+    for (int e = 0; e < DH; ++e) {
+      av[e] += p * dO[(int64_t)qi * lddo + hc + e];
+      ak[e] += w * Q[(int64_t)qi * ldqkv + hc + e];
+    }
+  }
+  for (int e = 0; e < DH; ++e) {
+    float a = ak[e] * alpha * scale, bv = av[e] * scale;
+    if (zk) {
+      const float z1 = zk[i * ldz + hc + e], z2 = zv[i * ldz + hc + e];
+      a *= silu_grad_from(z1, sigmoid_precise(z1));
+      bv *= silu_grad_from(z2, sigmoid_precise(z2));
+    }
+    dK[i * lddkv + hc + e] = a;
+    dV[i * lddkv + hc + e] = bv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+static void fwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
+  dim3 grid((unsigned)pv.max_tiles, a.H);
+  hipLaunchKernelGGL((attn_fwd_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (uint16_t*)a.o, a.ldo, pv.seg,
+                     a.ts, pv.tiles, pv.ntiles, a.alpha, a.scale);
+}
+
+template <typename T, int DH>
+static void bwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
+  dim3 grid((unsigned)pv.max_tiles, a.H);
+  hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (const uint16_t*)a.d_o, a.lddo,
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv, (const uint16_t*)a.zk,
+                     (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.tiles, pv.ntiles, a.alpha, a.scale);
+  hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (const uint16_t*)a.d_o, a.lddo,
+                     (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg, a.ts, pv.tiles,
+                     pv.ntiles, a.alpha, a.scale);
+}
+
+template <int DH>
+static void fwd_f32(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
+  dim3 grid((unsigned)((a.T + 63) / 64), a.H);
+  hipLaunchKernelGGL((attn_fwd_f32<DH>), grid, dim3(64), 0, st, (const float*)a.q, (const float*)a.k,
+                     (const float*)a.v, a.ldqkv, (float*)a.o, a.ldo, pv.seg, a.B, a.T, a.ts, a.alpha, a.scale);
+}
+
+template <int DH>
+static void bwd_f32(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
+  dim3 grid((unsigned)((a.T + 63) / 64), a.H);
+  hipLaunchKernelGGL((attn_bwd_dq_f32<DH>), grid, dim3(64), 0, st, (const float*)a.q, (const float*)a.k,
+                     (const float*)a.v, a.ldqkv, (const float*)a.d_o, a.lddo, (float*)a.dq, a.lddqkv,
+                     (const float*)a.zq, a.ldz, pv.seg, a.B, a.T, a.ts, a.alpha, a.scale);
+  hipLaunchKernelGGL((attn_bwd_dkdv_f32<DH>), grid, dim3(64), 0, st, (const float*)a.q, (const float*)a.k,
+                     (const float*)a.v, a.ldqkv, (const float*)a.d_o, a.lddo, (float*)a.dk, (float*)a.dv,
+                     a.lddqkv, (const float*)a.zk, (const float*)a.zv, a.ldz, pv.seg, a.B, a.T, a.ts,
+                     a.alpha, a.scale);
+}
+
+int launch_attn_fwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t st) {
+  if (a.T <= 0 || a.B <= 0) return MTGR_OK;
+  if (dt == MTGR_BF16) {
+    if (a.dh == 128) fwd_mfma<bf16_t, 128>(a, pv, st);
+    else if (a.dh == 64) fwd_mfma<bf16_t, 64>(a, pv, st);
+    else return MTGR_ERR_UNSUPPORTED;
+  } else if (dt == MTGR_F16) {
+    if (a.dh == 128) fwd_mfma<f16_t, 128>(a, pv, st);
+    else if (a.dh == 64) fwd_mfma<f16_t, 64>(a, pv, st);
+    else return MTGR_ERR_UNSUPPORTED;
+  } else if (dt == MTGR_F32) {
+    switch (a.dh) {
+      case 16: fwd_f32<16>(a, pv, st); break;
+      case 32: fwd_f32<32>(a, pv, st); break;
+      case 64: fwd_f32<64>(a, pv, st); break;
+      case 128: fwd_f32<128>(a, pv, st); break;
+      default: return MTGR_ERR_UNSUPPORTED;
+    }
+  } else {
+    return MTGR_ERR_UNSUPPORTED;
+  }
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+int launch_attn_bwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t st) {
+  if (a.T <= 0 || a.B <= 0) return MTGR_OK;
+  if (dt == MTGR_BF16) {
+    if (a.dh == 128) bwd_mfma<bf16_t, 128>(a, pv, st);
+    else if (a.dh == 64) bwd_mfma<bf16_t, 64>(a, pv, st);
+    else return MTGR_ERR_UNSUPPORTED;
+  } else if (dt == MTGR_F16) {
+    if (a.dh == 128) bwd_mfma<f16_t, 128>(a, pv, st);
+    else if (a.dh == 64) bwd_mfma<f16_t, 64>(a, pv, st);
+    else return MTGR_ERR_UNSUPPORTED;
+  } else if (dt == MTGR_F32) {
+    switch (a.dh) {
+      case 16: bwd_f32<16>(a, pv, st); break;
+      case 32: bwd_f32<32>(a, pv, st); break;
+      case 64: bwd_f32<64>(a, pv, st); break;
+      case 128: bwd_f32<128>(a, pv, st); break;
+      default: return MTGR_ERR_UNSUPPORTED;
+    }
+  } else {
+    return MTGR_ERR_UNSUPPORTED;
+  }
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+}  // namespace mtgr

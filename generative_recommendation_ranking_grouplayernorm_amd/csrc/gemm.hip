@@ -1,0 +1,264 @@
+// GEMMs of the layer: the fused UQKV projection with bias + SiLU in the
+// epilogue (a3; paper-daily 模型怎么搭: one linear layer followed by SiLU gives
+// U, Q, K, V), the output projection with bias + residual (a6), and the
+// backward products (data gradients and fp32 weight gradients).
+//
+// bf16 / f16: 128x128 output tile per 256-thread workgroup, 4 waves in 2x2,
+// each wave 64x64 = 2x2 MFMA 32x32x16 tiles; K staged through LDS 64 deep,
+// double-buffered, one barrier per K step.  Operands stored K-contiguous are
+// read with 16-byte LDS loads; operands stored M/N-contiguous (the transposed
+// products of the backward) are read with gfx950's LDS transpose load, so no
+// operand is ever transposed in memory.
+// f32: a plain LDS-tiled FMA kernel (small parity workloads only).
+#include "kernels.h"
+
+namespace mtgr {
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_apply(const GemmEpiArgs& ep, int m, int n, float acc) {
+  if (EPI == EPI_STORE) {
+    ((T*)ep.C)[(int64_t)m * ep.ldc + n] = from_f32<T>(acc);
+  } else if (EPI == EPI_BIAS_SILU) {
+    float z = acc + (ep.bias ? to_f32(((const T*)ep.bias)[n]) : 0.f);
+    T zr = from_f32<T>(z);
+    if (ep.Z) ((T*)ep.Z)[(int64_t)m * ep.ldz + n] = zr;
+    // SiLU of the stored (rounded) pre-activation, so that forward and
+    // backward see the same z.
+    float zq = to_f32(zr);
+    ((T*)ep.C)[(int64_t)m * ep.ldc + n] = from_f32<T>(silu_f(zq));
+  } else if (EPI == EPI_BIAS_RESID) {
+    float r = acc + (ep.bias ? to_f32(((const T*)ep.bias)[n]) : 0.f) +
+              to_f32(((const T*)ep.R)[(int64_t)m * ep.ldr + n]);
+    ((T*)ep.C)[(int64_t)m * ep.ldc + n] = from_f32<T>(r);
+  } else if (EPI == EPI_F32_STORE) {
+    ((float*)ep.C)[(int64_t)m * ep.ldc + n] = acc;
+  } else {
+    atomicAdd(&((float*)ep.C)[(int64_t)m * ep.ldc + n], acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel
+// ---------------------------------------------------------------------------
+constexpr int G_BM = 128, G_BN = 128, G_BK = 64;
+constexpr int G_KC_PITCH = G_BK + 8;    // K-contiguous tile row pitch (elements)
+constexpr int G_MN_PITCH = G_BM + 16;   // M/N-contiguous tile row pitch (elements)
+constexpr int G_TILE_ELEMS = 9216;      // = 128 * 72 = 64 * 144
+static_assert(G_BM * G_KC_PITCH == G_TILE_ELEMS && G_BK * G_MN_PITCH == G_TILE_ELEMS, "tile size");
+
+template <bool KC>
+__device__ __forceinline__ uint4 gemm_gload(const uint16_t* __restrict__ P, int64_t ld, int r0, int R,
+                                            int k0, int kend, int c) {
+  if (KC) {
+    const int row = c >> 3, kc = (c & 7) * 8;
+    const int r = r0 + row, k = k0 + kc;
+    if (r < R && k < kend) return *(const uint4*)(P + (int64_t)r * ld + k);
+  } else {
+    const int krow = c >> 4, rc = (c & 15) * 8;
+    const int k = k0 + krow, r = r0 + rc;
+    if (k < kend && r < R) return *(const uint4*)(P + (int64_t)k * ld + r);
+  }
+  return make_uint4(0, 0, 0, 0);
+}
+
+template <bool KC>
+__device__ __forceinline__ void gemm_swrite(uint16_t* s, int c, uint4 v) {
+  if (KC) {
+    const int row = c >> 3, kc = (c & 7) * 8;
+    *(uint4*)(s + row * G_KC_PITCH + kc) = v;
+  } else {
+    const int krow = c >> 4, rc = (c & 15) * 8;
+    *(uint4*)(s + krow * G_MN_PITCH + rc) = v;
+  }
+}
+
+// MFMA operand for 32 rows starting at r0 (within the tile), k-step ks.
+template <bool KC>
+__device__ __forceinline__ op8 gemm_operand(const uint16_t* s, int r0, int ks, int lane) {
+  op8 o;
+  if (KC) {
+    const int row = r0 + (lane & 31), kk = ks * 16 + 8 * (lane >> 5);
+    o.v = *(const u32x4_t*)(s + row * G_KC_PITCH + kk);
+  } else {
+    const int G = lane >> 4, i = lane & 15;
+    const int kr = ks * 16 + 8 * (G >> 1) + (i >> 2);
+    const int col = r0 + 16 * (G & 1) + 4 * (i & 3);
+    uint2 lo = lds_read_tr16(s + kr * G_MN_PITCH + col);
+    uint2 hi = lds_read_tr16(s + (kr + 4) * G_MN_PITCH + col);
+    o.v[0] = lo.x; o.v[1] = lo.y; o.v[2] = hi.x; o.v[3] = hi.y;
+  }
+  return o;
+}
+
+template <typename T, bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                        const uint16_t* __restrict__ B, int64_t ldb,
+                                                        int M, int N, int K, int k_per_split,
+                                                        GemmEpiArgs ep) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2 * G_TILE_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * G_BM, n0 = blockIdx.x * G_BN;
+  const int kbeg = blockIdx.z * k_per_split;
+  const int kend = min(K, kbeg + k_per_split);
+  const int nk = kend > kbeg ? (kend - kbeg + G_BK - 1) / G_BK : 0;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[t][u][j] = 0.f;
+
+  uint4 ra[4], rb[4];
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = gemm_gload<AK>(A, lda, m0, M, kbeg, kend, tid + 256 * i);
+      rb[i] = gemm_gload<BKC>(B, ldb, n0, N, kbeg, kend, tid + 256 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gemm_swrite<AK>(smem[0], tid + 256 * i, ra[i]);
+      gemm_swrite<BKC>(smem[0] + G_TILE_ELEMS, tid + 256 * i, rb[i]);
+    }
+  }
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < nk;
+    if (more) {
+      const int kn = kbeg + (it + 1) * G_BK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ra[i] = gemm_gload<AK>(A, lda, m0, M, kn, kend, tid + 256 * i);
+        rb[i] = gemm_gload<BKC>(B, ldb, n0, N, kn, kend, tid + 256 * i);
+      }
+    }
+    const uint16_t* sa = smem[buf];
+    const uint16_t* sb = smem[buf] + G_TILE_ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < G_BK / 16; ++ks) {
+      op8 a[2], b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) a[t] = gemm_operand<AK>(sa, wm * 64 + t * 32, ks, lane);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) b[u] = gemm_operand<BKC>(sb, wn * 64 + u * 32, ks, lane);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[t][u] = mfma32<T>(a[t], b[u], acc[t][u]);
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gemm_swrite<AK>(smem[buf ^ 1], tid + 256 * i, ra[i]);
+        gemm_swrite<BKC>(smem[buf ^ 1] + G_TILE_ELEMS, tid + 256 * i, rb[i]);
+      }
+    }
+    __syncthreads();
+  }
+  if (EPI == EPI_F32_ATOMIC && nk == 0) return;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = m0 + wm * 64 + t * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+        const int n = n0 + wn * 64 + u * 32 + (lane & 31);
+        if (m < M && n < N) epi_apply<T, EPI>(ep, m, n, acc[t][u][j]);
+      }
+}
+
+// ---------------------------------------------------------------------------
+// Plain kernel (f32)
+// ---------------------------------------------------------------------------
+template <typename T, bool AK, bool BKC, int EPI>
+__global__ __launch_bounds__(256) void gemm_simple_kernel(const T* __restrict__ A, int64_t lda,
+                                                          const T* __restrict__ B, int64_t ldb, int M,
+                                                          int N, int K, int k_per_split,
+                                                          GemmEpiArgs ep) {
+  __shared__ float As[16][17], Bs[16][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m = blockIdx.y * 16 + ty, n = blockIdx.x * 16 + tx;
+  const int kbeg = blockIdx.z * k_per_split;
+  const int kend = min(K, kbeg + k_per_split);
+  float acc = 0.f;
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
+    const int am = blockIdx.y * 16 + ty, bn = blockIdx.x * 16 + ty, kk = k0 + tx;
+    float av = 0.f, bv = 0.f;
+    if (am < M && kk < kend) av = to_f32(AK ? A[(int64_t)am * lda + kk] : A[(int64_t)kk * lda + am]);
+    if (bn < N && kk < kend) bv = to_f32(BKC ? B[(int64_t)bn * ldb + kk] : B[(int64_t)kk * ldb + bn]);
+    As[ty][tx] = av;
+    Bs[ty][tx] = bv;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc += As[ty][q] * Bs[tx][q];
+    __syncthreads();
+  }
+  if (EPI == EPI_F32_ATOMIC && kend <= kbeg) return;
+  if (m < M && n < N) epi_apply<T, EPI>(ep, m, n, acc);
+}
+
+template <typename T, bool AK, bool BKC, int EPI>
+static void gemm_launch_t(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K,
+                          int splits, const GemmEpiArgs& ep, hipStream_t st) {
+  int kps = (K + splits - 1) / splits;
+  if constexpr (sizeof(T) == 2) {
+    kps = (kps + G_BK - 1) / G_BK * G_BK;
+    dim3 grid((N + G_BN - 1) / G_BN, (M + G_BM - 1) / G_BM, splits);
+    hipLaunchKernelGGL((gemm_mfma_kernel<T, AK, BKC, EPI>), grid, dim3(256), 0, st, (const uint16_t*)A,
+                       lda, (const uint16_t*)B, ldb, M, N, K, kps, ep);
+  } else {
+    dim3 grid((N + 15) / 16, (M + 15) / 16, splits);
+    hipLaunchKernelGGL((gemm_simple_kernel<T, AK, BKC, EPI>), grid, dim3(256), 0, st, (const T*)A, lda,
+                       (const T*)B, ldb, M, N, K, kps, ep);
+  }
+}
+
+template <typename T, int EPI>
+static void gemm_launch_layout(const void* A, int64_t lda, bool ak, const void* B, int64_t ldb, bool bk,
+                               int M, int N, int K, int splits, const GemmEpiArgs& ep, hipStream_t st) {
+  if (ak && bk) gemm_launch_t<T, true, true, EPI>(A, lda, B, ldb, M, N, K, splits, ep, st);
+  else if (ak && !bk) gemm_launch_t<T, true, false, EPI>(A, lda, B, ldb, M, N, K, splits, ep, st);
+  else if (!ak && !bk) gemm_launch_t<T, false, false, EPI>(A, lda, B, ldb, M, N, K, splits, ep, st);
+  else gemm_launch_t<T, false, true, EPI>(A, lda, B, ldb, M, N, K, splits, ep, st);
+}
+
+template <typename T>
+static void gemm_launch_epi(const void* A, int64_t lda, bool ak, const void* B, int64_t ldb, bool bk,
+                            int M, int N, int K, int splits, const GemmEpiArgs& ep, hipStream_t st) {
+  switch (ep.kind) {
+    case EPI_STORE: gemm_launch_layout<T, EPI_STORE>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
+    case EPI_BIAS_SILU: gemm_launch_layout<T, EPI_BIAS_SILU>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
+    case EPI_BIAS_RESID: gemm_launch_layout<T, EPI_BIAS_RESID>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
+    case EPI_F32_STORE: gemm_launch_layout<T, EPI_F32_STORE>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
+    default: gemm_launch_layout<T, EPI_F32_ATOMIC>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
+  }
+}
+
+int launch_gemm(int dt, const void* A, int64_t lda, bool a_kcontig, const void* B, int64_t ldb,
+                bool b_kcontig, int M, int N, int K, const GemmEpiArgs& ep, int splits,
+                hipStream_t stream) {
+  if (M <= 0 || N <= 0) return MTGR_OK;
+  if (splits < 1) splits = 1;
+  if (ep.kind == EPI_F32_ATOMIC) {
+    // split-K partial sums land in a zeroed output
+    int r = launch_fill_f32((float*)ep.C, (int64_t)M * ep.ldc, 0.f, stream);
+    if (r) return r;
+  }
+  switch (dt) {
+    case MTGR_F32: gemm_launch_epi<float>(A, lda, a_kcontig, B, ldb, b_kcontig, M, N, K, splits, ep, stream); break;
+    case MTGR_BF16: gemm_launch_epi<bf16_t>(A, lda, a_kcontig, B, ldb, b_kcontig, M, N, K, splits, ep, stream); break;
+    case MTGR_F16: gemm_launch_epi<f16_t>(A, lda, a_kcontig, B, ldb, b_kcontig, M, N, K, splits, ep, stream); break;
+    default: return MTGR_ERR_UNSUPPORTED;
+  }
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+}  // namespace mtgr

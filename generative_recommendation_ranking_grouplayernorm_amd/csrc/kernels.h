@@ -1,0 +1,93 @@
+// Host-side launchers of the gfx950 kernels (C++ linkage, used by api.cpp).
+#pragma once
+
+#include "common.h"
+
+namespace mtgr {
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Rows per attention tile: queries per forward / dQ workgroup, keys per
+// dK/dV workgroup.
+constexpr int ATTN_TILE_ROWS = 128;
+
+// ---- a1: segments and tile list ----------------------------------------
+struct PrepView {
+  int32_t* seg;      // [B, 5]
+  int32_t* ntiles;   // [1] number of valid entries in tiles
+  int2* tiles;       // [max_tiles] (user, first row), longest users first
+  int64_t max_tiles; // host-side upper bound on *ntiles
+};
+int64_t max_tiles(int B, int64_t T, int rows_per_tile);
+size_t prep_workspace_bytes(int B, int64_t T, int rows_per_tile);
+int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t T, int rows_per_tile,
+                void* ws, hipStream_t stream, PrepView* out);
+int launch_seg_only(const int32_t* offsets, const uint8_t* group_ids, int B, int32_t* seg,
+                    hipStream_t stream);
+
+// ---- a2/a5: group norm rows ---------------------------------------------
+// y = GLN(x) (mode plain) or y = GLN(x) * u (mode gate).
+int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,
+                   const void* beta, const uint8_t* g, int64_t T, int d, float eps, float* mean,
+                   float* rstd, const void* u, int64_t ldu, hipStream_t stream);
+// Backward.  Plain: dx = GLN'(dy) [+ resid].  Gate (u != NULL): the forward
+// was y = GLN(x) * u, so du = dy * GLN(x) [* SiLU'(zu) if zu != NULL] and
+// dx = GLN'(dy * u).  dgamma/dbeta fp32 [G, d] overwritten.
+size_t gln_bwd_workspace_bytes(int64_t T, int d, int G);
+int launch_gln_bwd(int dt, const void* dy, int64_t lddy, const void* x, int64_t ldx, const float* mean,
+                   const float* rstd, const void* gamma, const void* beta, const uint8_t* g,
+                   int64_t T, int d, int G, void* dx, int64_t lddx, const void* resid,
+                   int64_t ldr, const void* u, int64_t ldu, void* du, int64_t lddu,
+                   const void* zu, int64_t ldzu, float* dgamma, float* dbeta, void* ws,
+                   hipStream_t stream);
+
+// ---- GEMM ----------------------------------------------------------------
+// C[m, n] = sum_k A(m, k) * B(n, k).
+//   a_kcontig: A(m,k) = A[m*lda + k], else A[k*lda + m]
+//   b_kcontig: B(n,k) = B[n*ldb + k], else B[k*ldb + n]
+enum GemmEpi {
+  EPI_STORE = 0,       // C = acc                                  (dtype dt)
+  EPI_BIAS_SILU = 1,   // z = acc + bias; Z = z (if given); C = SiLU(z)
+  EPI_BIAS_RESID = 2,  // C = acc + bias + R
+  EPI_F32_STORE = 3,   // Cf = acc (fp32)
+  EPI_F32_ATOMIC = 4   // Cf += acc (fp32, for split-K)
+};
+struct GemmEpiArgs {
+  int kind;
+  void* C;
+  int64_t ldc;
+  const void* bias;  // [N] or NULL
+  void* Z;           // pre-activation out (EPI_BIAS_SILU) or NULL
+  int64_t ldz;
+  const void* R;     // residual (EPI_BIAS_RESID)
+  int64_t ldr;
+};
+int launch_gemm(int dt, const void* A, int64_t lda, bool a_kcontig, const void* B, int64_t ldb,
+                bool b_kcontig, int M, int N, int K, const GemmEpiArgs& ep, int splits,
+                hipStream_t stream);
+int launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+// Column sums of a [T, N] matrix into fp32 out[N] (bias gradients).
+int launch_colsum(int dt, const void* X, int64_t ldx, int64_t T, int N, float* out, void* ws,
+                  hipStream_t stream);
+size_t colsum_workspace_bytes(int64_t T, int N);
+// x[t, n] *= SiLU'(z[t, n]) for n < N (in place on x).
+int launch_silu_grad_mul(int dt, void* x, int64_t ldx, const void* z, int64_t ldz, int64_t T, int N,
+                         hipStream_t stream);
+
+// ---- a4/a7: attention ----------------------------------------------------
+struct AttnArgs {
+  const void* q; const void* k; const void* v; int64_t ldqkv;
+  void* o; int64_t ldo;
+  const void* d_o; int64_t lddo;
+  void* dq; void* dk; void* dv; int64_t lddqkv;
+  // optional pre-activations: when set, the backward writes dq * SiLU'(zq)
+  // (likewise dk, dv) with zq/zk/zv at row stride ldz.
+  const void* zq; const void* zk; const void* zv; int64_t ldz;
+  const int64_t* ts;
+  int B; int64_t T; int H; int dh;
+  float alpha, scale;
+};
+int launch_attn_fwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t stream);
+int launch_attn_bwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t stream);
+
+}  // namespace mtgr

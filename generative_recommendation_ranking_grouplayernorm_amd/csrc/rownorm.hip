@@ -1,0 +1,445 @@
+// a2 / a5: Group LayerNorm forward and backward, the norm-then-gate step
+// GLN2(O) * U, and small reductions (bias gradients, SiLU' products).
+//
+// Group LayerNorm: fun-rec 7.3.3 formula (x - mu) / sigma * gamma_g + beta_g,
+// read as statistics per token over its d features and affine parameters per
+// token group (paper-daily 模型怎么搭: each token class has its own norm
+// parameters).  The gate order (normalise the aggregate, then multiply by U)
+// follows paper-daily 模型怎么搭.
+//
+// All kernels are HBM-bound row sweeps: one 64-lane wave per token row, 16-byte
+// vector accesses, statistics in fp32 from values held in registers.
+#include "kernels.h"
+
+namespace mtgr {
+
+// ---- 8-element vector access ---------------------------------------------
+__device__ __forceinline__ void load8(const float* p, float* o) {
+  float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+template <typename H>
+__device__ __forceinline__ void load8_16(const H* p, float* o) {
+  uint4 r = *(const uint4*)p;
+  uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = from_bits16<H>((uint16_t)(w[i] & 0xffff));
+    o[2 * i + 1] = from_bits16<H>((uint16_t)(w[i] >> 16));
+  }
+}
+__device__ __forceinline__ void load8(const bf16_t* p, float* o) { load8_16(p, o); }
+__device__ __forceinline__ void load8(const f16_t* p, float* o) { load8_16(p, o); }
+
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <typename H>
+__device__ __forceinline__ void store8_16(H* p, const float* v) {
+  uint4 r;
+  r.x = pack2<H>(v[0], v[1]);
+  r.y = pack2<H>(v[2], v[3]);
+  r.z = pack2<H>(v[4], v[5]);
+  r.w = pack2<H>(v[6], v[7]);
+  *(uint4*)p = r;
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float* v) { store8_16(p, v); }
+__device__ __forceinline__ void store8(f16_t* p, const float* v) { store8_16(p, v); }
+
+// ---- forward ---------------------------------------------------------------
+// NCH = number of 512-column chunks a lane covers (lane owns columns
+// lane*8 + 512*i .. +7).
+template <typename T, int NCH, bool GATE>
+__global__ __launch_bounds__(256) void gln_fwd_kernel(
+    const T* x, int64_t ldx, T* y, int64_t ldy, const T* __restrict__ gamma,
+    const T* __restrict__ beta, const uint8_t* __restrict__ g, int64_t nrows, int d, float eps,
+    float* __restrict__ mean_out, float* __restrict__ rstd_out, const T* __restrict__ u, int64_t ldu) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= nrows) return;
+  float v[NCH][8];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane * 8 + i * 512;
+    if (c < d) {
+      load8(x + row * ldx + c, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += v[i][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    }
+  }
+  const float inv_d = 1.0f / (float)d;
+  const float mean = warp_sum(s) * inv_d;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane * 8 + i * 512;
+    if (c < d) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float t = v[i][e] - mean;
+        q += t * t;
+      }
+    }
+  }
+  const float var = warp_sum(q) * inv_d;
+  const float rstd = 1.0f / sqrtf(var + eps);
+  const int grp = g[row];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane * 8 + i * 512;
+    if (c < d) {
+      float ga[8], be[8], out[8];
+      load8(gamma + (int64_t)grp * d + c, ga);
+      load8(beta + (int64_t)grp * d + c, be);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = (v[i][e] - mean) * rstd * ga[e] + be[e];
+      if (GATE) {
+        float uu[8];
+        load8(u + row * ldu + c, uu);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] *= uu[e];
+      }
+      store8(y + row * ldy + c, out);
+    }
+  }
+  if (lane == 0 && mean_out) {
+    mean_out[row] = mean;
+    rstd_out[row] = rstd;
+  }
+}
+
+template <typename T, bool GATE>
+static int gln_fwd_dispatch(const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,
+                            const void* beta, const uint8_t* g, int64_t T_, int d, float eps,
+                            float* mean, float* rstd, const void* u, int64_t ldu, hipStream_t st) {
+  dim3 grid((unsigned)((T_ + 3) / 4)), block(256);
+  const int nch = (d + 511) / 512;
+#define GLN_FWD_CASE(N)                                                                              \
+  case N:                                                                                            \
+    hipLaunchKernelGGL((gln_fwd_kernel<T, N, GATE>), grid, block, 0, st, (const T*)x, ldx, (T*)y,   \
+                       ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, \
+                       ldu);                                                                         \
+    break;
+  switch (nch) {
+    GLN_FWD_CASE(1)
+    GLN_FWD_CASE(2)
+    GLN_FWD_CASE(4)
+    GLN_FWD_CASE(8)
+    GLN_FWD_CASE(16)
+    case 3: hipLaunchKernelGGL((gln_fwd_kernel<T, 4, GATE>), grid, block, 0, st, (const T*)x, ldx, (T*)y, ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, ldu); break;
+    default:
+      if (nch <= 8) hipLaunchKernelGGL((gln_fwd_kernel<T, 8, GATE>), grid, block, 0, st, (const T*)x, ldx, (T*)y, ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, ldu);
+      else hipLaunchKernelGGL((gln_fwd_kernel<T, 16, GATE>), grid, block, 0, st, (const T*)x, ldx, (T*)y, ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, ldu);
+  }
+#undef GLN_FWD_CASE
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,
+                   const void* beta, const uint8_t* g, int64_t T_, int d, float eps, float* mean,
+                   float* rstd, const void* u, int64_t ldu, hipStream_t stream) {
+  if (T_ <= 0) return MTGR_OK;
+  const bool gate = u != nullptr;
+  switch (dt) {
+    case MTGR_F32:
+      return gate ? gln_fwd_dispatch<float, true>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream)
+                  : gln_fwd_dispatch<float, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream);
+    case MTGR_BF16:
+      return gate ? gln_fwd_dispatch<bf16_t, true>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream)
+                  : gln_fwd_dispatch<bf16_t, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream);
+    case MTGR_F16:
+      return gate ? gln_fwd_dispatch<f16_t, true>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream)
+                  : gln_fwd_dispatch<f16_t, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream);
+  }
+  return MTGR_ERR_UNSUPPORTED;
+}
+
+// ---- backward ---------------------------------------------------------------
+constexpr int GLN_BWD_ROWS_PER_BLOCK = 128;  // 32 consecutive rows per wave
+
+__device__ __forceinline__ float silu_grad_f(float z) {
+  float s = 1.0f / (1.0f + __expf(-z));
+  return s * (1.0f + z * (1.0f - s));
+}
+
+// Per block: partial[blockIdx.x][0][G][d] = dgamma part, [1][G][d] = dbeta part.
+template <typename T, int NCH, bool GATE>
+__global__ __launch_bounds__(256) void gln_bwd_kernel(
+    const T* __restrict__ dy, int64_t lddy, const T* __restrict__ x, int64_t ldx,
+    const float* __restrict__ mean, const float* __restrict__ rstd, const T* __restrict__ gamma,
+    const T* __restrict__ beta, const uint8_t* __restrict__ g, int64_t nrows, int d, int G, T* dx,
+    int64_t lddx, const T* __restrict__ resid, int64_t ldr, const T* __restrict__ u, int64_t ldu,
+    T* du, int64_t lddu, const T* __restrict__ zu, int64_t ldzu, float* __restrict__ partial) {
+  extern __shared__ float acc[];  // [2][G][d]
+  const int Gd = G * d;
+  for (int i = threadIdx.x; i < 2 * Gd; i += blockDim.x) acc[i] = 0.f;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int RPW = GLN_BWD_ROWS_PER_BLOCK / 4;
+  const int64_t r0 = (int64_t)blockIdx.x * GLN_BWD_ROWS_PER_BLOCK + (int64_t)w * RPW;
+  const float inv_d = 1.0f / (float)d;
+  float ag[NCH][8], ab[NCH][8];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
+  int cur = -1;
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int64_t row = r0 + rr;
+    if (row >= nrows) break;
+    const int grp = g[row];
+    if (grp != cur) {
+      if (cur >= 0) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int c = lane * 8 + i * 512;
+          if (c < d) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              atomicAdd(&acc[cur * d + c + e], ag[i][e]);
+              atomicAdd(&acc[Gd + cur * d + c + e], ab[i][e]);
+              ag[i][e] = ab[i][e] = 0.f;
+            }
+          }
+        }
+      }
+      cur = grp;
+    }
+    const float mu = mean[row], rs = rstd[row];
+    float n[NCH][8], e[NCH][8];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane * 8 + i * 512;
+      if (c < d) {
+        float xv[8], dyv[8], ga[8];
+        load8(x + row * ldx + c, xv);
+        load8(dy + row * lddy + c, dyv);
+        load8(gamma + (int64_t)grp * d + c, ga);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) n[i][k] = (xv[k] - mu) * rs;
+        if (GATE) {
+          float uu[8], be[8], duv[8];
+          load8(u + row * ldu + c, uu);
+          load8(beta + (int64_t)grp * d + c, be);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) duv[k] = dyv[k] * (n[i][k] * ga[k] + be[k]);
+          if (zu) {
+            float zz[8];
+            load8(zu + row * ldzu + c, zz);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) duv[k] *= silu_grad_f(zz[k]);
+          }
+          store8(du + row * lddu + c, duv);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) dyv[k] *= uu[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          ag[i][k] += dyv[k] * n[i][k];
+          ab[i][k] += dyv[k];
+          e[i][k] = dyv[k] * ga[k];
+          s1 += e[i][k];
+          s2 += e[i][k] * n[i][k];
+        }
+      }
+    }
+    s1 = warp_sum(s1) * inv_d;
+    s2 = warp_sum(s2) * inv_d;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane * 8 + i * 512;
+      if (c < d) {
+        float out[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) out[k] = rs * (e[i][k] - s1 - n[i][k] * s2);
+        if (resid) {
+          float rv[8];
+          load8(resid + row * ldr + c, rv);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) out[k] += rv[k];
+        }
+        store8(dx + row * lddx + c, out);
+      }
+    }
+  }
+  if (cur >= 0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane * 8 + i * 512;
+      if (c < d) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          atomicAdd(&acc[cur * d + c + e], ag[i][e]);
+          atomicAdd(&acc[Gd + cur * d + c + e], ab[i][e]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  float* dst = partial + (int64_t)blockIdx.x * 2 * Gd;
+  for (int i = threadIdx.x; i < 2 * Gd; i += blockDim.x) dst[i] = acc[i];
+}
+
+// out[i] = sum over nparts of partial[p][i], i < n.  Then split into
+// dgamma = out[0 .. Gd), dbeta = out[Gd .. 2Gd).
+__global__ void reduce_partials_kernel(const float* __restrict__ partial, int nparts, int n,
+                                       float* __restrict__ out_a, float* __restrict__ out_b, int na) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += partial[(int64_t)p * n + i];
+  if (i < na) {
+    if (out_a) out_a[i] = s;
+  } else if (out_b) {
+    out_b[i - na] = s;
+  }
+}
+
+size_t gln_bwd_workspace_bytes(int64_t T_, int d, int G) {
+  const int64_t nblk = (T_ + GLN_BWD_ROWS_PER_BLOCK - 1) / GLN_BWD_ROWS_PER_BLOCK;
+  return align_up((size_t)(nblk > 0 ? nblk : 1) * 2 * G * d * sizeof(float), 256);
+}
+
+template <typename T, bool GATE>
+static int gln_bwd_dispatch(const void* dy, int64_t lddy, const void* x, int64_t ldx, const float* mean,
+                            const float* rstd, const void* gamma, const void* beta, const uint8_t* g,
+                            int64_t T_, int d, int G, void* dx, int64_t lddx, const void* resid,
+                            int64_t ldr, const void* u, int64_t ldu, void* du, int64_t lddu,
+                            const void* zu, int64_t ldzu, float* partial, hipStream_t st) {
+  const int64_t nblk = (T_ + GLN_BWD_ROWS_PER_BLOCK - 1) / GLN_BWD_ROWS_PER_BLOCK;
+  const size_t lds = (size_t)2 * G * d * sizeof(float);
+  const int nch = (d + 511) / 512;
+#define GLN_BWD_ARGS                                                                                 \
+  (const T*)dy, lddy, (const T*)x, ldx, mean, rstd, (const T*)gamma, (const T*)beta, g, T_, d, G,   \
+      (T*)dx, lddx, (const T*)resid, ldr, (const T*)u, ldu, (T*)du, lddu, (const T*)zu, ldzu, partial
+  if (nch <= 1)
+    hipLaunchKernelGGL((gln_bwd_kernel<T, 1, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
+  else if (nch <= 2)
+    hipLaunchKernelGGL((gln_bwd_kernel<T, 2, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
+  else if (nch <= 4)
+    hipLaunchKernelGGL((gln_bwd_kernel<T, 4, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
+  else
+    hipLaunchKernelGGL((gln_bwd_kernel<T, 8, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
+#undef GLN_BWD_ARGS
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+int launch_gln_bwd(int dt, const void* dy, int64_t lddy, const void* x, int64_t ldx, const float* mean,
+                   const float* rstd, const void* gamma, const void* beta, const uint8_t* g,
+                   int64_t T_, int d, int G, void* dx, int64_t lddx, const void* resid,
+                   int64_t ldr, const void* u, int64_t ldu, void* du, int64_t lddu,
+                   const void* zu, int64_t ldzu, float* dgamma, float* dbeta, void* ws,
+                   hipStream_t stream) {
+  const int Gd = G * d;
+  if (T_ <= 0) {
+    if (dgamma) { int r = launch_fill_f32(dgamma, Gd, 0.f, stream); if (r) return r; }
+    if (dbeta) { int r = launch_fill_f32(dbeta, Gd, 0.f, stream); if (r) return r; }
+    return MTGR_OK;
+  }
+  float* partial = (float*)ws;
+  const bool gate = u != nullptr;
+  int r = MTGR_ERR_UNSUPPORTED;
+#define GLN_BWD_CALL(TT, GG)                                                                         \
+  gln_bwd_dispatch<TT, GG>(dy, lddy, x, ldx, mean, rstd, gamma, beta, g, T_, d, G, dx, lddx, resid, \
+                           ldr, u, ldu, du, lddu, zu, ldzu, partial, stream)
+  switch (dt) {
+    case MTGR_F32: r = gate ? GLN_BWD_CALL(float, true) : GLN_BWD_CALL(float, false); break;
+    case MTGR_BF16: r = gate ? GLN_BWD_CALL(bf16_t, true) : GLN_BWD_CALL(bf16_t, false); break;
+    case MTGR_F16: r = gate ? GLN_BWD_CALL(f16_t, true) : GLN_BWD_CALL(f16_t, false); break;
+  }
+#undef GLN_BWD_CALL
+  if (r) return r;
+  const int nblk = (int)((T_ + GLN_BWD_ROWS_PER_BLOCK - 1) / GLN_BWD_ROWS_PER_BLOCK);
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((2 * Gd + 255) / 256), dim3(256), 0, stream, partial,
+                     nblk, 2 * Gd, dgamma, dbeta, Gd);
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+// ---- small helpers ----------------------------------------------------------
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+int launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream) {
+  if (n <= 0) return MTGR_OK;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+constexpr int COLSUM_ROWS = 256;
+
+template <typename T>
+__global__ void colsum_partial_kernel(const T* __restrict__ X, int64_t ldx, int64_t nrows, int N,
+                                      float* __restrict__ partial) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= N) return;
+  const int64_t r0 = (int64_t)blockIdx.y * COLSUM_ROWS;
+  const int64_t r1 = r0 + COLSUM_ROWS < nrows ? r0 + COLSUM_ROWS : nrows;
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) s += to_f32(X[r * ldx + c]);
+  partial[(int64_t)blockIdx.y * N + c] = s;
+}
+
+size_t colsum_workspace_bytes(int64_t T_, int N) {
+  const int64_t nb = (T_ + COLSUM_ROWS - 1) / COLSUM_ROWS;
+  return align_up((size_t)(nb > 0 ? nb : 1) * N * sizeof(float), 256);
+}
+
+int launch_colsum(int dt, const void* X, int64_t ldx, int64_t T_, int N, float* out, void* ws,
+                  hipStream_t stream) {
+  if (T_ <= 0) return launch_fill_f32(out, N, 0.f, stream);
+  const int nb = (int)((T_ + COLSUM_ROWS - 1) / COLSUM_ROWS);
+  float* partial = (float*)ws;
+  dim3 grid((N + 255) / 256, nb);
+  switch (dt) {
+    case MTGR_F32: hipLaunchKernelGGL(colsum_partial_kernel<float>, grid, dim3(256), 0, stream, (const float*)X, ldx, T_, N, partial); break;
+    case MTGR_BF16: hipLaunchKernelGGL(colsum_partial_kernel<bf16_t>, grid, dim3(256), 0, stream, (const bf16_t*)X, ldx, T_, N, partial); break;
+    case MTGR_F16: hipLaunchKernelGGL(colsum_partial_kernel<f16_t>, grid, dim3(256), 0, stream, (const f16_t*)X, ldx, T_, N, partial); break;
+    default: return MTGR_ERR_UNSUPPORTED;
+  }
+  MTGR_LAUNCH_CHECK();
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, partial, nb, N,
+                     out, (float*)nullptr, N);
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+template <typename T>
+__global__ void silu_grad_mul_kernel(T* x, int64_t ldx, const T* __restrict__ z, int64_t ldz,
+                                     int64_t nrows, int N) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = nrows * (int64_t)N;
+  if (i >= total) return;
+  const int64_t r = i / N;
+  const int c = (int)(i - r * N);
+  const float zz = to_f32(z[r * ldz + c]);
+  x[r * ldx + c] = from_f32<T>(to_f32(x[r * ldx + c]) * silu_grad_f(zz));
+}
+
+int launch_silu_grad_mul(int dt, void* x, int64_t ldx, const void* z, int64_t ldz, int64_t T_, int N,
+                         hipStream_t stream) {
+  const int64_t total = T_ * (int64_t)N;
+  if (total <= 0) return MTGR_OK;
+  dim3 grid((unsigned)((total + 255) / 256));
+  switch (dt) {
+    case MTGR_F32: hipLaunchKernelGGL(silu_grad_mul_kernel<float>, grid, dim3(256), 0, stream, (float*)x, ldx, (const float*)z, ldz, T_, N); break;
+    case MTGR_BF16: hipLaunchKernelGGL(silu_grad_mul_kernel<bf16_t>, grid, dim3(256), 0, stream, (bf16_t*)x, ldx, (const bf16_t*)z, ldz, T_, N); break;
+    case MTGR_F16: hipLaunchKernelGGL(silu_grad_mul_kernel<f16_t>, grid, dim3(256), 0, stream, (f16_t*)x, ldx, (const f16_t*)z, ldz, T_, N); break;
+    default: return MTGR_ERR_UNSUPPORTED;
+  }
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+}  // namespace mtgr

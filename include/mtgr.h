@@ -1,0 +1,254 @@
+/*
+ * mtgr.h - C ABI of the MTGR HSTU layer library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the hot path of one MTGR ranking layer over a jagged
+ * batch of user-aggregated token rows [U | S | R | C]:
+ *   Group LayerNorm -> fused UQKV projection + SiLU -> SiLU attention under
+ *   the dynamic mask -> GroupNorm(attention output) * U -> output projection
+ *   + residual, and the backward of all of it.
+ *
+ * Sources (page titles and sections):
+ *   [blog] "MTGR：工业级生成式推荐框架": 4 (aggregated row), 7 (HSTU encoder),
+ *          8 (Group-Layer Normalization), 9 (dynamic masking).
+ *   [wiki] "MTGR: Industrial-Scale Generative Recommendation Framework in
+ *          Meituan/es", Métodos: attention and X-update equations.
+ *   [pd]   "MTGR：美团外卖生成式推荐Scaling Law落地实践", 模型怎么搭 (layer
+ *          order: linear+SiLU gives U,Q,K,V; SiLU(QK^T) without softmax;
+ *          normalise the aggregate, gate by U, one linear layer),
+ *          训练数据怎么组织 (jagged rows, timestamps kept for the mask).
+ *   [fr]   "MTGR：混合范式建模" (fun-rec 7.3): 7.3.3 (GLN formula),
+ *          7.3.4 (the three mask rules).
+ *
+ * Conventions shared by every call
+ *   - All pointers are caller-owned DEVICE memory unless stated otherwise.
+ *     The library never allocates or frees memory; scratch space comes only
+ *     through `workspace`, sized by mtgr_workspace_size().
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronises.
+ *   - `dt` is one mtgr_dtype for every floating tensor of a call; statistics
+ *     (mean, rstd) are always fp32, weight gradients always fp32.
+ *   - Jagged metadata: offsets int32 [B+1] with offsets[0] = 0, non-decreasing,
+ *     offsets[B] = T; group_ids uint8 [T] with 0=U, 1=S, 2=R, 3=C,
+ *     NON-DECREASING inside each user; timestamps int64 [T] (values of U and S
+ *     tokens are not read).
+ *   - Return value: MTGR_OK or a negative mtgr_status.  Argument errors are
+ *     detected on the host before anything is launched, so no output is
+ *     written; MTGR_ERR_HIP reports a failed launch.
+ *   - Calls that share a workspace must not overlap; calls with distinct
+ *     workspaces may run concurrently on different streams.
+ */
+#ifndef MTGR_H_
+#define MTGR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTGR_F32 = 0,
+  MTGR_BF16 = 1,
+  MTGR_F16 = 2
+} mtgr_dtype;
+
+typedef enum {
+  MTGR_OK = 0,
+  MTGR_ERR_INVALID_ARG = -1,        /* null required pointer, bad size, bad stride */
+  MTGR_ERR_UNSUPPORTED = -2,        /* dtype / head_dim / d_model not supported */
+  MTGR_ERR_WORKSPACE_TOO_SMALL = -3,
+  MTGR_ERR_HIP = -4,                /* a kernel launch failed */
+  MTGR_ERR_VALIDATION = -5          /* MTGR_VALIDATE=1 found bad jagged metadata */
+} mtgr_status;
+
+/* Operation ids for mtgr_workspace_size(). */
+typedef enum {
+  MTGR_OP_PREP = 0,
+  MTGR_OP_GLN_FWD = 1,
+  MTGR_OP_GLN_BWD = 2,
+  MTGR_OP_ATTN_FWD = 3,
+  MTGR_OP_ATTN_BWD = 4,
+  MTGR_OP_LAYER_FWD = 5,
+  MTGR_OP_LAYER_BWD = 6
+} mtgr_op;
+
+typedef void* mtgr_stream_t; /* hipStream_t */
+
+/* Library version string, e.g. "mtgr-hstu 0.1.0 gfx950". Host memory, static. */
+const char* mtgr_version(void);
+
+/* Human-readable text of a status code. Host memory, static. */
+const char* mtgr_status_string(int status);
+
+/* Bytes of workspace `op` needs for these sizes (0 = none).  d = model width,
+ * H = heads.  The value only grows with B and T, so a workspace sized for the
+ * largest batch serves every smaller one. */
+size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t d, int32_t H, int dt);
+
+/*
+ * a1 - jagged segments.  For each user b writes seg[b*5 + 0..4] =
+ * {start of U, start of S, start of R, start of C, end} (token indices into
+ * the batch), the layout of the aggregated row [U, S, R, (C,I)_1..K]
+ * ([blog] 4; [fr] 7.3.1).  Groups absent from a user give empty ranges.
+ *   offsets, group_ids : device, see conventions
+ *   seg                : device int32 [B, 5], written
+ *   workspace          : MTGR_OP_PREP bytes (may be NULL if that is 0)
+ */
+int mtgr_jagged_prep(const int32_t* offsets, const uint8_t* group_ids, int32_t B, int64_t T,
+                     int32_t* seg, void* workspace, size_t ws_bytes, mtgr_stream_t stream);
+
+/*
+ * a2/a5 - Group LayerNorm ([fr] 7.3.3; [pd] 模型怎么搭; [blog] 8).
+ *   y_i = (x_i - mean_i) / sqrt(var_i + eps) * gamma[g(i)] + beta[g(i)],
+ * statistics per token over its d features (biased variance), affine
+ * parameters chosen by the token's group g(i) in [0, G).
+ *   x, y          : [T, d] row-major, dtype dt; y may alias x
+ *   gamma, beta   : [G, d], dtype dt
+ *   group_ids     : uint8 [T], every value < G
+ *   mean_out, rstd_out : fp32 [T] or NULL (the backward needs them)
+ *   d % 8 == 0, 8 <= d <= 8192, 1 <= G <= 8.
+ */
+int mtgr_group_layernorm(const void* x, void* y, const void* gamma, const void* beta,
+                         const uint8_t* group_ids, int64_t T, int32_t d, int32_t G, float eps,
+                         int dt, float* mean_out, float* rstd_out, mtgr_stream_t stream);
+
+/*
+ * Backward of mtgr_group_layernorm.  With n = (x - mean) * rstd and
+ * e = dy * gamma[g]:  dx = rstd * (e - mean(e) - n * mean(e * n)),
+ * dgamma[c] = sum over tokens of group c of dy * n,  dbeta[c] = sum of dy.
+ *   dy, x, dx     : [T, d] dtype dt (dx written; may alias dy)
+ *   mean, rstd    : fp32 [T] from the forward
+ *   dgamma, dbeta : fp32 [G, d], OVERWRITTEN (not accumulated)
+ *   workspace     : MTGR_OP_GLN_BWD bytes
+ */
+int mtgr_group_layernorm_bwd(const void* dy, const void* x, const float* mean, const float* rstd,
+                             const void* gamma, const uint8_t* group_ids, int64_t T, int32_t d,
+                             int32_t G, int dt, void* dx, float* dgamma, float* dbeta,
+                             void* workspace, size_t ws_bytes, mtgr_stream_t stream);
+
+/*
+ * a4 - jagged SiLU attention under the dynamic mask ([wiki] Métodos;
+ * [pd] 模型怎么搭; mask: [fr] 7.3.4 rules 1-3, [blog] 9).  Per user b, head h:
+ *   O_i = attn_scale * sum_j M_ij * SiLU(alpha * <q_i, k_j>) * v_j
+ * with M_ij = 1 when key j is a U/S token; when j is real-time and i is a
+ * real-time or candidate token with t_j < t_i, or i == j; when j is a
+ * candidate and i == j.  No softmax.
+ *   q, k, v : [T, H*dh] views with row stride ld_qkv elements (they may point
+ *             into one fused [T, 4d] buffer); head h = columns h*dh..h*dh+dh-1
+ *   o       : [T, H*dh] with row stride ld_o, written
+ *   bf16/f16: dh in {64, 128} (MFMA kernels); f32: dh <= 128, dh % 4 == 0.
+ *   workspace : MTGR_OP_ATTN_FWD bytes
+ */
+int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv, void* o,
+                       int64_t ld_o, const int32_t* offsets, const uint8_t* group_ids,
+                       const int64_t* timestamps, int32_t B, int64_t T, int32_t H, int32_t dh,
+                       float alpha, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                       mtgr_stream_t stream);
+
+/*
+ * a7 - backward of mtgr_hstu_attn_fwd.  With S = alpha q k^T,
+ * A = SiLU(S) * M:  dV = c A^T dO,  dA = c dO V^T,  dS = dA * M * SiLU'(S),
+ * dQ = alpha dS K,  dK = alpha dS^T Q  (c = attn_scale).  The attention
+ * weights are recomputed; nothing is saved by the forward.
+ *   d_o          : [T, H*dh] with row stride ld_do
+ *   dq, dk, dv   : [T, H*dh] with row stride ld_dqkv, OVERWRITTEN
+ *   workspace    : MTGR_OP_ATTN_BWD bytes
+ */
+int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_qkv,
+                       const void* d_o, int64_t ld_do, void* dq, void* dk, void* dv,
+                       int64_t ld_dqkv, const int32_t* offsets, const uint8_t* group_ids,
+                       const int64_t* timestamps, int32_t B, int64_t T, int32_t H, int32_t dh,
+                       float alpha, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                       mtgr_stream_t stream);
+
+/* Weights of one layer, all device memory of dtype dt. */
+typedef struct {
+  const void* W_uqkv; /* [4d, d]: output feature major, output blocks U | Q | K | V */
+  const void* b_uqkv; /* [4d] or NULL */
+  const void* gamma1; /* [G, d] input Group LayerNorm */
+  const void* beta1;  /* [G, d] */
+  const void* gamma2; /* [G, d] Group LayerNorm of the attention output */
+  const void* beta2;  /* [G, d] */
+  const void* W_o;    /* [d, d]: output feature major */
+  const void* b_o;    /* [d] or NULL */
+  int32_t d;          /* model width, = H * dh */
+  int32_t H;
+  int32_t dh;
+  int32_t G;          /* number of token groups (4: U, S, R, C) */
+  float eps;          /* Group LayerNorm epsilon (1e-5) */
+  float alpha;        /* factor inside the SiLU of the attention scores (1) */
+} mtgr_layer_params;
+
+/* Activations the forward keeps for the backward (device, caller-owned). */
+typedef struct {
+  void* xhat;    /* [T, d]  output of the input Group LayerNorm */
+  float* mean1;  /* [T] */
+  float* rstd1;  /* [T] */
+  void* z;       /* [T, 4d] pre-SiLU projection */
+  void* uqkv;    /* [T, 4d] SiLU(z): U | Q | K | V */
+  void* o;       /* [T, d]  attention output */
+  float* mean2;  /* [T] */
+  float* rstd2;  /* [T] */
+  void* y;       /* [T, d]  GroupNorm(o) * U, input of the output projection */
+} mtgr_layer_saved;
+
+/* fp32 weight gradients, OVERWRITTEN by mtgr_hstu_layer_bwd.  db_uqkv and
+ * db_o may be NULL (then not computed). */
+typedef struct {
+  float* W_uqkv; /* [4d, d] */
+  float* b_uqkv; /* [4d] */
+  float* gamma1; /* [G, d] */
+  float* beta1;
+  float* gamma2;
+  float* beta2;
+  float* W_o;    /* [d, d] */
+  float* b_o;    /* [d] */
+} mtgr_layer_grads;
+
+/* Optional intermediate gradients of the backward (device, dtype dt). */
+typedef struct {
+  void* d_uqkv; /* [T, 4d] gradient w.r.t. SiLU(z), blocks dU | dQ | dK | dV; or NULL */
+  void* d_o;    /* [T, d] gradient w.r.t. the attention output; or NULL */
+} mtgr_layer_bwd_extras;
+
+/*
+ * a2..a6 - forward of one HSTU layer ([pd] 模型怎么搭; [wiki] Métodos;
+ * per-layer input norm: paper-daily deep reading, 2 方法详解):
+ *   xhat = GLN1(x); [U|Q|K|V] = SiLU(xhat W_uqkv^T + b_uqkv);
+ *   O = attention(Q, K, V); Y = GLN2(O) * U; x_out = x + Y W_o^T + b_o.
+ *   x_in, x_out : [T, d] dtype dt (x_out must not alias x_in)
+ *   saved       : NULL for inference; else every member must be non-NULL
+ *   attn_scale  : the attention normaliser (1 / longest row of the batch)
+ *   d % 64 == 0 for bf16/f16.
+ *   workspace   : MTGR_OP_LAYER_FWD bytes (smaller when saved != NULL is not
+ *                 assumed: size it with the same call)
+ */
+int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_out,
+                        const mtgr_layer_saved* saved, const int32_t* offsets,
+                        const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T,
+                        float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                        mtgr_stream_t stream);
+
+/*
+ * a6..a2 backward (a8 plus the attention backward a7): from dx_out computes
+ * dx_in (including the residual path) and every weight gradient.
+ *   x_in        : the forward's input [T, d]
+ *   saved       : filled by mtgr_hstu_layer_fwd with the same inputs
+ *   dx_out      : [T, d] upstream gradient; dx_in : [T, d] written
+ *   grads       : fp32 weight gradients, overwritten
+ *   extras      : NULL or intermediate gradients to copy out
+ *   workspace   : MTGR_OP_LAYER_BWD bytes
+ */
+int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr_layer_saved* saved,
+                        const void* dx_out, void* dx_in, const mtgr_layer_grads* grads,
+                        const mtgr_layer_bwd_extras* extras, const int32_t* offsets,
+                        const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T,
+                        float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                        mtgr_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTGR_H_ */

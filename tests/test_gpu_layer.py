@@ -1,0 +1,125 @@
+"""GPU parity of the whole layer (forward and backward) against the CPU
+oracle through the C ABI, with every saved intermediate and gradient
+checked, on the tiny fp32 workload and small bf16/f16 multi-tile batches."""
+
+import numpy as np
+import pytest
+import torch
+
+from mtgr_inputs import config_inputs, make_batch_from_lengths, make_layer_params
+from oracle import mtgr_oracle as orc
+from tests.gpu_util import TOL, f64, meta, params_to, rel_l2, rounded, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def mb():
+    import generative_recommendation_ranking_grouplayernorm_amd.binding as b
+
+    b.load_library()
+    return b
+
+
+def run_layer(mb, batch, p, x, dtype, R=None, scale=None, extras=True):
+    """GPU forward (+ backward when R is given).  Returns dict of numpy fp64."""
+    scale = scale if scale is not None else 1.0 / batch.max_len
+    d, H = p.d, p.H
+    G = p.gamma1.shape[0]
+    dev_p, q = params_to(p, dtype, DEV)
+    xt = rounded(x, dtype)
+    off, g, ts = meta(batch, DEV)
+    params = mb.make_params(dev_p, H)
+    saved = mb.alloc_saved(batch.T, d, dtype, DEV)
+    x_out = torch.empty(batch.T, d, dtype=dtype, device=DEV)
+    ws = mb.workspace(mb.OP_LAYER_FWD, batch.B, batch.T, d, H, dtype, DEV)
+    xd = xt.to(DEV)
+    mb.mtgr_hstu_layer_fwd(params, xd, x_out, mb.make_saved(saved), off, g, ts, scale, ws)
+    out = {"x_out": f64(x_out)}
+    out.update({k: f64(v) for k, v in saved.items()})
+    if R is not None:
+        Rt = rounded(R, dtype)
+        grads = mb.alloc_grads(d, G, p.b_uqkv is not None, DEV)
+        dx = torch.empty(batch.T, d, dtype=dtype, device=DEV)
+        ex = None
+        if extras:
+            ex = dict(d_uqkv=torch.empty(batch.T, 4 * d, dtype=dtype, device=DEV),
+                      d_o=torch.empty(batch.T, d, dtype=dtype, device=DEV))
+        wsb = mb.workspace(mb.OP_LAYER_BWD, batch.B, batch.T, d, H, dtype, DEV)
+        mb.mtgr_hstu_layer_bwd(params, xd, mb.make_saved(saved), Rt.to(DEV), dx, grads, off, g, ts, scale, wsb,
+                               extras=ex)
+        out["dx"] = f64(dx)
+        out.update({"g_" + k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()})
+        if ex:
+            out["d_uqkv"] = f64(ex["d_uqkv"])
+            out["d_o"] = f64(ex["d_o"])
+        out["_R"] = f64(Rt)
+    torch.cuda.synchronize()
+    out["_x"] = f64(xt)
+    out["_q"] = q
+    out["_scale"] = scale
+    return out
+
+
+def oracle_layer(batch, res, with_bwd):
+    q = res["_q"]
+    ref, sv = orc.layer_fwd(q, res["_x"], batch.offsets, batch.group_ids, batch.timestamps, 1.0, res["_scale"])
+    want = {"x_out": ref, "xhat": sv["xhat"], "z": sv["z"], "uqkv": sv["uqkv"], "o": sv["o"], "y": sv["y"],
+            "mean1": sv["mean1"], "rstd1": sv["rstd1"], "mean2": sv["mean2"], "rstd2": sv["rstd2"]}
+    if with_bwd:
+        dx, gr = orc.layer_bwd(q, res["_x"], sv, res["_R"], batch.offsets, batch.group_ids, batch.timestamps, 1.0,
+                               res["_scale"])
+        want["dx"] = dx
+        for k in ("W_uqkv", "b_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o", "b_o"):
+            want["g_" + k] = gr[k]
+        want["d_uqkv"] = np.concatenate([gr["dU"], gr["dQ"], gr["dK"], gr["dV"]], axis=1)
+        want["d_o"] = gr["dO"]
+    return want
+
+
+def check(res, want, dtype, skip=()):
+    worst = {}
+    for k, ref in want.items():
+        if k in skip or k not in res:
+            continue
+        err = rel_l2(res[k], ref)
+        worst[k] = err
+        say(f"  {k}: rel-L2 {err:.3e}")
+    bad = {k: v for k, v in worst.items() if not v <= TOL[dtype]}
+    assert not bad, bad
+
+
+def test_layer_cfg1_fp32_fwd_bwd(mb):
+    batch, params, x = config_inputs(1)
+    R = np.random.default_rng(77).normal(0, 1, size=x.shape)
+    say("layer cfg1 fp32", batch.B, batch.T)
+    res = run_layer(mb, batch, params[0], x, torch.float32, R=R)
+    check(res, oracle_layer(batch, res, True), torch.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_layer_small_halfprec_fwd_bwd(mb, dtype):
+    rng = np.random.default_rng(31)
+    lengths = [[8, 260, 30, 20], [8, 33, 0, 20], [8, 129, 64, 7], [0, 0, 9, 4], [8, 500, 12, 60]]
+    batch = make_batch_from_lengths(lengths, rng, ts_max=86400)
+    p = make_layer_params(256, 2, rng, "xavier", False)
+    x = rng.normal(0, 1, size=(batch.T, 256))
+    R = rng.normal(0, 1, size=x.shape)
+    say("layer small", dtype, batch.T)
+    res = run_layer(mb, batch, p, x, dtype, R=R)
+    check(res, oracle_layer(batch, res, True), dtype)
+
+
+def test_layer_bias_bf16_no_extras(mb):
+    """Biases present and the fused SiLU' path (no intermediate gradients)."""
+    rng = np.random.default_rng(41)
+    lengths = [[8, 200, 30, 20], [8, 90, 5, 20]]
+    batch = make_batch_from_lengths(lengths, rng, ts_max=86400)
+    p = make_layer_params(128, 1, rng, "xavier", True)
+    x = rng.normal(0, 1, size=(batch.T, 128))
+    R = rng.normal(0, 1, size=x.shape)
+    say("layer bias bf16", batch.T)
+    res = run_layer(mb, batch, p, x, torch.bfloat16, R=R, extras=False)
+    check(res, oracle_layer(batch, res, True), torch.bfloat16)
