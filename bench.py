@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the MTGR HSTU layer on one MI355X.
+
+One step = the whole hot path over one batch: jagged segments, input Group
+LayerNorm, UQKV projection + SiLU, masked SiLU attention, GroupNorm(AV) * U,
+output projection + residual, and the backward of all of it (dQ, dK, dV,
+dU, dGLN and every weight gradient).  Workload: a token-balanced bf16 batch
+of exactly 65,536 tokens of long-tail users (history lognormal(6, 1) clipped
+to [32, 3000], 0-64 real-time tokens, 20 candidates), d_model 1024, 8 heads
+of 128, seeded synthetic data with random-init weights.
+
+Prints one JSON line.  ``value`` is the attention throughput (forward +
+backward algorithmic flops, 12 d P for P mask-visible pairs, over the summed
+duration of the attention kernels measured with HIP events on their stream
+inside the timed steps); ``users_per_sec`` is whole-step throughput.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU-oracle baseline sample (0 disables it)")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def profile_summary(lib):
+    n = 64
+    names = (ctypes.c_char_p * n)()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    lib.mtgr_profile_summary.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
+    k = lib.mtgr_profile_summary(n, names, ms, cnt)
+    if k < 0:
+        raise RuntimeError(f"mtgr_profile_summary failed: {k}")
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(min(k, n))}
+
+
+def kernel_work(T, d, P):
+    """Algorithmic work of one launch of each kernel step: (bound, amount)
+    with flops for MFMA-bound steps and HBM bytes for row sweeps."""
+    e = 2  # bf16 bytes
+    return {
+        "attn_fwd": ("mfma", 4 * d * P),
+        "attn_bwd_dkdv": ("mfma", 6 * d * P),   # dV, dA = dO V^T, dK
+        "attn_bwd_dq": ("mfma", 2 * d * P),     # dQ
+        "gemm_uqkv_silu": ("mfma", 8 * T * d * d),
+        "gemm_out_resid": ("mfma", 2 * T * d * d),
+        "gemm_dy": ("mfma", 2 * T * d * d),
+        "gemm_dW_o": ("mfma", 2 * T * d * d),
+        "gemm_dxhat": ("mfma", 8 * T * d * d),
+        "gemm_dW_uqkv": ("mfma", 8 * T * d * d),
+        "gln1_fwd": ("hbm", T * (2 * e * d + 9)),
+        "gln2_gate_fwd": ("hbm", T * (3 * e * d + 9)),
+        "gln2_gate_bwd": ("hbm", T * (6 * e * d + 9)),
+        "gln1_bwd": ("hbm", T * (4 * e * d + 9)),
+    }
+
+
+def cpu_baseline(batch, params, x, R, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole users in batch order until the time budget is spent."""
+    import numpy as np
+
+    from generative_recommendation_ranking_grouplayernorm_amd import flops as fl
+    from oracle import mtgr_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    p = params[0]
+    scale = 1.0 / batch.max_len
+    attn_t = layer_t = 0.0
+    attn_f = 0
+    users = 0
+    toks = 0
+    for b in range(batch.B):
+        off, g, ts, xs, rows = orc.select_users(batch.offsets, batch.group_ids, batch.timestamps, x, [b])
+        d = x.shape[1]
+        rng = np.random.default_rng(b)
+        q, k, v, do = (rng.normal(0, 0.35, size=(len(rows), d)) for _ in range(4))
+        t0 = time.perf_counter()
+        orc.hstu_attention(q, k, v, off, g, ts, p.H, 1.0, scale)
+        orc.hstu_attention_bwd(q, k, v, do, off, g, ts, p.H, 1.0, scale)
+        t1 = time.perf_counter()
+        out, sv = orc.layer_fwd(p, xs, off, g, ts, 1.0, scale)
+        orc.layer_bwd(p, xs, sv, R[rows], off, g, ts, 1.0, scale)
+        t2 = time.perf_counter()
+        attn_t += t1 - t0
+        layer_t += t2 - t1
+        fwd, bwd = fl.attention_flops(off, g, ts, d)
+        attn_f += fwd + bwd
+        users += 1
+        toks += len(rows)
+        if attn_t + layer_t >= budget_s:
+            break
+    return {
+        "value": attn_f / attn_t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {users} users ({toks} tokens) of the same 65,536-token batch, fp64 NumPy: "
+                  f"attention fwd+bwd timed alone ({attn_t:.2f} s), then the whole layer fwd+bwd "
+                  f"({layer_t:.2f} s)",
+        "users_per_sec": users / layer_t,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is a "
+              f"design note, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import generative_recommendation_ranking_grouplayernorm_amd.binding as mb
+    from generative_recommendation_ranking_grouplayernorm_amd import flops as fl
+    from mtgr_inputs import CONFIGS, config_inputs
+
+    cfg_id = 4
+    cfg = CONFIGS[cfg_id]
+    dev = torch.device("cuda:0")
+    lib = mb.load_library()
+    batch, params, x = config_inputs(cfg_id, seed=args.seed)
+    p = params[0]
+    d, H, G = cfg["d"], cfg["H"], 4
+    T, B = batch.T, batch.B
+    dt = torch.bfloat16
+    rng = np.random.default_rng([args.seed, cfg_id, 3])
+    R = rng.normal(0, 1, size=(T, d)).astype(np.float32)
+    scale = 1.0 / batch.max_len
+
+    def to(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(dev)
+
+    dev_p = {k: to(getattr(p, k)) for k in ("W_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o")}
+    xd, Rd = to(x), to(R)
+    off = torch.from_numpy(batch.offsets).to(dev)
+    g = torch.from_numpy(batch.group_ids).to(dev)
+    ts = torch.from_numpy(batch.timestamps).to(dev)
+    prm = mb.make_params(dev_p, H)
+    saved = mb.alloc_saved(T, d, dt, dev)
+    sv = mb.make_saved(saved)
+    x_out = torch.empty(T, d, dtype=dt, device=dev)
+    dx = torch.empty(T, d, dtype=dt, device=dev)
+    grads = mb.alloc_grads(d, G, False, dev)
+    ws_f = mb.workspace(mb.OP_LAYER_FWD, B, T, d, H, dt, dev)
+    ws_b = mb.workspace(mb.OP_LAYER_BWD, B, T, d, H, dt, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mb.mtgr_hstu_layer_fwd(prm, xd, x_out, sv, off, g, ts, scale, ws_f, stream)
+        mb.mtgr_hstu_layer_bwd(prm, xd, sv, Rd, dx, grads, off, g, ts, scale, ws_b, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
+    lib.mtgr_profile_enable(1)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    prof = profile_summary(lib)
+    lib.mtgr_profile_enable(0)
+    ms_step = ms_total / args.steps
+
+    P = fl.visible_pairs(batch.offsets, batch.group_ids, batch.timestamps)
+    attn_flops = 12 * d * P
+    attn_ms = sum(prof.get(k, (0.0, 0))[0] for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq")) / args.steps
+    value = attn_flops / (attn_ms / 1e3) / 1e12
+    layer_flops = 12 * d * P + fl.layer_gemm_flops(T, d, backward=True)
+
+    work = kernel_work(T, d, P)
+    kernels = {}
+    for name, (tot, n) in prof.items():
+        avg = tot / max(n, 1)
+        ent = {"avg_ms": round(avg, 5), "launches": n, "ms_per_step": round(tot / args.steps, 5)}
+        if name in work:
+            bound, amount = work[name]
+            if bound == "mfma":
+                ach = amount / (avg / 1e3) / 1e12
+                ent.update(bound="mfma", achieved=round(ach, 2), unit="TFLOP/s", frac=round(ach / BF16_PEAK_TFLOPS, 4))
+            else:
+                ach = amount / (avg / 1e3) / 1e9
+                ent.update(bound="hbm", achieved=round(ach, 1), unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4))
+        kernels[name] = ent
+    dom = max((k for k in kernels if "bound" in kernels[k]), key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dom]
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        try:
+            traffic = json.load(open(tpath)).get(dom)
+        except Exception:
+            traffic = None
+    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
+                "peak": BF16_PEAK_TFLOPS if dk["bound"] == "mfma" else HBM_PEAK_GBS,
+                "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(batch, params, x, R, args.cpu_seconds)
+
+    out = {
+        "metric": "fused jagged HSTU attn TFLOP/s (fwd+bwd, bf16, d=1024) + users/sec on 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded long-tail jagged users, random-init weights)",
+        "config": {"workload": "MTGR HSTU layer fwd+bwd, token-balanced batch", "tokens": T, "users": B,
+                   "d_model": d, "heads": H, "head_dim": d // H, "max_len": batch.max_len,
+                   "visible_pairs": P, "parallelism": "single GPU"},
+        "users_per_sec": round(B / (ms_step / 1e3), 1),
+        "attn_ms_per_step": round(attn_ms, 4),
+        "attn_frac_of_bf16_peak": round(value / BF16_PEAK_TFLOPS, 4),
+        "layer_tflops": round(layer_flops / (ms_step / 1e3) / 1e12, 2),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

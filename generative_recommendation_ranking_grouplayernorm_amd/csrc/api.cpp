@@ -257,18 +257,27 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
   void* o = saved ? saved->o : ws_o;
   void* y = saved ? saved->y : ws_xhat;  // xhat is dead once the projection has run
   PrepView pv;
-  r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, ws_prep, st, &pv);
+  {
+    ProfScope ps("prep", st);
+    r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, ws_prep, st, &pv);
+  }
   if (r) return r;
   // a2: input group norm
-  r = launch_gln_fwd(dt, x_in, d, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->eps,
-                     saved ? saved->mean1 : nullptr, saved ? saved->rstd1 : nullptr, nullptr, 0, st);
+  {
+    ProfScope ps("gln1_fwd", st);
+    r = launch_gln_fwd(dt, x_in, d, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->eps,
+                       saved ? saved->mean1 : nullptr, saved ? saved->rstd1 : nullptr, nullptr, 0, st);
+  }
   if (r) return r;
   // a3: [U|Q|K|V] = SiLU(xhat W^T + b)
   GemmEpiArgs ep = {};
   ep.kind = EPI_BIAS_SILU;
   ep.C = uqkv; ep.ldc = 4 * d; ep.bias = p->b_uqkv;
   ep.Z = saved ? saved->z : nullptr; ep.ldz = 4 * d;
-  r = launch_gemm(dt, xhat, d, true, p->W_uqkv, d, true, (int)T, 4 * d, d, ep, 1, st);
+  {
+    ProfScope ps("gemm_uqkv_silu", st);
+    r = launch_gemm(dt, xhat, d, true, p->W_uqkv, d, true, (int)T, 4 * d, d, ep, 1, st);
+  }
   if (r) return r;
   // a4: attention
   const char* base = (const char*)uqkv;
@@ -279,13 +288,17 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
   r = launch_attn_fwd(dt, a, pv, st);
   if (r) return r;
   // a5: y = GLN2(o) * U
-  r = launch_gln_fwd(dt, o, d, y, d, p->gamma2, p->beta2, group_ids, T, d, p->eps,
-                     saved ? saved->mean2 : nullptr, saved ? saved->rstd2 : nullptr, uqkv, 4 * d, st);
+  {
+    ProfScope ps("gln2_gate_fwd", st);
+    r = launch_gln_fwd(dt, o, d, y, d, p->gamma2, p->beta2, group_ids, T, d, p->eps,
+                       saved ? saved->mean2 : nullptr, saved ? saved->rstd2 : nullptr, uqkv, 4 * d, st);
+  }
   if (r) return r;
   // a6: x_out = x + y W_o^T + b_o
   GemmEpiArgs eo = {};
   eo.kind = EPI_BIAS_RESID;
   eo.C = x_out; eo.ldc = d; eo.bias = p->b_o; eo.R = x_in; eo.ldr = d;
+  ProfScope ps("gemm_out_resid", st);
   return launch_gemm(dt, y, d, true, p->W_o, d, true, (int)T, d, d, eo, 1, st);
 }
 
@@ -329,7 +342,10 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
   void* ws_red = cv.take(rbytes > cbytes ? rbytes : cbytes);
   if (!cv.ok) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   PrepView pv;
-  r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, ws_prep, st, &pv);
+  {
+    ProfScope ps("prep", st);
+    r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, ws_prep, st, &pv);
+  }
   if (r) return r;
   const bool want_dact = extras && extras->d_uqkv;
   void* dO = (extras && extras->d_o) ? extras->d_o : ws_do;
@@ -342,20 +358,29 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
   // a6 backward: dy = dx_out W_o ; dW_o = dx_out^T y ; db_o = colsum(dx_out)
   GemmEpiArgs ep = {};
   ep.kind = EPI_STORE; ep.C = ws_dy; ep.ldc = d;
-  r = launch_gemm(dt, dx_out, d, true, p->W_o, d, false, (int)T, d, d, ep, 1, st);
+  {
+    ProfScope ps("gemm_dy", st);
+    r = launch_gemm(dt, dx_out, d, true, p->W_o, d, false, (int)T, d, d, ep, 1, st);
+  }
   if (r) return r;
   GemmEpiArgs ew = {};
   ew.kind = EPI_F32_ATOMIC; ew.C = grads->W_o; ew.ldc = d;
-  r = launch_gemm(dt, dx_out, d, false, saved->y, d, false, d, d, (int)T, ew, splits_for(d, d, (int)T), st);
+  {
+    ProfScope ps("gemm_dW_o", st);
+    r = launch_gemm(dt, dx_out, d, false, saved->y, d, false, d, d, (int)T, ew, splits_for(d, d, (int)T), st);
+  }
   if (r) return r;
   if (grads->b_o) {
     r = launch_colsum(dt, dx_out, d, T, d, grads->b_o, ws_red, st);
     if (r) return r;
   }
   // a5 backward: dU = dy * GLN2(o) [* SiLU'(z_u)], dO = GLN2'(dy * U)
-  r = launch_gln_bwd(dt, ws_dy, d, saved->o, d, saved->mean2, saved->rstd2, p->gamma2, p->beta2, group_ids, T,
+  {
+    ProfScope ps("gln2_gate_bwd", st);
+    r = launch_gln_bwd(dt, ws_dy, d, saved->o, d, saved->mean2, saved->rstd2, p->gamma2, p->beta2, group_ids, T,
                      d, G, dO, d, nullptr, 0, ub, 4 * d, db, 4 * d, want_dact ? nullptr : zb, 4 * d,
-                     grads->gamma2, grads->beta2, ws_red, st);
+                       grads->gamma2, grads->beta2, ws_red, st);
+  }
   if (r) return r;
   // a7: attention backward into the Q, K, V blocks
   AttnArgs a = {};
@@ -377,18 +402,25 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
   // a3 backward: dxhat = dz W_uqkv ; dW_uqkv = dz^T xhat ; db_uqkv = colsum(dz)
   GemmEpiArgs ex = {};
   ex.kind = EPI_STORE; ex.C = ws_dy; ex.ldc = d;
-  r = launch_gemm(dt, ws_dz, 4 * d, true, p->W_uqkv, d, false, (int)T, d, 4 * d, ex, 1, st);
+  {
+    ProfScope ps("gemm_dxhat", st);
+    r = launch_gemm(dt, ws_dz, 4 * d, true, p->W_uqkv, d, false, (int)T, d, 4 * d, ex, 1, st);
+  }
   if (r) return r;
   GemmEpiArgs eu = {};
   eu.kind = EPI_F32_ATOMIC; eu.C = grads->W_uqkv; eu.ldc = d;
-  r = launch_gemm(dt, ws_dz, 4 * d, false, saved->xhat, d, false, 4 * d, d, (int)T, eu,
-                  splits_for(4 * d, d, (int)T), st);
+  {
+    ProfScope ps("gemm_dW_uqkv", st);
+    r = launch_gemm(dt, ws_dz, 4 * d, false, saved->xhat, d, false, 4 * d, d, (int)T, eu,
+                    splits_for(4 * d, d, (int)T), st);
+  }
   if (r) return r;
   if (grads->b_uqkv) {
     r = launch_colsum(dt, ws_dz, 4 * d, T, 4 * d, grads->b_uqkv, ws_red, st);
     if (r) return r;
   }
   // a2 backward with the residual: dx = GLN1'(dxhat) + dx_out
+  ProfScope ps("gln1_bwd", st);
   return launch_gln_bwd(dt, ws_dy, d, x_in, d, saved->mean1, saved->rstd1, p->gamma1, p->beta1, group_ids, T, d,
                         G, dx_in, d, dx_out, d, nullptr, 0, nullptr, 0, nullptr, 0, grads->gamma1, grads->beta1,
                         ws_red, st);

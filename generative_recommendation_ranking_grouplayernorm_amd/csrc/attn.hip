@@ -599,6 +599,7 @@ __global__ void attn_bwd_dkdv_f32(const float* __restrict__ Q, const float* __re
 template <typename T, int DH>
 static void fwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
   dim3 grid((unsigned)pv.max_tiles, a.H);
+  ProfScope ps("attn_fwd", st);
   hipLaunchKernelGGL((attn_fwd_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (uint16_t*)a.o, a.ldo, pv.seg,
                      a.ts, pv.tiles, pv.ntiles, a.alpha, a.scale);
@@ -607,10 +608,14 @@ static void fwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
 template <typename T, int DH>
 static void bwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
   dim3 grid((unsigned)pv.max_tiles, a.H);
-  hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (const uint16_t*)a.d_o, a.lddo,
-                     (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv, (const uint16_t*)a.zk,
-                     (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.tiles, pv.ntiles, a.alpha, a.scale);
+  {
+    ProfScope ps("attn_bwd_dkdv", st);
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (const uint16_t*)a.d_o, a.lddo,
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv, (const uint16_t*)a.zk,
+                       (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.tiles, pv.ntiles, a.alpha, a.scale);
+  }
+  ProfScope ps("attn_bwd_dq", st);
   hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (const uint16_t*)a.d_o, a.lddo,
                      (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg, a.ts, pv.tiles,

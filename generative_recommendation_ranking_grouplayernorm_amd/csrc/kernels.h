@@ -7,6 +7,21 @@ namespace mtgr {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Brackets the launches of one named kernel step with HIP events on stream
+// `s` when timing is switched on (mtgr_profile_enable); a no-op otherwise.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  void* begin_;
+};
+
 // Rows per attention tile: queries per forward / dQ workgroup, keys per
 // dK/dV workgroup.
 constexpr int ATTN_TILE_ROWS = 128;

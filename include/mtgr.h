@@ -247,6 +247,19 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
                         float attn_scale, int dt, void* workspace, size_t ws_bytes,
                         mtgr_stream_t stream);
 
+/*
+ * Benchmark instrumentation (not part of the method).  When enabled, every
+ * kernel step launched by the calls above is bracketed by HIP events recorded
+ * on the stream it runs on.  mtgr_profile_enable(1) clears earlier records
+ * and starts recording, (0) clears and stops.  mtgr_profile_summary waits for
+ * the recorded events and writes, per distinct step name (host strings owned
+ * by the library), the summed milliseconds and the number of launches;
+ * returns the number of distinct names (which may exceed max_entries) or a
+ * negative mtgr_status.  Not for concurrent use from several threads.
+ */
+int mtgr_profile_enable(int on);
+int mtgr_profile_summary(int max_entries, const char** names, double* total_ms, int32_t* launches);
+
 #ifdef __cplusplus
 }
 #endif
