@@ -30,7 +30,7 @@ bool attn_shape_ok(int dt, int dh) {
   return dh == 64 || dh == 128;
 }
 
-size_t attn_ws(int B, int64_t T) { return prep_workspace_bytes(B, T, ATTN_TILE_ROWS); }
+size_t attn_ws(int B, int64_t T) { return prep_workspace_bytes(B, T); }
 
 // Carve a workspace sequentially.
 struct Carver {
@@ -180,7 +180,7 @@ int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_q
   if (ld_o < (int64_t)H * dh || (T > 0 && !o) || !vec_ok(o, ld_o, dt)) return MTGR_ERR_INVALID_ARG;
   if (B == 0 || T == 0) return MTGR_OK;
   PrepView pv;
-  r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, workspace, S(stream), &pv);
+  r = launch_prep(offsets, group_ids, B, T, workspace, S(stream), &pv);
   if (r) return r;
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v; a.ldqkv = ld_qkv;
@@ -204,7 +204,7 @@ int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_q
     return MTGR_ERR_INVALID_ARG;
   if (B == 0 || T == 0) return MTGR_OK;
   PrepView pv;
-  r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, workspace, S(stream), &pv);
+  r = launch_prep(offsets, group_ids, B, T, workspace, S(stream), &pv);
   if (r) return r;
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v; a.ldqkv = ld_qkv;
@@ -259,7 +259,7 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
   PrepView pv;
   {
     ProfScope ps("prep", st);
-    r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, ws_prep, st, &pv);
+    r = launch_prep(offsets, group_ids, B, T, ws_prep, st, &pv);
   }
   if (r) return r;
   // a2: input group norm
@@ -344,7 +344,7 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
   PrepView pv;
   {
     ProfScope ps("prep", st);
-    r = launch_prep(offsets, group_ids, B, T, ATTN_TILE_ROWS, ws_prep, st, &pv);
+    r = launch_prep(offsets, group_ids, B, T, ws_prep, st, &pv);
   }
   if (r) return r;
   const bool want_dact = extras && extras->d_uqkv;

@@ -117,119 +117,345 @@ __device__ __forceinline__ op8 pack_kstep(const float (&v)[2][16], int u) {
 }
 
 // ---------------------------------------------------------------------------
-// forward
+// workgroup -> (tile, head), XCD-aware
 // ---------------------------------------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup L runs on
+// XCD L % 8), each XCD with its own L2.  Mapping the head to L % 8 puts every
+// query tile of one (user, head) on the same XCD, so its K/V rows are fetched
+// from HBM once and then served from that XCD's L2.
+__device__ __forceinline__ void xcd_tile_head(int L, int H, int& tile, int& head) {
+  if ((H & 7) == 0) {
+    const int x = L & 7, r = L >> 3, hg = H >> 3;
+    head = x + 8 * (r % hg);
+    tile = r / hg;
+  } else if ((8 % H) == 0) {
+    const int x = L & 7, r = L >> 3, per = 8 / H;
+    head = x % H;
+    tile = r * per + x / H;
+  } else {
+    head = L % H;
+    tile = L / H;
+  }
+}
+
+inline unsigned xcd_grid(int64_t max_tiles, int H) {
+  if ((H & 7) == 0) return (unsigned)(max_tiles * H);
+  if ((8 % H) == 0) {
+    const int64_t per = 8 / H;
+    return (unsigned)(((max_tiles + per - 1) / per) * 8);
+  }
+  return (unsigned)(max_tiles * H);
+}
+
+// Branch-free tile load: rows at or beyond rlim read as zero (the address is
+// clamped to a valid row so that no lane issues an out-of-range access).
+template <int DH, int ROWS>
+__device__ __forceinline__ void tile_gload_rows(uint4* r, const uint16_t* __restrict__ P, int64_t ld, int r0,
+                                                int rlim, int col0, int tid) {
+  constexpr int CPR = DH / 8;
+  constexpr int CH = ROWS * CPR / 256;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c / CPR, col = (c % CPR) * 8;
+    const int gr = r0 + row;
+    const int cr = gr < rlim ? gr : rlim - 1;
+    uint4 v = *(const uint4*)(P + (int64_t)cr * ld + col0 + col);
+    if (gr >= rlim) v = make_uint4(0, 0, 0, 0);
+    r[i] = v;
+  }
+}
+template <int DH, int ROWS, int PITCH>
+__device__ __forceinline__ void tile_swrite_rows(uint16_t* s, const uint4* r, int tid) {
+  constexpr int CPR = DH / 8;
+  constexpr int CH = ROWS * CPR / 256;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c / CPR, col = (c % CPR) * 8;
+    *(uint4*)(s + row * PITCH + col) = r[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// V^T tiles in LDS
+// ---------------------------------------------------------------------------
+// The B operand of P V needs, per lane, 8 keys of one dh column.  With the
+// keys of each 16-key group stored in the order pi(k) below, those 8 keys are
+// contiguous, so the operand is one 16-byte LDS read instead of two transpose
+// reads.  A [DH][64-key] tile is written from row-major global rows: each
+// thread owns 4 consecutive keys x 8 dh, transposes them in registers and
+// writes 8 eight-byte pieces; the lane -> (keys, dh chunk) assignment keeps
+// every half-wave of the writes and every quarter-wave of the reads on
+// distinct banks with a row pitch of 72 elements.
+constexpr int VT_PITCH = 72;
+
+__device__ __forceinline__ int key_perm(int k) {
+  const int k16 = k & 15;
+  return (k & ~15) + 8 * ((k16 >> 2) & 1) + 4 * (k16 >> 3) + (k16 & 3);
+}
+
+template <int DH>
+struct VtLoad {
+  uint4 x[4];
+  int kq, c;
+  bool on;
+};
+
+// Global loads of one 64-key V tile for V^T: 4 rows (keys 4kq..4kq+3) x 16
+// bytes (dh 8c..8c+7).
+template <int DH>
+__device__ __forceinline__ void vt_gload(VtLoad<DH>& L, const uint16_t* __restrict__ V, int64_t ld, int k0,
+                                         int rlim, int col0, int tid) {
+  const int lane = tid & 63, w = tid >> 6;
+  L.kq = lane & 15;
+  L.c = 4 * w + 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
+  L.on = L.c < DH / 8;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int gr = k0 + 4 * L.kq + r;
+    const int cr = gr < rlim ? gr : rlim - 1;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (L.on) v = *(const uint4*)(V + (int64_t)cr * ld + col0 + 8 * L.c);
+    L.x[r] = gr < rlim ? v : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ void vt_swrite(uint16_t* s, const VtLoad<DH>& L) {
+  if (!L.on) return;
+  const uint32_t* x0 = (const uint32_t*)&L.x[0];
+  const uint32_t* x1 = (const uint32_t*)&L.x[1];
+  const uint32_t* x2 = (const uint32_t*)&L.x[2];
+  const uint32_t* x3 = (const uint32_t*)&L.x[3];
+  const int col = key_perm(4 * L.kq);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    // dh 8c + 2m (low halves) and 8c + 2m + 1 (high halves)
+    uint2 lo, hi;
+    lo.x = __builtin_amdgcn_perm(x1[m], x0[m], 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(x3[m], x2[m], 0x05040100u);
+    hi.x = __builtin_amdgcn_perm(x1[m], x0[m], 0x07060302u);
+    hi.y = __builtin_amdgcn_perm(x3[m], x2[m], 0x07060302u);
+    *(uint2*)(s + (8 * L.c + 2 * m) * VT_PITCH + col) = lo;
+    *(uint2*)(s + (8 * L.c + 2 * m + 1) * VT_PITCH + col) = hi;
+  }
+}
+
+// B operand of P V from a V^T tile: column dh = col0 + l32, k-step u.
+__device__ __forceinline__ op8 vt_operand(const uint16_t* s, int u, int col0, int lane) {
+  op8 o;
+  o.v = *(const u32x4_t*)(s + (col0 + (lane & 31)) * VT_PITCH + 16 * u + 8 * (lane >> 5));
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// forward: 128 queries per workgroup (4 waves x 32), 64 keys per LDS stage,
+// two workgroups per CU so that one wave's SiLU overlaps another's MFMAs.
+// ---------------------------------------------------------------------------
+constexpr int F_BQ = 128;
+constexpr int F_BK = 64;
+
+template <typename T, int DH, bool MASKED>
+__device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt, const op8 (&qop)[DH / 16],
+                                         f32x16_t (&oacc)[DH / 32], int k0, int qi, int64_t tq, int s_end,
+                                         int r_end, int hi, const int64_t* __restrict__ ts, float kexp,
+                                         int lane) {
+  constexpr int KP = AttnPitch<DH>::B128;
+  const int g = lane >> 5;
+  f32x16_t sacc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[t][j] = 0.f;
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(row_operand<KP>(Ks, t * 32, s, lane), qop[s], sacc[t]);
+  float p[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float sv = sacc[t][j];
+      float pv = sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * kexp));
+      if (MASKED) {
+        const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+        if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) pv = 0.f;
+      }
+      p[t][j] = pv;
+    }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const op8 pa = pack_kstep<T>(p, u);
+#pragma unroll
+    for (int c = 0; c < DH / 32; ++c) oacc[c] = mfma32<T>(pa, vt_operand(Vt, u, c * 32, lane), oacc[c]);
+  }
+}
+
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void attn_fwd_mfma(
+__global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t ldqkv, uint16_t* __restrict__ O, int64_t ldo, const int32_t* __restrict__ seg,
     const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-    float alpha, float scale) {
-  constexpr int KP = AttnPitch<DH>::B128, VP = AttnPitch<DH>::TR;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][A_BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][A_BK * VP];
-  if ((int)blockIdx.x >= *ntiles) return;
-  const int h = blockIdx.y;
-  const int2 te = tiles[blockIdx.x];
+    int H, float kexp, float out_scale) {
+  constexpr int KP = AttnPitch<DH>::B128;
+  constexpr int NS = DH / 16, NC = DH / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][F_BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DH * VT_PITCH];
+  int tile, h;
+  xcd_tile_head(blockIdx.x, H, tile, h);
+  if (tile >= *ntiles) return;
+  const int2 te = tiles[tile];
   const int b = te.x, q0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int q_last = min(q0 + A_BQ, hi) - 1;
+  const int q_last = min(q0 + F_BQ, hi) - 1;
   const int kv_end = key_end_for(q_last, s_end, r_end);
   const int qi = q0 + wave * 32 + l32;
   const bool qv = qi < hi;
-  const int64_t tq = qv ? ts[qi] : 0;
+  const int qr = qv ? qi : lo;
+  const int64_t tq = ts[qr];
   const int hc = h * DH;
 
-  op8 qop[DH / 16];
+  op8 qop[NS];
 #pragma unroll
-  for (int s = 0; s < DH / 16; ++s) {
-    if (qv) qop[s].v = *(const u32x4_t*)(Q + (int64_t)qi * ldqkv + hc + 16 * s + 8 * g);
-    else qop[s].v = u32x4_t{0, 0, 0, 0};
+  for (int s = 0; s < NS; ++s) {
+    u32x4_t v = *(const u32x4_t*)(Q + (int64_t)qr * ldqkv + hc + 16 * s + 8 * g);
+    qop[s].v = qv ? v : u32x4_t{0, 0, 0, 0};
   }
-  f32x16_t oacc[DH / 32];
+  f32x16_t oacc[NC];
 #pragma unroll
-  for (int c = 0; c < DH / 32; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) oacc[c][j] = 0.f;
 
-  constexpr int CH = 64 * (DH / 8) / 256;
-  uint4 rk[CH], rv[CH];
-  const int nkt = (kv_end - lo + A_BK - 1) / A_BK;
+  constexpr int CH = F_BK * (DH / 8) / 256;
+  uint4 rk[CH];
+  VtLoad<DH> rv;
+  const int nkt = (kv_end - lo + F_BK - 1) / F_BK;
+  // leading tiles made only of U/S keys need no mask test
+  const int nfull = min(nkt, max(0, (s_end - lo) / F_BK));
   if (nkt > 0) {
-    tile_gload<DH>(rk, K, ldqkv, lo, hi, hc, tid);
-    tile_gload<DH>(rv, V, ldqkv, lo, hi, hc, tid);
-    tile_swrite<DH, KP>(Ks[0], rk, tid);
-    tile_swrite<DH, VP>(Vs[0], rv, tid);
+    tile_gload_rows<DH, F_BK>(rk, K, ldqkv, lo, hi, hc, tid);
+    vt_gload<DH>(rv, V, ldqkv, lo, hi, hc, tid);
+    tile_swrite_rows<DH, F_BK, KP>(Ks[0], rk, tid);
+    vt_swrite<DH>(Vt[0], rv);
   }
   __syncthreads();
-  for (int it = 0; it < nkt; ++it) {
-    const int buf = it & 1, k0 = lo + it * A_BK;
+  for (int it = 0; it < nfull; ++it) {
+    const int buf = it & 1, k0 = lo + it * F_BK;
     const bool more = it + 1 < nkt;
     if (more) {
-      tile_gload<DH>(rk, K, ldqkv, k0 + A_BK, hi, hc, tid);
-      tile_gload<DH>(rv, V, ldqkv, k0 + A_BK, hi, hc, tid);
+      tile_gload_rows<DH, F_BK>(rk, K, ldqkv, k0 + F_BK, hi, hc, tid);
+      vt_gload<DH>(rv, V, ldqkv, k0 + F_BK, hi, hc, tid);
     }
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[t][j] = 0.f;
-#pragma unroll
-    for (int s = 0; s < DH / 16; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(row_operand<KP>(Ks[buf], t * 32, s, lane), qop[s], sacc[t]);
-    float p[2][16];
-    const bool full = k0 + A_BK <= s_end;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float sv = alpha * sacc[t][j];
-        float pv = sv * fast_sigmoid(sv);
-        if (!full) {
-          const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-          if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) pv = 0.f;
-        }
-        p[t][j] = pv;
-      }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const op8 pa = pack_kstep<T>(p, u);
-#pragma unroll
-      for (int c = 0; c < DH / 32; ++c) oacc[c] = mfma32<T>(pa, tr_operand<VP>(Vs[buf], 16 * u, c * 32, lane), oacc[c]);
-    }
+    fwd_tile<T, DH, false>(Ks[buf], Vt[buf], qop, oacc, k0, qi, tq, s_end, r_end, hi, ts, kexp, lane);
     if (more) {
-      tile_swrite<DH, KP>(Ks[buf ^ 1], rk, tid);
-      tile_swrite<DH, VP>(Vs[buf ^ 1], rv, tid);
+      tile_swrite_rows<DH, F_BK, KP>(Ks[buf ^ 1], rk, tid);
+      vt_swrite<DH>(Vt[buf ^ 1], rv);
+    }
+    __syncthreads();
+  }
+  for (int it = nfull; it < nkt; ++it) {
+    const int buf = it & 1, k0 = lo + it * F_BK;
+    const bool more = it + 1 < nkt;
+    if (more) {
+      tile_gload_rows<DH, F_BK>(rk, K, ldqkv, k0 + F_BK, hi, hc, tid);
+      vt_gload<DH>(rv, V, ldqkv, k0 + F_BK, hi, hc, tid);
+    }
+    fwd_tile<T, DH, true>(Ks[buf], Vt[buf], qop, oacc, k0, qi, tq, s_end, r_end, hi, ts, kexp, lane);
+    if (more) {
+      tile_swrite_rows<DH, F_BK, KP>(Ks[buf ^ 1], rk, tid);
+      vt_swrite<DH>(Vt[buf ^ 1], rv);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int c = 0; c < DH / 32; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int row = q0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (row < hi) O[(int64_t)row * ldo + hc + c * 32 + l32] = bits16<T>(oacc[c][j] * scale);
+      if (row < hi) O[(int64_t)row * ldo + hc + c * 32 + l32] = bits16<T>(oacc[c][j] * out_scale);
     }
 }
 
 // ---------------------------------------------------------------------------
-// backward, query-major: dQ = alpha * c * sum_j [M SiLU'(S) (dO v_j)] k_j
+// Loads of a 64-row tile in "quad" form: each thread owns 4 consecutive rows
+// x 8 columns, which serves both the row-major copy (A operands read 16 bytes
+// per lane) and the transposed copy (B operands whose contraction index is the
+// row).  Same lane assignment as vt_gload.
 // ---------------------------------------------------------------------------
+template <int DH>
+__device__ __forceinline__ void quad_swrite_rows(uint16_t* s, const VtLoad<DH>& L) {
+  constexpr int KP = AttnPitch<DH>::B128;
+  if (!L.on) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) *(uint4*)(s + (4 * L.kq + r) * KP + 8 * L.c) = L.x[r];
+}
+
+// ---------------------------------------------------------------------------
+// backward, query-major: dQ = alpha * c * sum_j [M SiLU'(S) (dO v_j)] k_j
+// for 128 queries (4 waves x 32), 64 keys per LDS stage.
+// ---------------------------------------------------------------------------
+template <typename T, int DH, bool MASKED>
+__device__ __forceinline__ void dq_tile(const uint16_t* Ks, const uint16_t* Vs, const uint16_t* Kt,
+                                        const op8 (&qop)[DH / 16], const op8 (&dop)[DH / 16],
+                                        f32x16_t (&acc)[DH / 32], int k0, int qi, int64_t tq, int s_end,
+                                        int r_end, int hi, const int64_t* __restrict__ ts, float kexp,
+                                        float alpha, int lane) {
+  constexpr int KP = AttnPitch<DH>::B128;
+  const int g = lane >> 5;
+  f32x16_t sacc[2], dacc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[t][j] = dacc[t][j] = 0.f;
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sacc[t] = mfma32<T>(row_operand<KP>(Ks, t * 32, s, lane), qop[s], sacc[t]);
+      dacc[t] = mfma32<T>(row_operand<KP>(Vs, t * 32, s, lane), dop[s], dacc[t]);
+    }
+  float ds[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float sr = sacc[t][j];
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
+      float v = dacc[t][j] * silu_grad_from(alpha * sr, sg);
+      if (MASKED) {
+        const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+        if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) v = 0.f;
+      }
+      ds[t][j] = v;
+    }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const op8 da = pack_kstep<T>(ds, u);
+#pragma unroll
+    for (int c = 0; c < DH / 32; ++c) acc[c] = mfma32<T>(da, vt_operand(Kt, u, c * 32, lane), acc[c]);
+  }
+}
+
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void attn_bwd_dq_mfma(
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dQ,
     int64_t lddq, const uint16_t* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
     const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-    float alpha, float scale) {
+    int H, float kexp, float alpha, float out_scale) {
   constexpr int KP = AttnPitch<DH>::B128;
+  constexpr int NS = DH / 16, NC = DH / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][A_BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][A_BK * KP];
-  if ((int)blockIdx.x >= *ntiles) return;
-  const int h = blockIdx.y;
-  const int2 te = tiles[blockIdx.x];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][DH * VT_PITCH];
+  int tile, h;
+  xcd_tile_head(blockIdx.x, H, tile, h);
+  if (tile >= *ntiles) return;
+  const int2 te = tiles[tile];
   const int b = te.x, q0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -237,90 +463,64 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(
   const int kv_end = key_end_for(q_last, s_end, r_end);
   const int qi = q0 + wave * 32 + l32;
   const bool qv = qi < hi;
-  const int64_t tq = qv ? ts[qi] : 0;
+  const int qr = qv ? qi : lo;
+  const int64_t tq = ts[qr];
   const int hc = h * DH;
 
-  op8 qop[DH / 16], dop[DH / 16];
+  op8 qop[NS], dop[NS];
 #pragma unroll
-  for (int s = 0; s < DH / 16; ++s) {
-    if (qv) {
-      qop[s].v = *(const u32x4_t*)(Q + (int64_t)qi * ldqkv + hc + 16 * s + 8 * g);
-      dop[s].v = *(const u32x4_t*)(dO + (int64_t)qi * lddo + hc + 16 * s + 8 * g);
-    } else {
-      qop[s].v = u32x4_t{0, 0, 0, 0};
-      dop[s].v = u32x4_t{0, 0, 0, 0};
-    }
+  for (int s = 0; s < NS; ++s) {
+    u32x4_t a = *(const u32x4_t*)(Q + (int64_t)qr * ldqkv + hc + 16 * s + 8 * g);
+    u32x4_t d = *(const u32x4_t*)(dO + (int64_t)qr * lddo + hc + 16 * s + 8 * g);
+    qop[s].v = qv ? a : u32x4_t{0, 0, 0, 0};
+    dop[s].v = qv ? d : u32x4_t{0, 0, 0, 0};
   }
-  f32x16_t acc[DH / 32];
+  f32x16_t acc[NC];
 #pragma unroll
-  for (int c = 0; c < DH / 32; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
 
-  constexpr int CH = 64 * (DH / 8) / 256;
-  uint4 rk[CH], rv[CH];
+  constexpr int CH = A_BK * (DH / 8) / 256;
+  uint4 rv[CH];
+  VtLoad<DH> rk;
   const int nkt = (kv_end - lo + A_BK - 1) / A_BK;
+  const int nfull = min(nkt, max(0, (s_end - lo) / A_BK));
   if (nkt > 0) {
-    tile_gload<DH>(rk, K, ldqkv, lo, hi, hc, tid);
-    tile_gload<DH>(rv, V, ldqkv, lo, hi, hc, tid);
-    tile_swrite<DH, KP>(Ks[0], rk, tid);
-    tile_swrite<DH, KP>(Vs[0], rv, tid);
+    vt_gload<DH>(rk, K, ldqkv, lo, hi, hc, tid);
+    tile_gload_rows<DH, A_BK>(rv, V, ldqkv, lo, hi, hc, tid);
+    quad_swrite_rows<DH>(Ks[0], rk);
+    vt_swrite<DH>(Kt[0], rk);
+    tile_swrite_rows<DH, A_BK, KP>(Vs[0], rv, tid);
   }
   __syncthreads();
   for (int it = 0; it < nkt; ++it) {
     const int buf = it & 1, k0 = lo + it * A_BK;
     const bool more = it + 1 < nkt;
     if (more) {
-      tile_gload<DH>(rk, K, ldqkv, k0 + A_BK, hi, hc, tid);
-      tile_gload<DH>(rv, V, ldqkv, k0 + A_BK, hi, hc, tid);
+      vt_gload<DH>(rk, K, ldqkv, k0 + A_BK, hi, hc, tid);
+      tile_gload_rows<DH, A_BK>(rv, V, ldqkv, k0 + A_BK, hi, hc, tid);
     }
-    f32x16_t sacc[2], dacc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[t][j] = dacc[t][j] = 0.f;
-#pragma unroll
-    for (int s = 0; s < DH / 16; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sacc[t] = mfma32<T>(row_operand<KP>(Ks[buf], t * 32, s, lane), qop[s], sacc[t]);
-        dacc[t] = mfma32<T>(row_operand<KP>(Vs[buf], t * 32, s, lane), dop[s], dacc[t]);
-      }
-    float ds[2][16];
-    const bool full = k0 + A_BK <= s_end;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float sv = alpha * sacc[t][j];
-        const float sg = fast_sigmoid(sv);
-        float v = dacc[t][j] * silu_grad_from(sv, sg);
-        if (!full) {
-          const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-          if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) v = 0.f;
-        }
-        ds[t][j] = v;
-      }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const op8 da = pack_kstep<T>(ds, u);
-#pragma unroll
-      for (int c = 0; c < DH / 32; ++c) acc[c] = mfma32<T>(da, tr_operand<KP>(Ks[buf], 16 * u, c * 32, lane), acc[c]);
-    }
+    if (it < nfull)
+      dq_tile<T, DH, false>(Ks[buf], Vs[buf], Kt[buf], qop, dop, acc, k0, qi, tq, s_end, r_end, hi, ts, kexp,
+                            alpha, lane);
+    else
+      dq_tile<T, DH, true>(Ks[buf], Vs[buf], Kt[buf], qop, dop, acc, k0, qi, tq, s_end, r_end, hi, ts, kexp,
+                           alpha, lane);
     if (more) {
-      tile_swrite<DH, KP>(Ks[buf ^ 1], rk, tid);
-      tile_swrite<DH, KP>(Vs[buf ^ 1], rv, tid);
+      quad_swrite_rows<DH>(Ks[buf ^ 1], rk);
+      vt_swrite<DH>(Kt[buf ^ 1], rk);
+      tile_swrite_rows<DH, A_BK, KP>(Vs[buf ^ 1], rv, tid);
     }
     __syncthreads();
   }
-  const float f = alpha * scale;
 #pragma unroll
-  for (int c = 0; c < DH / 32; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int row = q0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
       if (row < hi) {
-        float v = acc[c][j] * f;
+        float v = acc[c][j] * out_scale;
         const int col = hc + c * 32 + l32;
         if (zq) {
           const float z = from_bits16<T>(zq[(int64_t)row * ldz + col]);
@@ -333,7 +533,64 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(
 
 // ---------------------------------------------------------------------------
 // backward, key-major: dV = c P^T dO, dK = alpha c dS^T Q for 128 keys
+// (4 waves x 32 keys), 64 queries per LDS stage.
 // ---------------------------------------------------------------------------
+template <typename T, int DH, bool MASKED>
+__device__ __forceinline__ void dkdv_tile(const uint16_t* Qs, const uint16_t* Ds, const uint16_t* Qt,
+                                          const uint16_t* Dt, const op8 (&kop)[DH / 16],
+                                          const op8 (&vop)[DH / 16], f32x16_t (&dk)[DH / 32],
+                                          f32x16_t (&dv)[DH / 32], int q0, int qhi, int kj, bool kv,
+                                          int64_t tk, int s_end, int r_end, const int64_t* __restrict__ ts,
+                                          float kexp, float alpha, int lane) {
+  constexpr int QP = AttnPitch<DH>::B128;
+  const int g = lane >> 5;
+  f32x16_t sacc[2], dacc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc[t][j] = dacc[t][j] = 0.f;
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sacc[t] = mfma32<T>(row_operand<QP>(Qs, t * 32, s, lane), kop[s], sacc[t]);
+      dacc[t] = mfma32<T>(row_operand<QP>(Ds, t * 32, s, lane), vop[s], dacc[t]);
+    }
+  float p[2][16], ds[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float sr = sacc[t][j];
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
+      float pv = sr * sg;  // SiLU(alpha s) / alpha
+      float dsv = dacc[t][j] * silu_grad_from(alpha * sr, sg);
+      if (MASKED) {
+        const int qi = q0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+        bool vis = qi < qhi && kv;
+        if (vis) {
+          const int64_t tq = ts[qi];
+          if (kj < s_end) vis = true;
+          else if (kj < r_end) vis = qi >= s_end && (tk < tq || kj == qi);
+          else vis = kj == qi;
+        }
+        if (!vis) { pv = 0.f; dsv = 0.f; }
+      }
+      p[t][j] = pv;
+      ds[t][j] = dsv;
+    }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const op8 pa = pack_kstep<T>(p, u);
+    const op8 da = pack_kstep<T>(ds, u);
+#pragma unroll
+    for (int c = 0; c < DH / 32; ++c) {
+      dv[c] = mfma32<T>(pa, vt_operand(Dt, u, c * 32, lane), dv[c]);
+      dk[c] = mfma32<T>(da, vt_operand(Qt, u, c * 32, lane), dk[c]);
+    }
+  }
+}
+
 template <typename T, int DH>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -341,13 +598,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     uint16_t* __restrict__ dV, int64_t lddkv, const uint16_t* __restrict__ zk,
     const uint16_t* __restrict__ zv, int64_t ldz, const int32_t* __restrict__ seg,
     const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-    float alpha, float scale) {
+    int H, float kexp, float alpha, float scale) {
   constexpr int QP = AttnPitch<DH>::B128;
+  constexpr int NS = DH / 16, NC = DH / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][A_BQB * QP];
   __shared__ __attribute__((aligned(16))) uint16_t Ds[2][A_BQB * QP];
-  if ((int)blockIdx.x >= *ntiles) return;
-  const int h = blockIdx.y;
-  const int2 te = tiles[blockIdx.x];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][DH * VT_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][DH * VT_PITCH];
+  int tile, h;
+  xcd_tile_head(blockIdx.x, H, tile, h);
+  if (tile >= *ntiles) return;
+  const int2 te = tiles[tile];
   const int b = te.x, k0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
@@ -358,98 +619,61 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
   else { qlo = k0; qhi = k_last + 1; }               // candidate keys: themselves
   const int kj = k0 + wave * 32 + l32;
   const bool kv = kj < hi;
-  const int64_t tk = kv ? ts[kj] : 0;
+  const int kr = kv ? kj : lo;
+  const int64_t tk = ts[kr];
   const int hc = h * DH;
 
-  op8 kop[DH / 16], vop[DH / 16];
+  op8 kop[NS], vop[NS];
 #pragma unroll
-  for (int s = 0; s < DH / 16; ++s) {
-    if (kv) {
-      kop[s].v = *(const u32x4_t*)(K + (int64_t)kj * ldqkv + hc + 16 * s + 8 * g);
-      vop[s].v = *(const u32x4_t*)(V + (int64_t)kj * ldqkv + hc + 16 * s + 8 * g);
-    } else {
-      kop[s].v = u32x4_t{0, 0, 0, 0};
-      vop[s].v = u32x4_t{0, 0, 0, 0};
-    }
+  for (int s = 0; s < NS; ++s) {
+    u32x4_t a = *(const u32x4_t*)(K + (int64_t)kr * ldqkv + hc + 16 * s + 8 * g);
+    u32x4_t v = *(const u32x4_t*)(V + (int64_t)kr * ldqkv + hc + 16 * s + 8 * g);
+    kop[s].v = kv ? a : u32x4_t{0, 0, 0, 0};
+    vop[s].v = kv ? v : u32x4_t{0, 0, 0, 0};
   }
-  f32x16_t dk[DH / 32], dv[DH / 32];
+  f32x16_t dk[NC], dv[NC];
 #pragma unroll
-  for (int c = 0; c < DH / 32; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) dk[c][j] = dv[c][j] = 0.f;
 
-  constexpr int CH = 64 * (DH / 8) / 256;
-  uint4 rq[CH], rd[CH];
+  VtLoad<DH> rq, rd;
   const int nqt = (qhi - qlo + A_BQB - 1) / A_BQB;
+  // every query sees keys that are all U/S
+  const bool full = k0 + A_BKW <= s_end;
   if (nqt > 0) {
-    tile_gload<DH>(rq, Q, ldqkv, qlo, qhi, hc, tid);
-    tile_gload<DH>(rd, dO, lddo, qlo, qhi, hc, tid);
-    tile_swrite<DH, QP>(Qs[0], rq, tid);
-    tile_swrite<DH, QP>(Ds[0], rd, tid);
+    vt_gload<DH>(rq, Q, ldqkv, qlo, qhi, hc, tid);
+    vt_gload<DH>(rd, dO, lddo, qlo, qhi, hc, tid);
+    quad_swrite_rows<DH>(Qs[0], rq);
+    vt_swrite<DH>(Qt[0], rq);
+    quad_swrite_rows<DH>(Ds[0], rd);
+    vt_swrite<DH>(Dt[0], rd);
   }
   __syncthreads();
-  const bool full = k0 + A_BKW <= s_end;
   for (int it = 0; it < nqt; ++it) {
     const int buf = it & 1, q0 = qlo + it * A_BQB;
     const bool more = it + 1 < nqt;
     if (more) {
-      tile_gload<DH>(rq, Q, ldqkv, q0 + A_BQB, qhi, hc, tid);
-      tile_gload<DH>(rd, dO, lddo, q0 + A_BQB, qhi, hc, tid);
+      vt_gload<DH>(rq, Q, ldqkv, q0 + A_BQB, qhi, hc, tid);
+      vt_gload<DH>(rd, dO, lddo, q0 + A_BQB, qhi, hc, tid);
     }
-    f32x16_t sacc[2], dacc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[t][j] = dacc[t][j] = 0.f;
-#pragma unroll
-    for (int s = 0; s < DH / 16; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sacc[t] = mfma32<T>(row_operand<QP>(Qs[buf], t * 32, s, lane), kop[s], sacc[t]);
-        dacc[t] = mfma32<T>(row_operand<QP>(Ds[buf], t * 32, s, lane), vop[s], dacc[t]);
-      }
-    float p[2][16], ds[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float sv = alpha * sacc[t][j];
-        const float sg = fast_sigmoid(sv);
-        float pv = sv * sg;
-        float dsv = dacc[t][j] * silu_grad_from(sv, sg);
-        if (!full) {
-          const int qi = q0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-          bool vis = qi < qhi && kv;
-          if (vis) {
-            const int64_t tq = ts[qi];
-            if (kj < s_end) vis = true;
-            else if (kj < r_end) vis = qi >= s_end && (tk < tq || kj == qi);
-            else vis = kj == qi;
-          }
-          if (!vis) { pv = 0.f; dsv = 0.f; }
-        }
-        p[t][j] = pv;
-        ds[t][j] = dsv;
-      }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const op8 pa = pack_kstep<T>(p, u);
-      const op8 da = pack_kstep<T>(ds, u);
-#pragma unroll
-      for (int c = 0; c < DH / 32; ++c) {
-        dv[c] = mfma32<T>(pa, tr_operand<QP>(Ds[buf], 16 * u, c * 32, lane), dv[c]);
-        dk[c] = mfma32<T>(da, tr_operand<QP>(Qs[buf], 16 * u, c * 32, lane), dk[c]);
-      }
-    }
+    if (full)
+      dkdv_tile<T, DH, false>(Qs[buf], Ds[buf], Qt[buf], Dt[buf], kop, vop, dk, dv, q0, qhi, kj, kv, tk, s_end,
+                              r_end, ts, kexp, alpha, lane);
+    else
+      dkdv_tile<T, DH, true>(Qs[buf], Ds[buf], Qt[buf], Dt[buf], kop, vop, dk, dv, q0, qhi, kj, kv, tk, s_end,
+                             r_end, ts, kexp, alpha, lane);
     if (more) {
-      tile_swrite<DH, QP>(Qs[buf ^ 1], rq, tid);
-      tile_swrite<DH, QP>(Ds[buf ^ 1], rd, tid);
+      quad_swrite_rows<DH>(Qs[buf ^ 1], rq);
+      vt_swrite<DH>(Qt[buf ^ 1], rq);
+      quad_swrite_rows<DH>(Ds[buf ^ 1], rd);
+      vt_swrite<DH>(Dt[buf ^ 1], rd);
     }
     __syncthreads();
   }
-  const float fk = alpha * scale, fv = scale;
+  const float fk = alpha * scale, fv = alpha * scale;
 #pragma unroll
-  for (int c = 0; c < DH / 32; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int row = k0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
@@ -598,28 +822,31 @@ __global__ void attn_bwd_dkdv_f32(const float* __restrict__ Q, const float* __re
 // ---------------------------------------------------------------------------
 template <typename T, int DH>
 static void fwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
-  dim3 grid((unsigned)pv.max_tiles, a.H);
+  // SiLU(alpha s) = alpha * s * sigmoid(alpha s); sigmoid via exp2 with the
+  // factor -alpha*log2(e) folded in; alpha and the normaliser scale O once.
+  const float kexp = -a.alpha * 1.4426950408889634f;
   ProfScope ps("attn_fwd", st);
-  hipLaunchKernelGGL((attn_fwd_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (uint16_t*)a.o, a.ldo, pv.seg,
-                     a.ts, pv.tiles, pv.ntiles, a.alpha, a.scale);
+  hipLaunchKernelGGL((attn_fwd_mfma<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(256), 0, st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (uint16_t*)a.o,
+                     a.ldo, pv.seg, a.ts, pv.q.tiles, pv.q.ntiles, a.H, kexp, a.alpha * a.scale);
 }
 
 template <typename T, int DH>
 static void bwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
-  dim3 grid((unsigned)pv.max_tiles, a.H);
+  const float kexp = -a.alpha * 1.4426950408889634f;
   {
     ProfScope ps("attn_bwd_dkdv", st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (const uint16_t*)a.d_o, a.lddo,
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv, (const uint16_t*)a.zk,
-                       (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.tiles, pv.ntiles, a.alpha, a.scale);
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH>), dim3(xcd_grid(pv.k.max_tiles, a.H)), dim3(256), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
+                       (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv,
+                       (const uint16_t*)a.zk, (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.k.tiles, pv.k.ntiles,
+                       a.H, kexp, a.alpha, a.scale);
   }
   ProfScope ps("attn_bwd_dq", st);
-  hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (const uint16_t*)a.d_o, a.lddo,
-                     (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg, a.ts, pv.tiles,
-                     pv.ntiles, a.alpha, a.scale);
+  hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(256), 0, st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
+                     (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg,
+                     a.ts, pv.q.tiles, pv.q.ntiles, a.H, kexp, a.alpha, a.alpha * a.scale);
 }
 
 template <int DH>

@@ -24,19 +24,24 @@ class ProfScope {
 
 // Rows per attention tile: queries per forward / dQ workgroup, keys per
 // dK/dV workgroup.
-constexpr int ATTN_TILE_ROWS = 128;
+constexpr int ATTN_QTILE = 128;
+constexpr int ATTN_KTILE = 128;
 
-// ---- a1: segments and tile list ----------------------------------------
-struct PrepView {
-  int32_t* seg;      // [B, 5]
-  int32_t* ntiles;   // [1] number of valid entries in tiles
-  int2* tiles;       // [max_tiles] (user, first row), longest users first
+// ---- a1: segments and tile lists -----------------------------------------
+struct TileList {
+  int32_t* ntiles;   // [1] number of valid entries
+  int2* tiles;       // (user, first row) of each tile, longest users first
   int64_t max_tiles; // host-side upper bound on *ntiles
 };
+struct PrepView {
+  int32_t* seg;      // [B, 5]
+  TileList q;        // ATTN_QTILE-row tiles
+  TileList k;        // ATTN_KTILE-row tiles
+};
 int64_t max_tiles(int B, int64_t T, int rows_per_tile);
-size_t prep_workspace_bytes(int B, int64_t T, int rows_per_tile);
-int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t T, int rows_per_tile,
-                void* ws, hipStream_t stream, PrepView* out);
+size_t prep_workspace_bytes(int B, int64_t T);
+int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t T, void* ws,
+                hipStream_t stream, PrepView* out);
 int launch_seg_only(const int32_t* offsets, const uint8_t* group_ids, int B, int32_t* seg,
                     hipStream_t stream);
 

@@ -110,37 +110,45 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
   if (tid == 0) *ntiles = carry;
 }
 
-size_t prep_workspace_bytes(int B, int64_t T, int rows_per_tile) {
-  size_t n = 0;
-  n += align_up((size_t)B * 5 * sizeof(int32_t), 256);      // seg
-  n += 256;                                                    // tile count
-  n += align_up((size_t)B * sizeof(int32_t), 256);           // order scratch
-  n += align_up((size_t)max_tiles(B, T, rows_per_tile) * sizeof(int2), 256);
-  return n;
-}
-
 int64_t max_tiles(int B, int64_t T, int rows_per_tile) {
   return (T + rows_per_tile - 1) / rows_per_tile + B;
 }
 
-int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t T,
-                int rows_per_tile, void* ws, hipStream_t stream, PrepView* out) {
+size_t prep_workspace_bytes(int B, int64_t T) {
+  size_t n = 0;
+  n += align_up((size_t)B * 5 * sizeof(int32_t), 256);      // seg
+  n += 256;                                                    // tile counts
+  n += align_up((size_t)B * sizeof(int32_t), 256);           // order scratch
+  n += align_up((size_t)max_tiles(B, T, ATTN_QTILE) * sizeof(int2), 256);
+  n += align_up((size_t)max_tiles(B, T, ATTN_KTILE) * sizeof(int2), 256);
+  return n;
+}
+
+int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t T, void* ws,
+                hipStream_t stream, PrepView* out) {
   char* p = (char*)ws;
   out->seg = (int32_t*)p;
   p += align_up((size_t)B * 5 * sizeof(int32_t), 256);
-  out->ntiles = (int32_t*)p;
+  out->q.ntiles = (int32_t*)p;
+  out->k.ntiles = (int32_t*)p + 1;
   p += 256;
   int32_t* order = (int32_t*)p;
   p += align_up((size_t)B * sizeof(int32_t), 256);
-  out->tiles = (int2*)p;
-  out->max_tiles = max_tiles(B, T, rows_per_tile);
+  out->q.tiles = (int2*)p;
+  out->q.max_tiles = max_tiles(B, T, ATTN_QTILE);
+  p += align_up((size_t)out->q.max_tiles * sizeof(int2), 256);
+  out->k.tiles = (int2*)p;
+  out->k.max_tiles = max_tiles(B, T, ATTN_KTILE);
   if (B > 0) {
     hipLaunchKernelGGL(seg_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, offsets, group_ids, B,
                        out->seg);
     MTGR_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, rows_per_tile, order,
-                     out->tiles, out->ntiles);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, ATTN_QTILE, order,
+                     out->q.tiles, out->q.ntiles);
+  MTGR_LAUNCH_CHECK();
+  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, ATTN_KTILE, order,
+                     out->k.tiles, out->k.ntiles);
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
 }
