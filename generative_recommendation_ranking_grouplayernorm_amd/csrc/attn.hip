@@ -147,22 +147,26 @@ inline unsigned xcd_grid(int64_t max_tiles, int H) {
   return (unsigned)(max_tiles * H);
 }
 
-// Branch-free tile load: rows at or beyond rlim read as zero (the address is
-// clamped to a valid row so that no lane issues an out-of-range access).
+// Buffer resource over rows [r0, rlim) of a row-major [.., ld] 16-bit array,
+// starting at column col0: rows at or beyond rlim read as zero.  The row
+// range is wave-uniform, so advancing a tile changes only scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* P, int64_t ld, int r0, int rlim,
+                                                         int col0) {
+  return make_rsrc(P + (int64_t)r0 * ld + col0, (int)((int64_t)(rlim - r0) * ld * 2));
+}
+
+// Tile load: thread chunks c = tid + 256 i, row c / (DH/8), 8 columns.
 template <int DH, int ROWS>
 __device__ __forceinline__ void tile_gload_rows(uint4* r, const uint16_t* __restrict__ P, int64_t ld, int r0,
                                                 int rlim, int col0, int tid) {
   constexpr int CPR = DH / 8;
   constexpr int CH = ROWS * CPR / 256;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(P, ld, r0, rlim, col0);
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = tid + 256 * i;
     const int row = c / CPR, col = (c % CPR) * 8;
-    const int gr = r0 + row;
-    const int cr = gr < rlim ? gr : rlim - 1;
-    uint4 v = *(const uint4*)(P + (int64_t)cr * ld + col0 + col);
-    if (gr >= rlim) v = make_uint4(0, 0, 0, 0);
-    r[i] = v;
+    r[i] = buf_load16(rs, (row * (int)ld + col) * 2);
   }
 }
 template <int DH, int ROWS, int PITCH>
@@ -211,14 +215,10 @@ __device__ __forceinline__ void vt_gload(VtLoad<DH>& L, const uint16_t* __restri
   L.kq = lane & 15;
   L.c = 4 * w + 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
   L.on = L.c < DH / 8;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(V, ld, k0, rlim, col0);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int gr = k0 + 4 * L.kq + r;
-    const int cr = gr < rlim ? gr : rlim - 1;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (L.on) v = *(const uint4*)(V + (int64_t)cr * ld + col0 + 8 * L.c);
-    L.x[r] = gr < rlim ? v : make_uint4(0, 0, 0, 0);
-  }
+  for (int r = 0; r < 4; ++r)
+    L.x[r] = L.on ? buf_load16(rs, ((4 * L.kq + r) * (int)ld + 8 * L.c) * 2) : make_uint4(0, 0, 0, 0);
 }
 
 template <int DH>
@@ -265,11 +265,9 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt,
   const int g = lane >> 5;
   f32x16_t sacc[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(row_operand<KP>(Ks, t * 32, 0, lane), qop[0], f32x16_t{});
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[t][j] = 0.f;
-#pragma unroll
-  for (int s = 0; s < DH / 16; ++s)
+  for (int s = 1; s < DH / 16; ++s)
 #pragma unroll
     for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(row_operand<KP>(Ks, t * 32, s, lane), qop[s], sacc[t]);
   float p[2][16];
@@ -406,42 +404,48 @@ __device__ __forceinline__ void dq_tile(const uint16_t* Ks, const uint16_t* Vs, 
                                         float alpha, int lane) {
   constexpr int KP = AttnPitch<DH>::B128;
   const int g = lane >> 5;
-  f32x16_t sacc[2], dacc[2];
+  // one 32-key half of the tile at a time keeps the live accumulators small
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 2; ++t) {
+    f32x16_t sacc = mfma32<T>(row_operand<KP>(Ks, t * 32, 0, lane), qop[0], f32x16_t{});
+    f32x16_t dacc = mfma32<T>(row_operand<KP>(Vs, t * 32, 0, lane), dop[0], f32x16_t{});
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[t][j] = dacc[t][j] = 0.f;
-#pragma unroll
-  for (int s = 0; s < DH / 16; ++s)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sacc[t] = mfma32<T>(row_operand<KP>(Ks, t * 32, s, lane), qop[s], sacc[t]);
-      dacc[t] = mfma32<T>(row_operand<KP>(Vs, t * 32, s, lane), dop[s], dacc[t]);
+    for (int s = 1; s < DH / 16; ++s) {
+      sacc = mfma32<T>(row_operand<KP>(Ks, t * 32, s, lane), qop[s], sacc);
+      dacc = mfma32<T>(row_operand<KP>(Vs, t * 32, s, lane), dop[s], dacc);
     }
-  float ds[2][16];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
+    float ds[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float sr = sacc[t][j];
+      const float sr = sacc[j];
       const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
-      float v = dacc[t][j] * silu_grad_from(alpha * sr, sg);
+      float v = dacc[j] * silu_grad_from(alpha * sr, sg);
       if (MASKED) {
         const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
         if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) v = 0.f;
       }
-      ds[t][j] = v;
+      ds[j] = v;
     }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const op8 da = pack_kstep<T>(ds, u);
+    for (int uu = 0; uu < 2; ++uu) {
+      op8 da;
 #pragma unroll
-    for (int c = 0; c < DH / 32; ++c) acc[c] = mfma32<T>(da, vt_operand(Kt, u, c * 32, lane), acc[c]);
+      for (int e = 0; e < 4; ++e) da.v[e] = pack2<T>(ds[8 * uu + 2 * e], ds[8 * uu + 2 * e + 1]);
+#pragma unroll
+      for (int c = 0; c < DH / 32; ++c)
+        acc[c] = mfma32<T>(da, vt_operand(Kt, 2 * t + uu, c * 32, lane), acc[c]);
+    }
   }
 }
 
+// 512 threads, 256 queries (8 waves x 32): the K/V tiles are shared by 8
+// waves and each wave stays under 256 registers, so two waves share a SIMD
+// and one's SiLU' arithmetic overlaps the other's MFMAs.  Waves 0-3 load K
+// (written both row-major and transposed), waves 4-7 load V.
+constexpr int DQ_BQ = 256;
+
 template <typename T, int DH>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_mfma(
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dQ,
     int64_t lddq, const uint16_t* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
@@ -459,9 +463,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_mfma(
   const int b = te.x, q0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int q_last = min(q0 + A_BQ, hi) - 1;
+  const bool loads_k = wave < 4;
+  const int ltid = tid & 255;
+  const int q_last = min(q0 + DQ_BQ, hi) - 1;
   const int kv_end = key_end_for(q_last, s_end, r_end);
-  const int qi = q0 + wave * 32 + l32;
+  const int qw = q0 + wave * 32;
+  const bool active = qw < hi;
+  const int qi = qw + l32;
   const bool qv = qi < hi;
   const int qr = qv ? qi : lo;
   const int64_t tq = ts[qr];
@@ -481,44 +489,47 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_mfma(
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
 
-  constexpr int CH = A_BK * (DH / 8) / 256;
-  uint4 rv[CH];
-  VtLoad<DH> rk;
+  VtLoad<DH> ld;  // K quads (waves 0-3) or V rows (waves 4-7, in ld.x)
+  auto gload = [&](int k0) {
+    if (loads_k) vt_gload<DH>(ld, K, ldqkv, k0, hi, hc, ltid);
+    else tile_gload_rows<DH, A_BK>(ld.x, V, ldqkv, k0, hi, hc, ltid);
+  };
+  auto swrite = [&](int buf) {
+    if (loads_k) {
+      quad_swrite_rows<DH>(Ks[buf], ld);
+      vt_swrite<DH>(Kt[buf], ld);
+    } else {
+      tile_swrite_rows<DH, A_BK, KP>(Vs[buf], ld.x, ltid);
+    }
+  };
   const int nkt = (kv_end - lo + A_BK - 1) / A_BK;
   const int nfull = min(nkt, max(0, (s_end - lo) / A_BK));
   if (nkt > 0) {
-    vt_gload<DH>(rk, K, ldqkv, lo, hi, hc, tid);
-    tile_gload_rows<DH, A_BK>(rv, V, ldqkv, lo, hi, hc, tid);
-    quad_swrite_rows<DH>(Ks[0], rk);
-    vt_swrite<DH>(Kt[0], rk);
-    tile_swrite_rows<DH, A_BK, KP>(Vs[0], rv, tid);
+    gload(lo);
+    swrite(0);
   }
   __syncthreads();
   for (int it = 0; it < nkt; ++it) {
     const int buf = it & 1, k0 = lo + it * A_BK;
     const bool more = it + 1 < nkt;
-    if (more) {
-      vt_gload<DH>(rk, K, ldqkv, k0 + A_BK, hi, hc, tid);
-      tile_gload_rows<DH, A_BK>(rv, V, ldqkv, k0 + A_BK, hi, hc, tid);
+    if (more) gload(k0 + A_BK);
+    if (active) {
+      if (it < nfull)
+        dq_tile<T, DH, false>(Ks[buf], Vs[buf], Kt[buf], qop, dop, acc, k0, qi, tq, s_end, r_end, hi, ts, kexp,
+                              alpha, lane);
+      else
+        dq_tile<T, DH, true>(Ks[buf], Vs[buf], Kt[buf], qop, dop, acc, k0, qi, tq, s_end, r_end, hi, ts, kexp,
+                             alpha, lane);
     }
-    if (it < nfull)
-      dq_tile<T, DH, false>(Ks[buf], Vs[buf], Kt[buf], qop, dop, acc, k0, qi, tq, s_end, r_end, hi, ts, kexp,
-                            alpha, lane);
-    else
-      dq_tile<T, DH, true>(Ks[buf], Vs[buf], Kt[buf], qop, dop, acc, k0, qi, tq, s_end, r_end, hi, ts, kexp,
-                           alpha, lane);
-    if (more) {
-      quad_swrite_rows<DH>(Ks[buf ^ 1], rk);
-      vt_swrite<DH>(Kt[buf ^ 1], rk);
-      tile_swrite_rows<DH, A_BK, KP>(Vs[buf ^ 1], rv, tid);
-    }
+    if (more) swrite(buf ^ 1);
     __syncthreads();
   }
+  if (!active) return;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int row = q0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+      const int row = qw + 8 * (j >> 2) + 4 * g + (j & 3);
       if (row < hi) {
         float v = acc[c][j] * out_scale;
         const int col = hc + c * 32 + l32;
@@ -532,67 +543,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_mfma(
 }
 
 // ---------------------------------------------------------------------------
-// backward, key-major: dV = c P^T dO, dK = alpha c dS^T Q for 128 keys
-// (4 waves x 32 keys), 64 queries per LDS stage.
+// backward, key-major: dV = c P^T dO, dK = alpha c dS^T Q for 128 keys, 64
+// queries per LDS stage.  512 threads in producer/consumer pairs: wave i
+// (i < 4) computes S for key group i, the SiLU weights P and the factor
+// f = M * SiLU'(alpha s) (written to LDS as f16), then dV; wave i + 4
+// computes dA = dO V^T for the same keys, reads f, forms dS = dA * f, then dK.
+// Each wave holds only half of the per-key state, so two waves fit per SIMD.
 // ---------------------------------------------------------------------------
-template <typename T, int DH, bool MASKED>
-__device__ __forceinline__ void dkdv_tile(const uint16_t* Qs, const uint16_t* Ds, const uint16_t* Qt,
-                                          const uint16_t* Dt, const op8 (&kop)[DH / 16],
-                                          const op8 (&vop)[DH / 16], f32x16_t (&dk)[DH / 32],
-                                          f32x16_t (&dv)[DH / 32], int q0, int qhi, int kj, bool kv,
-                                          int64_t tk, int s_end, int r_end, const int64_t* __restrict__ ts,
-                                          float kexp, float alpha, int lane) {
-  constexpr int QP = AttnPitch<DH>::B128;
-  const int g = lane >> 5;
-  f32x16_t sacc[2], dacc[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) sacc[t][j] = dacc[t][j] = 0.f;
-#pragma unroll
-  for (int s = 0; s < DH / 16; ++s)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sacc[t] = mfma32<T>(row_operand<QP>(Qs, t * 32, s, lane), kop[s], sacc[t]);
-      dacc[t] = mfma32<T>(row_operand<QP>(Ds, t * 32, s, lane), vop[s], dacc[t]);
-    }
-  float p[2][16], ds[2][16];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float sr = sacc[t][j];
-      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
-      float pv = sr * sg;  // SiLU(alpha s) / alpha
-      float dsv = dacc[t][j] * silu_grad_from(alpha * sr, sg);
-      if (MASKED) {
-        const int qi = q0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-        bool vis = qi < qhi && kv;
-        if (vis) {
-          const int64_t tq = ts[qi];
-          if (kj < s_end) vis = true;
-          else if (kj < r_end) vis = qi >= s_end && (tk < tq || kj == qi);
-          else vis = kj == qi;
-        }
-        if (!vis) { pv = 0.f; dsv = 0.f; }
-      }
-      p[t][j] = pv;
-      ds[t][j] = dsv;
-    }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const op8 pa = pack_kstep<T>(p, u);
-    const op8 da = pack_kstep<T>(ds, u);
-#pragma unroll
-    for (int c = 0; c < DH / 32; ++c) {
-      dv[c] = mfma32<T>(pa, vt_operand(Dt, u, c * 32, lane), dv[c]);
-      dk[c] = mfma32<T>(da, vt_operand(Qt, u, c * 32, lane), dk[c]);
-    }
-  }
-}
+constexpr int KV_BK = 128;    // keys per workgroup (4 groups of 32)
+constexpr int KV_BQ = 64;     // queries per LDS stage
+constexpr int F_PITCH = 64;   // f16 exchange tile: [key group][64 queries][32 keys]
 
 template <typename T, int DH>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int64_t lddkv, const uint16_t* __restrict__ zk,
@@ -601,10 +564,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
     int H, float kexp, float alpha, float scale) {
   constexpr int QP = AttnPitch<DH>::B128;
   constexpr int NS = DH / 16, NC = DH / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][A_BQB * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][A_BQB * QP];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][KV_BQ * QP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][KV_BQ * QP];
   __shared__ __attribute__((aligned(16))) uint16_t Qt[2][DH * VT_PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Dt[2][DH * VT_PITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t Fx[4][32 * 16 * 2];  // per group: 2 x 16 x 32 lanes
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
@@ -612,82 +576,142 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_mfma(
   const int b = te.x, k0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const int k_last = min(k0 + A_BKW, hi) - 1;
+  const bool producer = wave < 4;   // S-side wave; wave + 4 is its dA-side partner
+  const int grp = wave & 3;
+  const int ltid = tid & 255;
+  const int k_last = min(k0 + KV_BK, hi) - 1;
   int qlo, qhi;
   if (k0 < s_end) { qlo = lo; qhi = hi; }            // static keys: every query
   else if (k0 < r_end) { qlo = s_end; qhi = hi; }    // real-time keys: R and C queries
   else { qlo = k0; qhi = k_last + 1; }               // candidate keys: themselves
-  const int kj = k0 + wave * 32 + l32;
+  const int kj = k0 + grp * 32 + l32;
   const bool kv = kj < hi;
   const int kr = kv ? kj : lo;
   const int64_t tk = ts[kr];
   const int hc = h * DH;
+  const bool full = k0 + KV_BK <= s_end;  // every query sees these keys
 
-  op8 kop[NS], vop[NS];
+  // producer: K of its keys (B operand of S = Q K^T); consumer: V (B of dA)
+  op8 bop[NS];
+  {
+    const uint16_t* src = producer ? K : V;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4_t a = *(const u32x4_t*)(K + (int64_t)kr * ldqkv + hc + 16 * s + 8 * g);
-    u32x4_t v = *(const u32x4_t*)(V + (int64_t)kr * ldqkv + hc + 16 * s + 8 * g);
-    kop[s].v = kv ? a : u32x4_t{0, 0, 0, 0};
-    vop[s].v = kv ? v : u32x4_t{0, 0, 0, 0};
+    for (int s = 0; s < NS; ++s) {
+      u32x4_t a = *(const u32x4_t*)(src + (int64_t)kr * ldqkv + hc + 16 * s + 8 * g);
+      bop[s].v = kv ? a : u32x4_t{0, 0, 0, 0};
+    }
   }
-  f32x16_t dk[NC], dv[NC];
+  f32x16_t acc[NC];  // producer: dV, consumer: dK
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) dk[c][j] = dv[c][j] = 0.f;
+    for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
 
-  VtLoad<DH> rq, rd;
-  const int nqt = (qhi - qlo + A_BQB - 1) / A_BQB;
-  // every query sees keys that are all U/S
-  const bool full = k0 + A_BKW <= s_end;
+  VtLoad<DH> ld;  // producers load Q quads, consumers dO quads
+  auto gload = [&](int q0) {
+    if (producer) vt_gload<DH>(ld, Q, ldqkv, q0, qhi, hc, ltid);
+    else vt_gload<DH>(ld, dO, lddo, q0, qhi, hc, ltid);
+  };
+  auto swrite = [&](int buf) {
+    if (producer) {
+      quad_swrite_rows<DH>(Qs[buf], ld);
+      vt_swrite<DH>(Qt[buf], ld);
+    } else {
+      quad_swrite_rows<DH>(Ds[buf], ld);
+      vt_swrite<DH>(Dt[buf], ld);
+    }
+  };
+  const int nqt = (qhi - qlo + KV_BQ - 1) / KV_BQ;
   if (nqt > 0) {
-    vt_gload<DH>(rq, Q, ldqkv, qlo, qhi, hc, tid);
-    vt_gload<DH>(rd, dO, lddo, qlo, qhi, hc, tid);
-    quad_swrite_rows<DH>(Qs[0], rq);
-    vt_swrite<DH>(Qt[0], rq);
-    quad_swrite_rows<DH>(Ds[0], rd);
-    vt_swrite<DH>(Dt[0], rd);
+    gload(qlo);
+    swrite(0);
   }
   __syncthreads();
+  uint32_t* fx = Fx[grp];
   for (int it = 0; it < nqt; ++it) {
-    const int buf = it & 1, q0 = qlo + it * A_BQB;
+    const int buf = it & 1, q0 = qlo + it * KV_BQ;
     const bool more = it + 1 < nqt;
-    if (more) {
-      vt_gload<DH>(rq, Q, ldqkv, q0 + A_BQB, qhi, hc, tid);
-      vt_gload<DH>(rd, dO, lddo, q0 + A_BQB, qhi, hc, tid);
+    if (more) gload(q0 + KV_BQ);
+    // phase 1: S (producer) or dA (consumer) for 64 queries x 32 keys
+    const uint16_t* A = producer ? Qs[buf] : Ds[buf];
+    f32x16_t x[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<QP>(A, t * 32, 0, lane), bop[0], f32x16_t{});
+#pragma unroll
+    for (int s = 1; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<QP>(A, t * 32, s, lane), bop[s], x[t]);
+    op8 w[4];
+    if (producer) {
+      float p[2][16];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float sr = x[t][j];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
+          float pv = sr * sg;                          // SiLU(alpha s) / alpha
+          float f = silu_grad_from(alpha * sr, sg);    // SiLU'(alpha s)
+          if (!full) {
+            const int qi = q0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+            bool vis = qi < qhi && kv;
+            if (vis) {
+              if (kj < s_end) vis = true;
+              else if (kj < r_end) vis = qi >= s_end && (tk < ts[qi] || kj == qi);
+              else vis = kj == qi;
+            }
+            if (!vis) { pv = 0.f; f = 0.f; }
+          }
+          p[t][j] = pv;
+          x[t][j] = f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          fx[(t * 8 + e) * 64 + lane] = pack2<f16_t>(x[t][2 * e], x[t][2 * e + 1]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = pack_kstep<T>(p, u);
     }
-    if (full)
-      dkdv_tile<T, DH, false>(Qs[buf], Ds[buf], Qt[buf], Dt[buf], kop, vop, dk, dv, q0, qhi, kj, kv, tk, s_end,
-                              r_end, ts, kexp, alpha, lane);
-    else
-      dkdv_tile<T, DH, true>(Qs[buf], Ds[buf], Qt[buf], Dt[buf], kop, vop, dk, dv, q0, qhi, kj, kv, tk, s_end,
-                             r_end, ts, kexp, alpha, lane);
-    if (more) {
-      quad_swrite_rows<DH>(Qs[buf ^ 1], rq);
-      vt_swrite<DH>(Qt[buf ^ 1], rq);
-      quad_swrite_rows<DH>(Ds[buf ^ 1], rd);
-      vt_swrite<DH>(Dt[buf ^ 1], rd);
+    __syncthreads();  // f of this stage visible to the consumers
+    if (!producer) {
+      float d[2][16];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t fv = fx[(t * 8 + e) * 64 + lane];
+          d[t][2 * e] = x[t][2 * e] * from_bits16<f16_t>((uint16_t)(fv & 0xffff));
+          d[t][2 * e + 1] = x[t][2 * e + 1] * from_bits16<f16_t>((uint16_t)(fv >> 16));
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = pack_kstep<T>(d, u);
     }
+    // phase 2: dV += P^T dO (producer) or dK += dS^T Q (consumer)
+    const uint16_t* Bt = producer ? Dt[buf] : Qt[buf];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], vt_operand(Bt, u, c * 32, lane), acc[c]);
+    if (more) swrite(buf ^ 1);
     __syncthreads();
   }
-  const float fk = alpha * scale, fv = alpha * scale;
+  // producer holds dV, consumer dK; both scale by alpha * c
+  const float f = alpha * scale;
+  const uint16_t* z = producer ? zv : zk;
+  uint16_t* dst = producer ? dV : dK;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int row = k0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+      const int row = k0 + grp * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
       if (row < hi) {
         const int col = hc + c * 32 + l32;
-        float a = dk[c][j] * fk, bv = dv[c][j] * fv;
-        if (zk) {
-          const float z1 = from_bits16<T>(zk[(int64_t)row * ldz + col]);
-          const float z2 = from_bits16<T>(zv[(int64_t)row * ldz + col]);
-          a *= silu_grad_from(z1, 1.0f / (1.0f + __expf(-z1)));
-          bv *= silu_grad_from(z2, 1.0f / (1.0f + __expf(-z2)));
+        float a = acc[c][j] * f;
+        if (z) {
+          const float zz = from_bits16<T>(z[(int64_t)row * ldz + col]);
+          a *= silu_grad_from(zz, 1.0f / (1.0f + __expf(-zz)));
         }
-        dK[(int64_t)row * lddkv + col] = bits16<T>(a);
-        dV[(int64_t)row * lddkv + col] = bits16<T>(bv);
+        dst[(int64_t)row * lddkv + col] = bits16<T>(a);
       }
     }
 }
@@ -836,17 +860,17 @@ static void bwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
   const float kexp = -a.alpha * 1.4426950408889634f;
   {
     ProfScope ps("attn_bwd_dkdv", st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH>), dim3(xcd_grid(pv.k.max_tiles, a.H)), dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH>), dim3(xcd_grid(pv.k.max_tiles, a.H)), dim3(512), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
                        (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv,
                        (const uint16_t*)a.zk, (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.k.tiles, pv.k.ntiles,
                        a.H, kexp, a.alpha, a.scale);
   }
   ProfScope ps("attn_bwd_dq", st);
-  hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(256), 0, st,
+  hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), dim3(xcd_grid(pv.q2.max_tiles, a.H)), dim3(512), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
                      (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg,
-                     a.ts, pv.q.tiles, pv.q.ntiles, a.H, kexp, a.alpha, a.alpha * a.scale);
+                     a.ts, pv.q2.tiles, pv.q2.ntiles, a.H, kexp, a.alpha, a.alpha * a.scale);
 }
 
 template <int DH>

@@ -58,9 +58,30 @@ template <> __device__ __forceinline__ f32x16_t mfma32<f16_t>(const op8& a, cons
                                                 __builtin_bit_cast(f16x8_t, b.v), c, 0, 0, 0);
 }
 
-// Pack two floats as 16-bit values of T into one dword (lo first).
-template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)bits16<T>(lo) | ((uint32_t)bits16<T>(hi) << 16);
+// Pack two floats as 16-bit values of T into one dword (lo first), one
+// v_cvt_pk_* instruction, round to nearest even.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// Raw buffer resource over `bytes` bytes from `base`: 16-byte loads at
+// offsets at or beyond `bytes` return zeros (hardware range check).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  i32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return __builtin_bit_cast(uint4, x);
 }
 
 // LDS transpose read of gfx950: the 16 lanes of each quarter-wave together
