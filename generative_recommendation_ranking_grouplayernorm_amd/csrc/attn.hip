@@ -396,54 +396,12 @@ __device__ __forceinline__ void quad_swrite_rows(uint16_t* s, const VtLoad<DH>& 
 // backward, query-major: dQ = alpha * c * sum_j [M SiLU'(S) (dO v_j)] k_j
 // for 128 queries (4 waves x 32), 64 keys per LDS stage.
 // ---------------------------------------------------------------------------
-template <typename T, int DH, bool MASKED>
-__device__ __forceinline__ void dq_tile(const uint16_t* Ks, const uint16_t* Vs, const uint16_t* Kt,
-                                        const op8 (&qop)[DH / 16], const op8 (&dop)[DH / 16],
-                                        f32x16_t (&acc)[DH / 32], int k0, int qi, int64_t tq, int s_end,
-                                        int r_end, int hi, const int64_t* __restrict__ ts, float kexp,
-                                        float alpha, int lane) {
-  constexpr int KP = AttnPitch<DH>::B128;
-  const int g = lane >> 5;
-  // one 32-key half of the tile at a time keeps the live accumulators small
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    f32x16_t sacc = mfma32<T>(row_operand<KP>(Ks, t * 32, 0, lane), qop[0], f32x16_t{});
-    f32x16_t dacc = mfma32<T>(row_operand<KP>(Vs, t * 32, 0, lane), dop[0], f32x16_t{});
-#pragma unroll
-    for (int s = 1; s < DH / 16; ++s) {
-      sacc = mfma32<T>(row_operand<KP>(Ks, t * 32, s, lane), qop[s], sacc);
-      dacc = mfma32<T>(row_operand<KP>(Vs, t * 32, s, lane), dop[s], dacc);
-    }
-    float ds[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float sr = sacc[j];
-      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
-      float v = dacc[j] * silu_grad_from(alpha * sr, sg);
-      if (MASKED) {
-        const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-        if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) v = 0.f;
-      }
-      ds[j] = v;
-    }
-#pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      op8 da;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) da.v[e] = pack2<T>(ds[8 * uu + 2 * e], ds[8 * uu + 2 * e + 1]);
-#pragma unroll
-      for (int c = 0; c < DH / 32; ++c)
-        acc[c] = mfma32<T>(da, vt_operand(Kt, 2 * t + uu, c * 32, lane), acc[c]);
-    }
-  }
-}
-
-// 512 threads, 256 queries (8 waves x 32): the K/V tiles are shared by 8
-// waves and each wave stays under 256 registers, so two waves share a SIMD
-// and one's SiLU' arithmetic overlaps the other's MFMAs.  Waves 0-3 load K
-// (written both row-major and transposed), waves 4-7 load V.
-constexpr int DQ_BQ = 256;
-
+// 512 threads in producer/consumer pairs over 128 queries: wave i (i < 4)
+// computes S^T for query group i and the factor f = M * SiLU'(alpha s)
+// (written to LDS as f16); wave i + 4 computes dA^T = V dO^T for the same
+// queries and forms dS = dA * f, which it hands back through LDS; each wave
+// of the pair then accumulates half of the dQ = dS K columns, so both do
+// the same number of MFMAs.
 template <typename T, int DH>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -456,6 +414,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][A_BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][A_BK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Kt[2][DH * VT_PITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t Fx[4][32 * 16 * 2];
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
@@ -463,39 +422,41 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   const int b = te.x, q0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
-  const bool loads_k = wave < 4;
+  const bool producer = wave < 4;
+  const int grp = wave & 3;
   const int ltid = tid & 255;
-  const int q_last = min(q0 + DQ_BQ, hi) - 1;
+  const int q_last = min(q0 + A_BQ, hi) - 1;
   const int kv_end = key_end_for(q_last, s_end, r_end);
-  const int qw = q0 + wave * 32;
-  const bool active = qw < hi;
-  const int qi = qw + l32;
+  const int qi = q0 + grp * 32 + l32;
   const bool qv = qi < hi;
   const int qr = qv ? qi : lo;
   const int64_t tq = ts[qr];
   const int hc = h * DH;
 
-  op8 qop[NS], dop[NS];
+  // producer: Q (B operand of S^T = K Q^T); consumer: dO (B of dA^T = V dO^T)
+  op8 bop[NS];
+  {
+    const uint16_t* src = producer ? Q : dO;
+    const int64_t lds = producer ? ldqkv : lddo;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4_t a = *(const u32x4_t*)(Q + (int64_t)qr * ldqkv + hc + 16 * s + 8 * g);
-    u32x4_t d = *(const u32x4_t*)(dO + (int64_t)qr * lddo + hc + 16 * s + 8 * g);
-    qop[s].v = qv ? a : u32x4_t{0, 0, 0, 0};
-    dop[s].v = qv ? d : u32x4_t{0, 0, 0, 0};
+    for (int s = 0; s < NS; ++s) {
+      u32x4_t a = *(const u32x4_t*)(src + (int64_t)qr * lds + hc + 16 * s + 8 * g);
+      bop[s].v = qv ? a : u32x4_t{0, 0, 0, 0};
+    }
   }
-  f32x16_t acc[NC];
+  f32x16_t acc[NC / 2];  // half of the dQ columns per role
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
 
-  VtLoad<DH> ld;  // K quads (waves 0-3) or V rows (waves 4-7, in ld.x)
+  VtLoad<DH> ld;  // producers load K quads (row-major + transposed), consumers V rows
   auto gload = [&](int k0) {
-    if (loads_k) vt_gload<DH>(ld, K, ldqkv, k0, hi, hc, ltid);
+    if (producer) vt_gload<DH>(ld, K, ldqkv, k0, hi, hc, ltid);
     else tile_gload_rows<DH, A_BK>(ld.x, V, ldqkv, k0, hi, hc, ltid);
   };
   auto swrite = [&](int buf) {
-    if (loads_k) {
+    if (producer) {
       quad_swrite_rows<DH>(Ks[buf], ld);
       vt_swrite<DH>(Kt[buf], ld);
     } else {
@@ -509,30 +470,83 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     swrite(0);
   }
   __syncthreads();
+  uint32_t* fx = Fx[grp];
   for (int it = 0; it < nkt; ++it) {
     const int buf = it & 1, k0 = lo + it * A_BK;
     const bool more = it + 1 < nkt;
     if (more) gload(k0 + A_BK);
-    if (active) {
-      if (it < nfull)
-        dq_tile<T, DH, false>(Ks[buf], Vs[buf], Kt[buf], qop, dop, acc, k0, qi, tq, s_end, r_end, hi, ts, kexp,
-                              alpha, lane);
-      else
-        dq_tile<T, DH, true>(Ks[buf], Vs[buf], Kt[buf], qop, dop, acc, k0, qi, tq, s_end, r_end, hi, ts, kexp,
-                             alpha, lane);
+    // phase 1: S^T (producer) or dA^T (consumer) for 64 keys x 32 queries
+    const uint16_t* A = producer ? Ks[buf] : Vs[buf];
+    f32x16_t x[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<KP>(A, t * 32, 0, lane), bop[0], f32x16_t{});
+#pragma unroll
+    for (int s = 1; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<KP>(A, t * 32, s, lane), bop[s], x[t]);
+    if (producer) {
+      const bool masked = it >= nfull;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float sr = x[t][j];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
+          float f = silu_grad_from(alpha * sr, sg);
+          if (masked) {
+            const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+            if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) f = 0.f;
+          }
+          x[t][j] = f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          fx[(t * 8 + e) * 64 + lane] = pack2<f16_t>(x[t][2 * e], x[t][2 * e + 1]);
+      }
     }
+    __syncthreads();  // f of this tile visible to the consumers
+    op8 da[4];
+    if (!producer) {
+      float d[2][16];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t fv = fx[(t * 8 + e) * 64 + lane];
+          d[t][2 * e] = x[t][2 * e] * from_bits16<f16_t>((uint16_t)(fv & 0xffff));
+          d[t][2 * e + 1] = x[t][2 * e + 1] * from_bits16<f16_t>((uint16_t)(fv >> 16));
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        da[u] = pack_kstep<T>(d, u);
+        // hand dS to the producer, which accumulates the other half of dQ
+        *(u32x4_t*)&fx[(u * 4) * 64 + lane * 4] = da[u].v;
+      }
+    }
+    __syncthreads();  // dS of this tile visible to the producers
+    if (producer) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) da[u].v = *(const u32x4_t*)&fx[(u * 4) * 64 + lane * 4];
+    }
+    // dQ += dS K: producers take column blocks [0, NC/2), consumers the rest
+    const int cb = producer ? 0 : NC / 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < NC / 2; ++c)
+        acc[c] = mfma32<T>(da[u], vt_operand(Kt[buf], u, (cb + c) * 32, lane), acc[c]);
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
-  if (!active) return;
+  const int cb = producer ? 0 : NC / 2;
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int row = qw + 8 * (j >> 2) + 4 * g + (j & 3);
+      const int row = q0 + grp * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
       if (row < hi) {
         float v = acc[c][j] * out_scale;
-        const int col = hc + c * 32 + l32;
+        const int col = hc + (cb + c) * 32 + l32;
         if (zq) {
           const float z = from_bits16<T>(zq[(int64_t)row * ldz + col]);
           v *= silu_grad_from(z, 1.0f / (1.0f + __expf(-z)));
@@ -867,10 +881,10 @@ static void bwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
                        a.H, kexp, a.alpha, a.scale);
   }
   ProfScope ps("attn_bwd_dq", st);
-  hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), dim3(xcd_grid(pv.q2.max_tiles, a.H)), dim3(512), 0, st,
+  hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(512), 0, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
                      (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg,
-                     a.ts, pv.q2.tiles, pv.q2.ntiles, a.H, kexp, a.alpha, a.alpha * a.scale);
+                     a.ts, pv.q.tiles, pv.q.ntiles, a.H, kexp, a.alpha, a.alpha * a.scale);
 }
 
 template <int DH>

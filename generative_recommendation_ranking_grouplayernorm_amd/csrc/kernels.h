@@ -24,8 +24,7 @@ class ProfScope {
 
 // Rows per attention tile: queries per forward / dQ workgroup, keys per
 // dK/dV workgroup.
-constexpr int ATTN_QTILE = 128;   // forward
-constexpr int ATTN_QTILE2 = 256;  // dQ
+constexpr int ATTN_QTILE = 128;   // forward and dQ
 constexpr int ATTN_KTILE = 128;   // dK/dV
 
 // ---- a1: segments and tile lists -----------------------------------------
@@ -37,7 +36,6 @@ struct TileList {
 struct PrepView {
   int32_t* seg;      // [B, 5]
   TileList q;        // ATTN_QTILE-row tiles
-  TileList q2;       // ATTN_QTILE2-row tiles
   TileList k;        // ATTN_KTILE-row tiles
 };
 int64_t max_tiles(int B, int64_t T, int rows_per_tile);

@@ -120,7 +120,6 @@ size_t prep_workspace_bytes(int B, int64_t T) {
   n += 256;                                                    // tile counts
   n += align_up((size_t)B * sizeof(int32_t), 256);           // order scratch
   n += align_up((size_t)max_tiles(B, T, ATTN_QTILE) * sizeof(int2), 256);
-  n += align_up((size_t)max_tiles(B, T, ATTN_QTILE2) * sizeof(int2), 256);
   n += align_up((size_t)max_tiles(B, T, ATTN_KTILE) * sizeof(int2), 256);
   return n;
 }
@@ -131,17 +130,13 @@ int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t
   out->seg = (int32_t*)p;
   p += align_up((size_t)B * 5 * sizeof(int32_t), 256);
   out->q.ntiles = (int32_t*)p;
-  out->q2.ntiles = (int32_t*)p + 1;
-  out->k.ntiles = (int32_t*)p + 2;
+  out->k.ntiles = (int32_t*)p + 1;
   p += 256;
   int32_t* order = (int32_t*)p;
   p += align_up((size_t)B * sizeof(int32_t), 256);
   out->q.tiles = (int2*)p;
   out->q.max_tiles = max_tiles(B, T, ATTN_QTILE);
   p += align_up((size_t)out->q.max_tiles * sizeof(int2), 256);
-  out->q2.tiles = (int2*)p;
-  out->q2.max_tiles = max_tiles(B, T, ATTN_QTILE2);
-  p += align_up((size_t)out->q2.max_tiles * sizeof(int2), 256);
   out->k.tiles = (int2*)p;
   out->k.max_tiles = max_tiles(B, T, ATTN_KTILE);
   if (B > 0) {
@@ -151,9 +146,6 @@ int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t
   }
   hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, ATTN_QTILE, order,
                      out->q.tiles, out->q.ntiles);
-  MTGR_LAUNCH_CHECK();
-  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, ATTN_QTILE2, order,
-                     out->q2.tiles, out->q2.ntiles);
   MTGR_LAUNCH_CHECK();
   hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, ATTN_KTILE, order,
                      out->k.tiles, out->k.ntiles);
