@@ -76,9 +76,9 @@ bool jagged_ok(const int32_t* offsets, const uint8_t* g, const int64_t* ts, int3
 }
 
 int splits_for(int M, int N, int K) {
-  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  const int tiles = ((M + 255) / 256) * ((N + 255) / 256);
   int s = (512 + tiles - 1) / tiles;
-  const int maxs = K / 512 > 0 ? K / 512 : 1;
+  const int maxs = K / 1024 > 0 ? K / 1024 : 1;
   if (s > maxs) s = maxs;
   return s < 1 ? 1 : s;
 }

@@ -3,8 +3,8 @@
 // U, Q, K, V), the output projection with bias + residual (a6), and the
 // backward products (data gradients and fp32 weight gradients).
 //
-// bf16 / f16: 128x128 output tile per 256-thread workgroup, 4 waves in 2x2,
-// each wave 64x64 = 2x2 MFMA 32x32x16 tiles; K staged through LDS 64 deep,
+// bf16 / f16: 256x256 output tile per 512-thread workgroup, 8 waves in 2x4,
+// each wave 128x64 = 4x2 MFMA 32x32x16 tiles; K staged through LDS 64 deep,
 // double-buffered, one barrier per K step.  Operands stored K-contiguous are
 // read with 16-byte LDS loads; operands stored M/N-contiguous (the transposed
 // products of the backward) are read with gfx950's LDS transpose load, so no
@@ -40,38 +40,38 @@ __device__ __forceinline__ void epi_apply(const GemmEpiArgs& ep, int m, int n, f
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel
+// MFMA kernel: 256 x 256 output tile, 512 threads = 8 waves as 2 (M) x 4 (N),
+// each wave 128 x 64 = 4 x 2 MFMA 32x32x16 tiles; K staged 64 deep through
+// LDS, double-buffered with register prefetch, one barrier per K step.
+// Global reads are buffer loads whose range check zero-fills rows past the
+// matrix edge; advancing a K step changes only scalar registers.
 // ---------------------------------------------------------------------------
-constexpr int G_BM = 128, G_BN = 128, G_BK = 64;
-constexpr int G_KC_PITCH = G_BK + 8;    // K-contiguous tile row pitch (elements)
-constexpr int G_MN_PITCH = G_BM + 16;   // M/N-contiguous tile row pitch (elements)
-constexpr int G_TILE_ELEMS = 9216;      // = 128 * 72 = 64 * 144
-static_assert(G_BM * G_KC_PITCH == G_TILE_ELEMS && G_BK * G_MN_PITCH == G_TILE_ELEMS, "tile size");
+constexpr int G_BM = 256, G_BN = 256, G_BK = 64;
+constexpr int G_KC_PITCH = G_BK + 8;    // K-contiguous tile [256][72]
+constexpr int G_MN_PITCH = G_BM + 16;   // M/N-contiguous tile [64][272]
+constexpr int G_TILE_ELEMS = G_BM * G_KC_PITCH;  // >= G_BK * G_MN_PITCH
+static_assert(G_BK * G_MN_PITCH <= G_TILE_ELEMS, "tile size");
+
+// Buffer resource over one operand's K step.  K-contiguous: rows r0.. (the
+// M or N index), columns k0..; M/N-contiguous: rows k0.. (the K index),
+// columns r0...  Reads beyond the valid rows return zeros.
+template <bool KC>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const uint16_t* P, int64_t ld, int r0, int R, int k0,
+                                                         int kend) {
+  if (KC) return make_rsrc(P + (int64_t)r0 * ld + k0, (int)((int64_t)(R - r0) * ld * 2 - (int64_t)k0 * 2));
+  return make_rsrc(P + (int64_t)k0 * ld + r0, (int)((int64_t)(kend - k0) * ld * 2 - (int64_t)r0 * 2));
+}
 
 template <bool KC>
-__device__ __forceinline__ uint4 gemm_gload(const uint16_t* __restrict__ P, int64_t ld, int r0, int R,
-                                            int k0, int kend, int c) {
-  if (KC) {
-    const int row = c >> 3, kc = (c & 7) * 8;
-    const int r = r0 + row, k = k0 + kc;
-    if (r < R && k < kend) return *(const uint4*)(P + (int64_t)r * ld + k);
-  } else {
-    const int krow = c >> 4, rc = (c & 15) * 8;
-    const int k = k0 + krow, r = r0 + rc;
-    if (k < kend && r < R) return *(const uint4*)(P + (int64_t)k * ld + r);
-  }
-  return make_uint4(0, 0, 0, 0);
+__device__ __forceinline__ int gemm_voff(int64_t ld, int c) {
+  if (KC) return ((c >> 3) * (int)ld + (c & 7) * 8) * 2;
+  return ((c >> 5) * (int)ld + (c & 31) * 8) * 2;
 }
 
 template <bool KC>
 __device__ __forceinline__ void gemm_swrite(uint16_t* s, int c, uint4 v) {
-  if (KC) {
-    const int row = c >> 3, kc = (c & 7) * 8;
-    *(uint4*)(s + row * G_KC_PITCH + kc) = v;
-  } else {
-    const int krow = c >> 4, rc = (c & 15) * 8;
-    *(uint4*)(s + krow * G_MN_PITCH + rc) = v;
-  }
+  if (KC) *(uint4*)(s + (c >> 3) * G_KC_PITCH + (c & 7) * 8) = v;
+  else *(uint4*)(s + (c >> 5) * G_MN_PITCH + (c & 31) * 8) = v;
 }
 
 // MFMA operand for 32 rows starting at r0 (within the tile), k-step ks.
@@ -92,83 +92,97 @@ __device__ __forceinline__ op8 gemm_operand(const uint16_t* s, int r0, int ks, i
   return o;
 }
 
+// Workgroup L -> (row job, N tile).  Workgroups run round-robin on the 8
+// XCDs; every N tile of one row job goes to the same XCD so that the A rows
+// are fetched once into that XCD's L2.
+__device__ __forceinline__ bool gemm_tile_of(int L, int NT, int R, int& rr, int& nt) {
+  const int x = L & 7, r = L >> 3;
+  nt = r % NT;
+  rr = (r / NT) * 8 + x;
+  return rr < R;
+}
+
 template <typename T, bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(const uint16_t* __restrict__ A, int64_t lda,
-                                                        const uint16_t* __restrict__ B, int64_t ldb,
-                                                        int M, int N, int K, int k_per_split,
-                                                        GemmEpiArgs ep) {
+__global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                           const uint16_t* __restrict__ B, int64_t ldb,
+                                                           int M, int N, int K, int k_per_split, int MT,
+                                                           int NT, int R, GemmEpiArgs ep) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2 * G_TILE_ELEMS];
+  int rr, nt;
+  if (!gemm_tile_of(blockIdx.x, NT, R, rr, nt)) return;
+  const int mt = rr % MT, split = rr / MT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * G_BM, n0 = blockIdx.x * G_BN;
-  const int kbeg = blockIdx.z * k_per_split;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int m0 = mt * G_BM, n0 = nt * G_BN;
+  const int kbeg = split * k_per_split;
   const int kend = min(K, kbeg + k_per_split);
   const int nk = kend > kbeg ? (kend - kbeg + G_BK - 1) / G_BK : 0;
+  if (EPI == EPI_F32_ATOMIC && nk == 0) return;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[4][2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[t][u][j] = 0.f;
 
+  int va[4], vb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    va[i] = gemm_voff<AK>(lda, tid + 512 * i);
+    vb[i] = gemm_voff<BKC>(ldb, tid + 512 * i);
+  }
   uint4 ra[4], rb[4];
+  auto gload = [&](int k0) {
+    const __amdgpu_buffer_rsrc_t sa = gemm_rsrc<AK>(A, lda, m0, M, k0, kend);
+    const __amdgpu_buffer_rsrc_t sb = gemm_rsrc<BKC>(B, ldb, n0, N, k0, kend);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = buf_load16(sa, va[i]);
+      rb[i] = buf_load16(sb, vb[i]);
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gemm_swrite<AK>(smem[buf], tid + 512 * i, ra[i]);
+      gemm_swrite<BKC>(smem[buf] + G_TILE_ELEMS, tid + 512 * i, rb[i]);
+    }
+  };
   if (nk > 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = gemm_gload<AK>(A, lda, m0, M, kbeg, kend, tid + 256 * i);
-      rb[i] = gemm_gload<BKC>(B, ldb, n0, N, kbeg, kend, tid + 256 * i);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gemm_swrite<AK>(smem[0], tid + 256 * i, ra[i]);
-      gemm_swrite<BKC>(smem[0] + G_TILE_ELEMS, tid + 256 * i, rb[i]);
-    }
+    gload(kbeg);
+    swrite(0);
   }
   __syncthreads();
   for (int it = 0; it < nk; ++it) {
     const int buf = it & 1;
     const bool more = it + 1 < nk;
-    if (more) {
-      const int kn = kbeg + (it + 1) * G_BK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = gemm_gload<AK>(A, lda, m0, M, kn, kend, tid + 256 * i);
-        rb[i] = gemm_gload<BKC>(B, ldb, n0, N, kn, kend, tid + 256 * i);
-      }
-    }
+    if (more) gload(kbeg + (it + 1) * G_BK);
     const uint16_t* sa = smem[buf];
     const uint16_t* sb = smem[buf] + G_TILE_ELEMS;
 #pragma unroll
     for (int ks = 0; ks < G_BK / 16; ++ks) {
-      op8 a[2], b[2];
+      op8 a[4], b[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) a[t] = gemm_operand<AK>(sa, wm * 64 + t * 32, ks, lane);
+      for (int t = 0; t < 4; ++t) a[t] = gemm_operand<AK>(sa, wm * 128 + t * 32, ks, lane);
 #pragma unroll
       for (int u = 0; u < 2; ++u) b[u] = gemm_operand<BKC>(sb, wn * 64 + u * 32, ks, lane);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int u = 0; u < 2; ++u) acc[t][u] = mfma32<T>(a[t], b[u], acc[t][u]);
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gemm_swrite<AK>(smem[buf ^ 1], tid + 256 * i, ra[i]);
-        gemm_swrite<BKC>(smem[buf ^ 1] + G_TILE_ELEMS, tid + 256 * i, rb[i]);
-      }
-    }
+    if (more) swrite(buf ^ 1);
     __syncthreads();
   }
-  if (EPI == EPI_F32_ATOMIC && nk == 0) return;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int m = m0 + wm * 64 + t * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+        const int m = m0 + wm * 128 + t * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
         const int n = n0 + wn * 64 + u * 32 + (lane & 31);
         if (m < M && n < N) epi_apply<T, EPI>(ep, m, n, acc[t][u][j]);
       }
@@ -210,9 +224,10 @@ static void gemm_launch_t(const void* A, int64_t lda, const void* B, int64_t ldb
   int kps = (K + splits - 1) / splits;
   if constexpr (sizeof(T) == 2) {
     kps = (kps + G_BK - 1) / G_BK * G_BK;
-    dim3 grid((N + G_BN - 1) / G_BN, (M + G_BM - 1) / G_BM, splits);
-    hipLaunchKernelGGL((gemm_mfma_kernel<T, AK, BKC, EPI>), grid, dim3(256), 0, st, (const uint16_t*)A,
-                       lda, (const uint16_t*)B, ldb, M, N, K, kps, ep);
+    const int MT = (M + G_BM - 1) / G_BM, NT = (N + G_BN - 1) / G_BN, R = MT * splits;
+    const unsigned grid = (unsigned)((R + 7) / 8 * 8 * NT);
+    hipLaunchKernelGGL((gemm_mfma_kernel<T, AK, BKC, EPI>), dim3(grid), dim3(512), 0, st, (const uint16_t*)A,
+                       lda, (const uint16_t*)B, ldb, M, N, K, kps, MT, NT, R, ep);
   } else {
     dim3 grid((N + 15) / 16, (M + 15) / 16, splits);
     hipLaunchKernelGGL((gemm_simple_kernel<T, AK, BKC, EPI>), grid, dim3(256), 0, st, (const T*)A, lda,
