@@ -223,7 +223,8 @@ static int layer_param_checks(const mtgr_layer_params* p, int dt) {
   if (dt != MTGR_F32 && p->d % 64 != 0) return MTGR_ERR_UNSUPPORTED;
   if (!p->W_uqkv || !p->gamma1 || !p->beta1 || !p->gamma2 || !p->beta2 || !p->W_o) return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(p->gamma1, p->d, dt) || !vec_ok(p->beta1, p->d, dt) || !vec_ok(p->gamma2, p->d, dt) ||
-      !vec_ok(p->beta2, p->d, dt) || !vec_ok(p->W_uqkv, p->d, dt) || !vec_ok(p->W_o, p->d, dt))
+      !vec_ok(p->beta2, p->d, dt) || !vec_ok(p->W_uqkv, p->d, dt) || !vec_ok(p->W_o, p->d, dt) ||
+      (p->b_uqkv && !aligned16(p->b_uqkv)) || (p->b_o && !aligned16(p->b_o)))
     return MTGR_ERR_INVALID_ARG;
   return MTGR_OK;
 }

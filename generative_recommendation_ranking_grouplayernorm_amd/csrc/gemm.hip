@@ -16,6 +16,60 @@ namespace mtgr {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// Staged epilogue of 8 consecutive outputs (m, n..n+7), N % 8 == 0.
+constexpr int G_EPI_PITCH = 72;  // floats per staged row
+
+template <typename T>
+__device__ __forceinline__ void load8_t(const T* p, float* o) {
+  const uint4 r = *(const uint4*)p;
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = from_bits16<T>((uint16_t)(w[i] & 0xffff));
+    o[2 * i + 1] = from_bits16<T>((uint16_t)(w[i] >> 16));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8_t(T* p, const float* v) {
+  uint4 r;
+  r.x = pack2<T>(v[0], v[1]);
+  r.y = pack2<T>(v[2], v[3]);
+  r.z = pack2<T>(v[4], v[5]);
+  r.w = pack2<T>(v[6], v[7]);
+  *(uint4*)p = r;
+}
+
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, float* v) {
+  if (EPI == EPI_BIAS_SILU || EPI == EPI_BIAS_RESID) {
+    if (ep.bias) {
+      float bb[8];
+      load8_t<T>((const T*)ep.bias + n, bb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += bb[e];
+    }
+  }
+  if (EPI == EPI_BIAS_SILU) {
+    float z[8];
+    // round z to T first so forward and backward see the same pre-activation
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = to_f32(from_f32<T>(v[e]));
+    if (ep.Z) store8_t<T>((T*)ep.Z + (int64_t)m * ep.ldz + n, z);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = silu_f(z[e]);
+    store8_t<T>((T*)ep.C + (int64_t)m * ep.ldc + n, z);
+  } else if (EPI == EPI_BIAS_RESID) {
+    float r[8];
+    load8_t<T>((const T*)ep.R + (int64_t)m * ep.ldr + n, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += r[e];
+    store8_t<T>((T*)ep.C + (int64_t)m * ep.ldc + n, v);
+  } else {
+    store8_t<T>((T*)ep.C + (int64_t)m * ep.ldc + n, v);
+  }
+}
+
 template <typename T, int EPI>
 __device__ __forceinline__ void epi_apply(const GemmEpiArgs& ep, int m, int n, float acc) {
   if (EPI == EPI_STORE) {
@@ -176,16 +230,50 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(const uint16_t* __res
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
+  if constexpr (EPI == EPI_F32_STORE || EPI == EPI_F32_ATOMIC) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = m0 + wm * 128 + t * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-        const int n = n0 + wn * 64 + u * 32 + (lane & 31);
-        if (m < M && n < N) epi_apply<T, EPI>(ep, m, n, acc[t][u][j]);
+        for (int j = 0; j < 16; ++j) {
+          const int m = m0 + wm * 128 + t * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+          const int n = n0 + wn * 64 + u * 32 + (lane & 31);
+          if (m < M && n < N) epi_apply<T, EPI>(ep, m, n, acc[t][u][j]);
+        }
+  } else {
+    // 16-bit outputs: stage each wave's tile through its own LDS region (64
+    // rows at a time, fp32) and write whole 128-byte row segments.
+    float* st = (float*)&smem[0][0] + wave * (64 * G_EPI_PITCH);
+    const int wr0 = m0 + wm * 128, wc0 = n0 + wn * 64;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = tt * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            st[r * G_EPI_PITCH + u * 32 + (lane & 31)] = acc[2 * half + tt][u][j];
+          }
+      // lane -> 8 consecutive columns of one row; 8 rows per pass
+      const int cc = (lane & 7) * 8;
+      const int n = wc0 + cc;
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        const int r = pass * 8 + (lane >> 3);
+        const int m = wr0 + half * 64 + r;
+        if (m < M && n < N) {
+          float v[8];
+          const float4 a = *(const float4*)&st[r * G_EPI_PITCH + cc];
+          const float4 b = *(const float4*)&st[r * G_EPI_PITCH + cc + 4];
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+          epi_row8<T, EPI>(ep, m, n, v);
+        }
       }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
