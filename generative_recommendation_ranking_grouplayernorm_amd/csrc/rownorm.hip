@@ -161,7 +161,7 @@ int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, con
 }
 
 // ---- backward ---------------------------------------------------------------
-constexpr int GLN_BWD_ROWS_PER_BLOCK = 128;  // 32 consecutive rows per wave
+constexpr int GLN_BWD_ROWS_PER_BLOCK = 64;  // 16 consecutive rows per wave
 
 __device__ __forceinline__ float silu_grad_f(float z) {
   float s = 1.0f / (1.0f + __expf(-z));
@@ -169,6 +169,9 @@ __device__ __forceinline__ float silu_grad_f(float z) {
 }
 
 // Per block: partial[blockIdx.x][0][G][d] = dgamma part, [1][G][d] = dbeta part.
+// Each wave walks 16 consecutive rows; the group rarely changes along them,
+// so the per-group sums stay in registers and are flushed to LDS (atomic
+// adds) only on a change.
 template <typename T, int NCH, bool GATE>
 __global__ __launch_bounds__(256) void gln_bwd_kernel(
     const T* __restrict__ dy, int64_t lddy, const T* __restrict__ x, int64_t ldx,
@@ -190,25 +193,26 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
   int cur = -1;
+  auto flush = [&]() {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane * 8 + i * 512;
+      if (c < d) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          atomicAdd(&acc[cur * d + c + e], ag[i][e]);
+          atomicAdd(&acc[Gd + cur * d + c + e], ab[i][e]);
+          ag[i][e] = ab[i][e] = 0.f;
+        }
+      }
+    }
+  };
   for (int rr = 0; rr < RPW; ++rr) {
     const int64_t row = r0 + rr;
     if (row >= nrows) break;
     const int grp = g[row];
     if (grp != cur) {
-      if (cur >= 0) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const int c = lane * 8 + i * 512;
-          if (c < d) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              atomicAdd(&acc[cur * d + c + e], ag[i][e]);
-              atomicAdd(&acc[Gd + cur * d + c + e], ab[i][e]);
-              ag[i][e] = ab[i][e] = 0.f;
-            }
-          }
-        }
-      }
+      if (cur >= 0) flush();
       cur = grp;
     }
     const float mu = mean[row], rs = rstd[row];
@@ -218,12 +222,12 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
     for (int i = 0; i < NCH; ++i) {
       const int c = lane * 8 + i * 512;
       if (c < d) {
-        float xv[8], dyv[8], ga[8];
-        load8(x + row * ldx + c, xv);
+        float dyv[8], ga[8];
+        load8(x + row * ldx + c, n[i]);
         load8(dy + row * lddy + c, dyv);
         load8(gamma + (int64_t)grp * d + c, ga);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) n[i][k] = (xv[k] - mu) * rs;
+        for (int k = 0; k < 8; ++k) n[i][k] = (n[i][k] - mu) * rs;
         if (GATE) {
           float uu[8], be[8], duv[8];
           load8(u + row * ldu + c, uu);
@@ -269,36 +273,36 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
       }
     }
   }
-  if (cur >= 0) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = lane * 8 + i * 512;
-      if (c < d) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          atomicAdd(&acc[cur * d + c + e], ag[i][e]);
-          atomicAdd(&acc[Gd + cur * d + c + e], ab[i][e]);
-        }
-      }
-    }
-  }
+  if (cur >= 0) flush();
   __syncthreads();
   float* dst = partial + (int64_t)blockIdx.x * 2 * Gd;
   for (int i = threadIdx.x; i < 2 * Gd; i += blockDim.x) dst[i] = acc[i];
 }
 
-// out[i] = sum over nparts of partial[p][i], i < n.  Then split into
-// dgamma = out[0 .. Gd), dbeta = out[Gd .. 2Gd).
-__global__ void reduce_partials_kernel(const float* __restrict__ partial, int nparts, int n,
-                                       float* __restrict__ out_a, float* __restrict__ out_b, int na) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+// out[i] = sum over nparts of partial[p][i], i < n, then split into
+// out_a = out[0 .. na), out_b = out[na .. n).  64 columns per workgroup,
+// 16 groups of parts summed in parallel and combined through LDS.
+__global__ __launch_bounds__(1024) void reduce_partials_kernel(const float* __restrict__ partial, int nparts, int n,
+                                                               float* __restrict__ out_a, float* __restrict__ out_b,
+                                                               int na) {
+  __shared__ float red[16][65];
+  const int cl = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + cl;
   float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += partial[(int64_t)p * n + i];
+  if (i < n) {
+#pragma unroll 8
+    for (int p = rg; p < nparts; p += 16) s += partial[(int64_t)p * n + i];
+  }
+  red[rg][cl] = s;
+  __syncthreads();
+  if (rg != 0 || i >= n) return;
+  float t = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) t += red[r][cl];
   if (i < na) {
-    if (out_a) out_a[i] = s;
+    if (out_a) out_a[i] = t;
   } else if (out_b) {
-    out_b[i - na] = s;
+    out_b[i - na] = t;
   }
 }
 
@@ -358,7 +362,7 @@ int launch_gln_bwd(int dt, const void* dy, int64_t lddy, const void* x, int64_t 
 #undef GLN_BWD_CALL
   if (r) return r;
   const int nblk = (int)((T_ + GLN_BWD_ROWS_PER_BLOCK - 1) / GLN_BWD_ROWS_PER_BLOCK);
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3((2 * Gd + 255) / 256), dim3(256), 0, stream, partial,
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((2 * Gd + 63) / 64), dim3(1024), 0, stream, partial,
                      nblk, 2 * Gd, dgamma, dbeta, Gd);
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
@@ -409,7 +413,7 @@ int launch_colsum(int dt, const void* X, int64_t ldx, int64_t T_, int N, float* 
     default: return MTGR_ERR_UNSUPPORTED;
   }
   MTGR_LAUNCH_CHECK();
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, partial, nb, N,
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((N + 63) / 64), dim3(1024), 0, stream, partial, nb, N,
                      out, (float*)nullptr, N);
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
