@@ -169,12 +169,14 @@ def main():
     dx = torch.empty(T, d, dtype=dt, device=dev)
     grads = mb.alloc_grads(d, G, False, dev)
     ws_f = mb.workspace(mb.OP_LAYER_FWD, B, T, d, H, dt, dev)
-    ws_b = mb.workspace(mb.OP_LAYER_BWD, B, T, d, H, dt, dev)
+    # a row-length bound sizes the backward for stored score gradients
+    ws_b = mb.workspace(mb.OP_LAYER_BWD, B, T, d, H, dt, dev, max_len=batch.max_len)
     stream = torch.cuda.current_stream()
 
     def step():
         mb.mtgr_hstu_layer_fwd(prm, xd, x_out, sv, off, g, ts, scale, ws_f, stream)
-        mb.mtgr_hstu_layer_bwd(prm, xd, sv, Rd, dx, grads, off, g, ts, scale, ws_b, stream=stream)
+        mb.mtgr_hstu_layer_bwd(prm, xd, sv, Rd, dx, grads, off, g, ts, scale, ws_b, max_len=batch.max_len,
+                               stream=stream)
 
     for _ in range(args.warmup):
         step()

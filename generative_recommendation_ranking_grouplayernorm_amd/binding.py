@@ -76,20 +76,20 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "mtgr_version": ([], ctypes.c_char_p),
         "mtgr_status_string": ([ctypes.c_int], ctypes.c_char_p),
-        "mtgr_workspace_size": ([ctypes.c_int, I32, I64, I32, I32, ctypes.c_int], SZ),
+        "mtgr_workspace_size": ([ctypes.c_int, I32, I64, I32, I32, I32, ctypes.c_int], SZ),
         "mtgr_jagged_prep": ([P, P, I32, I64, P, P, SZ, P], ctypes.c_int),
         "mtgr_group_layernorm": ([P, P, P, P, P, I64, I32, I32, F, ctypes.c_int, P, P, P], ctypes.c_int),
         "mtgr_group_layernorm_bwd": ([P, P, P, P, P, P, I64, I32, I32, ctypes.c_int, P, P, P, P, SZ, P],
                                      ctypes.c_int),
         "mtgr_hstu_attn_fwd": ([P, P, P, I64, P, I64, P, P, P, I32, I64, I32, I32, F, F, ctypes.c_int, P, SZ, P],
                                ctypes.c_int),
-        "mtgr_hstu_attn_bwd": ([P, P, P, I64, P, I64, P, P, P, I64, P, P, P, I32, I64, I32, I32, F, F,
+        "mtgr_hstu_attn_bwd": ([P, P, P, I64, P, I64, P, P, P, I64, P, P, P, I32, I64, I32, I32, I32, F, F,
                                 ctypes.c_int, P, SZ, P], ctypes.c_int),
         "mtgr_hstu_layer_fwd": ([ctypes.POINTER(LayerParams), P, P, ctypes.POINTER(LayerSaved), P, P, P, I32,
                                  I64, F, ctypes.c_int, P, SZ, P], ctypes.c_int),
         "mtgr_hstu_layer_bwd": ([ctypes.POINTER(LayerParams), P, ctypes.POINTER(LayerSaved), P, P,
                                  ctypes.POINTER(LayerGrads), ctypes.POINTER(LayerBwdExtras), P, P, P, I32, I64,
-                                 F, ctypes.c_int, P, SZ, P], ctypes.c_int),
+                                 I32, F, ctypes.c_int, P, SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -141,13 +141,16 @@ def mtgr_status_string(status: int) -> str:
     return load_library().mtgr_status_string(status).decode()
 
 
-def mtgr_workspace_size(op: int, B: int, T: int, d: int, H: int, dtype: torch.dtype) -> int:
-    return int(load_library().mtgr_workspace_size(op, B, T, d, H, dtype_code(dtype)))
+def mtgr_workspace_size(op: int, B: int, T: int, max_len: int, d: int, H: int, dtype: torch.dtype) -> int:
+    return int(load_library().mtgr_workspace_size(op, B, T, max_len, d, H, dtype_code(dtype)))
 
 
-def workspace(op: int, B: int, T: int, d: int, H: int, dtype: torch.dtype, device="cuda") -> torch.Tensor:
-    """A byte buffer of the size ``op`` needs (allocation through torch)."""
-    n = mtgr_workspace_size(op, B, T, d, H, dtype)
+def workspace(op: int, B: int, T: int, d: int, H: int, dtype: torch.dtype, device="cuda",
+              max_len: int = 0) -> torch.Tensor:
+    """A byte buffer of the size ``op`` needs (allocation through torch).
+    ``max_len`` > 0 (a bound on every row's length) sizes the backward ops for
+    stored score gradients; the same value goes to the backward call."""
+    n = mtgr_workspace_size(op, B, T, max_len, d, H, dtype)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -185,14 +188,14 @@ def mtgr_hstu_attn_fwd(q, k, v, o, offsets, group_ids, timestamps, H, dh, alpha,
 
 
 def mtgr_hstu_attn_bwd(q, k, v, d_o, dq, dk, dv, offsets, group_ids, timestamps, H, dh, alpha, attn_scale, ws,
-                       stream=None) -> None:
+                       max_len: int = 0, stream=None) -> None:
     B = offsets.numel() - 1
     T = q.shape[0]
     assert _ld(q) == _ld(k) == _ld(v) and _ld(dq) == _ld(dk) == _ld(dv)
     _check("mtgr_hstu_attn_bwd", load_library().mtgr_hstu_attn_bwd(
         _p(q), _p(k), _p(v), _ld(q), _p(d_o), _ld(d_o), _p(dq), _p(dk), _p(dv), _ld(dq), _p(offsets),
-        _p(group_ids), _p(timestamps), B, T, H, dh, alpha, attn_scale, dtype_code(q.dtype), _p(ws), ws.numel(),
-        _stream(stream)))
+        _p(group_ids), _p(timestamps), B, T, max_len, H, dh, alpha, attn_scale, dtype_code(q.dtype), _p(ws),
+        ws.numel(), _stream(stream)))
 
 
 def make_params(p: Dict[str, torch.Tensor], H: int, eps: float = 1e-5, alpha: float = 1.0) -> LayerParams:
@@ -236,7 +239,7 @@ def mtgr_hstu_layer_fwd(params: LayerParams, x_in, x_out, saved: Optional[LayerS
 
 def mtgr_hstu_layer_bwd(params: LayerParams, x_in, saved: LayerSaved, dx_out, dx_in, grads: Dict[str, torch.Tensor],
                         offsets, group_ids, timestamps, attn_scale, ws, extras: Optional[Dict] = None,
-                        stream=None) -> None:
+                        max_len: int = 0, stream=None) -> None:
     B = offsets.numel() - 1
     T = x_in.shape[0]
     g = LayerGrads(_p(grads["W_uqkv"]), _p(grads.get("b_uqkv")), _p(grads["gamma1"]), _p(grads["beta1"]),
@@ -246,5 +249,5 @@ def mtgr_hstu_layer_bwd(params: LayerParams, x_in, saved: LayerSaved, dx_out, dx
         ex = ctypes.byref(LayerBwdExtras(_p(extras.get("d_uqkv")), _p(extras.get("d_o"))))
     _check("mtgr_hstu_layer_bwd", load_library().mtgr_hstu_layer_bwd(
         ctypes.byref(params), _p(x_in), ctypes.byref(saved), _p(dx_out), _p(dx_in), ctypes.byref(g), ex,
-        _p(offsets), _p(group_ids), _p(timestamps), B, T, attn_scale, dtype_code(x_in.dtype), _p(ws),
+        _p(offsets), _p(group_ids), _p(timestamps), B, T, max_len, attn_scale, dtype_code(x_in.dtype), _p(ws),
         ws.numel(), _stream(stream)))

@@ -56,7 +56,16 @@ size_t layer_fwd_ws(int B, int64_t T, int d, int dt) {
   return n;
 }
 
-size_t layer_bwd_ws(int B, int64_t T, int d, int dt) {
+// dS storage of the backward (bf16/f16 with a declared row bound only).
+size_t ds_ws(int B, int64_t T, int max_len, int H, int dt) {
+  return dt == MTGR_F32 ? 0 : attn_ds_bytes(B, T, max_len, H);
+}
+
+size_t attn_bwd_ws(int B, int64_t T, int max_len, int H, int dt) {
+  return align_up(attn_ws(B, T), 256) + ds_ws(B, T, max_len, H, dt);
+}
+
+size_t layer_bwd_ws(int B, int64_t T, int max_len, int d, int H, int dt) {
   const size_t e = elt(dt);
   size_t n = align_up(attn_ws(B, T), 256);
   n += align_up((size_t)T * d * e, 256);       // dy, then dxhat
@@ -65,7 +74,15 @@ size_t layer_bwd_ws(int B, int64_t T, int d, int dt) {
   size_t r = gln_bwd_workspace_bytes(T, d, kMaxG);
   size_t c = colsum_workspace_bytes(T, 4 * d);
   n += align_up(r > c ? r : c, 256);
+  n += ds_ws(B, T, max_len, H, dt);
   return n;
+}
+
+// Point the attention backward at its dS buffer when a row bound was given.
+void set_ds(AttnArgs& a, void* buf, int max_len, int dt) {
+  if (dt == MTGR_F32 || max_len <= 0 || !buf) return;
+  a.ds = buf;
+  a.ds_cap = (int64_t)(ds_ws(a.B, a.T, max_len, a.H, dt) / ((size_t)a.H * DS_TILE_BYTES));
 }
 
 bool jagged_ok(const int32_t* offsets, const uint8_t* g, const int64_t* ts, int32_t B, int64_t T) {
@@ -101,17 +118,16 @@ const char* mtgr_status_string(int status) {
   }
 }
 
-size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t d, int32_t H, int dt) {
-  (void)H;
-  if (B < 0 || T < 0 || d < 0 || !dt_ok(dt)) return 0;
+size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t max_len, int32_t d, int32_t H, int dt) {
+  if (B < 0 || T < 0 || d < 0 || max_len < 0 || H < 0 || !dt_ok(dt)) return 0;
   switch (op) {
     case MTGR_OP_PREP: return 0;
     case MTGR_OP_GLN_FWD: return 0;
     case MTGR_OP_GLN_BWD: return gln_bwd_workspace_bytes(T, d, kMaxG);
     case MTGR_OP_ATTN_FWD: return attn_ws(B, T);
-    case MTGR_OP_ATTN_BWD: return attn_ws(B, T);
+    case MTGR_OP_ATTN_BWD: return attn_bwd_ws(B, T, max_len, H, dt);
     case MTGR_OP_LAYER_FWD: return layer_fwd_ws(B, T, d, dt);
-    case MTGR_OP_LAYER_BWD: return layer_bwd_ws(B, T, d, dt);
+    case MTGR_OP_LAYER_BWD: return layer_bwd_ws(B, T, max_len, d, H, dt);
     default: return 0;
   }
 }
@@ -191,12 +207,14 @@ int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_q
 
 int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_qkv, const void* d_o,
                        int64_t ld_do, void* dq, void* dk, void* dv, int64_t ld_dqkv, const int32_t* offsets,
-                       const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T, int32_t H,
-                       int32_t dh, float alpha, float attn_scale, int dt, void* workspace, size_t ws_bytes,
-                       mtgr_stream_t stream) {
+                       const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T,
+                       int32_t max_len, int32_t H, int32_t dh, float alpha, float attn_scale, int dt,
+                       void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
   int r = attn_common_checks(q, k, v, ld_qkv, offsets, group_ids, timestamps, B, T, H, dh, dt, workspace,
                              ws_bytes);
   if (r) return r;
+  if (max_len < 0) return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < attn_bwd_ws(B, T, max_len, H, dt)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   if (ld_do < (int64_t)H * dh || ld_dqkv < (int64_t)H * dh) return MTGR_ERR_INVALID_ARG;
   if (T > 0 && (!d_o || !dq || !dk || !dv)) return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(d_o, ld_do, dt) || !vec_ok(dq, ld_dqkv, dt) || !vec_ok(dk, ld_dqkv, dt) ||
@@ -211,6 +229,7 @@ int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_q
   a.d_o = d_o; a.lddo = ld_do;
   a.dq = dq; a.dk = dk; a.dv = dv; a.lddqkv = ld_dqkv;
   a.ts = timestamps; a.B = B; a.T = T; a.H = H; a.dh = dh; a.alpha = alpha; a.scale = attn_scale;
+  set_ds(a, (char*)workspace + align_up(attn_ws(B, T), 256), max_len, dt);
   return launch_attn_bwd(dt, a, pv, S(stream));
 }
 
@@ -306,11 +325,11 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
 int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr_layer_saved* saved,
                         const void* dx_out, void* dx_in, const mtgr_layer_grads* grads,
                         const mtgr_layer_bwd_extras* extras, const int32_t* offsets, const uint8_t* group_ids,
-                        const int64_t* timestamps, int32_t B, int64_t T, float attn_scale, int dt,
-                        void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
+                        const int64_t* timestamps, int32_t B, int64_t T, int32_t max_len, float attn_scale,
+                        int dt, void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
   int r = layer_param_checks(p, dt);
   if (r) return r;
-  if (!jagged_ok(offsets, group_ids, timestamps, B, T)) return MTGR_ERR_INVALID_ARG;
+  if (!jagged_ok(offsets, group_ids, timestamps, B, T) || max_len < 0) return MTGR_ERR_INVALID_ARG;
   if (!saved || !grads) return MTGR_ERR_INVALID_ARG;
   if (!grads->W_uqkv || !grads->gamma1 || !grads->beta1 || !grads->gamma2 || !grads->beta2 || !grads->W_o)
     return MTGR_ERR_INVALID_ARG;
@@ -319,7 +338,8 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
                 !saved->uqkv || !saved->o || !saved->mean2 || !saved->rstd2 || !saved->y))
     return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(x_in, d, dt) || !vec_ok(dx_out, d, dt) || !vec_ok(dx_in, d, dt)) return MTGR_ERR_INVALID_ARG;
-  if (ws_bytes < layer_bwd_ws(B, T, d, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < layer_bwd_ws(B, T, max_len, d, p->H, dt) || (T > 0 && !workspace))
+    return MTGR_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = S(stream);
   const int G = p->G;
   if (T == 0 || B == 0) {
@@ -341,6 +361,8 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
   void* ws_dz = cv.take((size_t)T * 4 * d * e);
   size_t rbytes = gln_bwd_workspace_bytes(T, d, kMaxG), cbytes = colsum_workspace_bytes(T, 4 * d);
   void* ws_red = cv.take(rbytes > cbytes ? rbytes : cbytes);
+  const size_t dsb = ds_ws(B, T, max_len, p->H, dt);
+  void* ws_ds = dsb ? cv.take(dsb) : nullptr;
   if (!cv.ok) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   PrepView pv;
   {
@@ -392,6 +414,7 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
     a.zq = zb + (size_t)d * e; a.zk = zb + (size_t)2 * d * e; a.zv = zb + (size_t)3 * d * e; a.ldz = 4 * d;
   }
   a.ts = timestamps; a.B = B; a.T = T; a.H = p->H; a.dh = p->dh; a.alpha = p->alpha; a.scale = attn_scale;
+  set_ds(a, ws_ds, max_len, dt);
   r = launch_attn_bwd(dt, a, pv, st);
   if (r) return r;
   if (want_dact) {

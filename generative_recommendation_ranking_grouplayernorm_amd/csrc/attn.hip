@@ -568,14 +568,15 @@ constexpr int KV_BK = 128;    // keys per workgroup (4 groups of 32)
 constexpr int KV_BQ = 64;     // queries per LDS stage
 constexpr int F_PITCH = 64;   // f16 exchange tile: [key group][64 queries][32 keys]
 
-template <typename T, int DH>
+template <typename T, int DH, bool STORE>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int64_t lddkv, const uint16_t* __restrict__ zk,
     const uint16_t* __restrict__ zv, int64_t ldz, const int32_t* __restrict__ seg,
     const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-    int H, float kexp, float alpha, float scale) {
+    int H, float kexp, float alpha, float scale, uint8_t* __restrict__ dS, int64_t ds_cap,
+    const int64_t* __restrict__ tprefix) {
   constexpr int QP = AttnPitch<DH>::B128;
   constexpr int NS = DH / 16, NC = DH / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][KV_BQ * QP];
@@ -594,16 +595,31 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   const int grp = wave & 3;
   const int ltid = tid & 255;
   const int k_last = min(k0 + KV_BK, hi) - 1;
+  // Query stages lie on a 64-row grid from the row start, so that every
+  // stored dS block has a fixed place; real-time keys start at the stage
+  // holding the first real-time query.
   int qlo, qhi;
-  if (k0 < s_end) { qlo = lo; qhi = hi; }            // static keys: every query
-  else if (k0 < r_end) { qlo = s_end; qhi = hi; }    // real-time keys: R and C queries
-  else { qlo = k0; qhi = k_last + 1; }               // candidate keys: themselves
+  if (k0 < s_end) { qlo = lo; qhi = hi; }                              // static keys: every query
+  else if (k0 < r_end) { qlo = lo + ((s_end - lo) & ~63); qhi = hi; }  // real-time keys: R and C queries
+  else { qlo = k0; qhi = k_last + 1; }                                 // candidate keys: themselves
   const int kj = k0 + grp * 32 + l32;
   const bool kv = kj < hi;
   const int kr = kv ? kj : lo;
   const int64_t tk = ts[kr];
   const int hc = h * DH;
   const bool full = k0 + KV_BK <= s_end;  // every query sees these keys
+  // dS store target of this (dA-side) wave: see attn_bwd_dq_stream for the layout
+  uint8_t* dsw = nullptr;
+  int64_t ds_qt_stride = 0;
+  if (STORE && !producer) {
+    const int nt = (hi - lo + 127) >> 7;
+    const int64_t pb = tprefix[b];
+    if (pb + (int64_t)nt * nt <= ds_cap) {
+      ds_qt_stride = (int64_t)nt * DS_TILE_BYTES;
+      dsw = dS + (pb * H + (int64_t)h * nt * nt) * (int64_t)DS_TILE_BYTES +
+            (int64_t)((k0 - lo) >> 7) * DS_TILE_BYTES + (grp >> 1) * 16384 + (grp & 1) * 4096 + lane * 16;
+    }
+  }
 
   // producer: K of its keys (B operand of S = Q K^T); consumer: V (B of dA)
   op8 bop[NS];
@@ -699,6 +715,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
         }
 #pragma unroll
       for (int u = 0; u < 4; ++u) w[u] = pack_kstep<T>(d, u);
+      if (STORE && dsw) {
+        const int qs = (q0 - lo) >> 6;
+        uint8_t* dp = dsw + (qs >> 1) * ds_qt_stride + (qs & 1) * 8192;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(w[u].v, (u32x4_t*)(dp + u * 1024));
+      }
     }
     // phase 2: dV += P^T dO (producer) or dK += dS^T Q (consumer)
     const uint16_t* Bt = producer ? Dt[buf] : Qt[buf];
@@ -726,6 +748,151 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
           a *= silu_grad_from(zz, 1.0f / (1.0f + __expf(-zz)));
         }
         dst[(int64_t)row * lddkv + col] = bits16<T>(a);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward, query-major from stored dS: dQ = alpha c dS K.
+// ---------------------------------------------------------------------------
+// dS layout.  For user b and head h the buffer holds n_t x n_t tiles of
+// 128 queries x 128 keys (n_t = ceil(L / 128)), 32 KB each, at
+//   ((P_b H + h n_t^2) + qt n_t + kt) * 32 KB,   P_b = sum_{b' < b} n_t(b')^2.
+// Inside a tile, 16 KB per 64-key half; inside a half, 8 KB per 64-query
+// stage; inside a stage, 4 KB per 32-key group, written by the dK/dV wave of
+// that key group as its dK A operands: [k-step u][lane][16 B], lane = key
+// (l32) + 32 g, the 16 bytes holding queries 16u + 8e + 4g + (0..3) for
+// e = 0, 1.  Tiles the dK/dV pass does not visit (fully masked) are never
+// written and never read.
+//
+// Each workgroup takes 128 queries (4 waves x 32) and walks 64-key steps:
+// the 16 KB dS piece and the K rows go to LDS, dS is read back transposed
+// (one query per lane) with the LDS transpose load and K as V^T-style tiles.
+// LDS position of byte b of a 16 KB dS piece: address bits 6 <-> 10 and
+// 7 <-> 9 exchanged, so that the 32 lanes of each half-wave of a transpose
+// read (4 keys x 2 query quads x 2 query eighths x 2 sixteenths) land on 32
+// distinct 8-byte bank slots, while the k-step and the second key quad of
+// a read move only bits 8, 9 and 12 (plain immediate offsets).
+__device__ __forceinline__ int ds_lds_pos(int b) {
+  const int b6 = (b >> 6) & 1, b7 = (b >> 7) & 1, b9 = (b >> 9) & 1, b10 = (b >> 10) & 1;
+  return (b & ~0x6c0) | (b10 << 6) | (b9 << 7) | (b7 << 9) | (b6 << 10);
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
+    const uint16_t* __restrict__ K, int64_t ldqkv, const uint8_t* __restrict__ dS, int64_t ds_cap,
+    const int64_t* __restrict__ tprefix, uint16_t* __restrict__ dQ, int64_t lddq,
+    const uint16_t* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
+    const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, int H, float out_scale) {
+  constexpr int NC = DH / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t Ss[2][16384];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][DH * VT_PITCH];
+  int tile, h;
+  xcd_tile_head(blockIdx.x, H, tile, h);
+  if (tile >= *ntiles) return;
+  const int2 te = tiles[tile];
+  const int b = te.x, q0 = te.y;
+  const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int hc = h * DH;
+  const int nt = (hi - lo + 127) >> 7;
+  const int qt = (q0 - lo) >> 7;
+  const int64_t pb = tprefix[b];
+  if (pb + (int64_t)nt * nt > ds_cap) {
+    // this row's dS did not fit the buffer (a row longer than the declared
+    // maximum): its dQ is NaN rather than garbage
+    const uint16_t nan16 = bits16<T>(__builtin_nanf(""));
+    for (int i = tid; i < 128 * DH; i += 256) {
+      const int row = q0 + i / DH;
+      if (row < hi) dQ[(int64_t)row * lddq + hc + i % DH] = nan16;
+    }
+    return;
+  }
+  const uint8_t* dsq = dS + (pb * H + (int64_t)h * nt * nt + (int64_t)qt * nt) * (int64_t)DS_TILE_BYTES;
+  const int q_last = min(q0 + 128, hi) - 1;
+  const int kv_end = key_end_for(q_last, s_end, r_end);
+  // key tiles with k0 < r_end (static or real-time) come first; of the
+  // candidate tiles only this query tile's own (the diagonal) is visible
+  const int n_nc = (r_end - lo + 127) >> 7;
+  const int end_a = min(kv_end, lo + 128 * n_nc);
+  const int na = end_a > lo ? (end_a - lo + 63) >> 6 : 0;
+  const int nb = qt >= n_nc ? (kv_end - q0 + 63) >> 6 : 0;
+  const int nsteps = na + nb;
+  const int rt_stage0 = (s_end - lo) >> 6;
+
+  // per-thread pieces of the 16 KB dS step: chunks tid + 256 i, stage i >> 1
+  u32x4_t rs[4];
+  VtLoad<DH> rk;
+  auto gload = [&](int it) {
+    const int kpos = it < na ? lo + 64 * it : q0 + 64 * (it - na);
+    const int kt = (kpos - lo) >> 7, half = ((kpos - lo) >> 6) & 1;
+    const int k0 = lo + 128 * kt;
+    const uint8_t* src = dsq + (int64_t)kt * DS_TILE_BYTES + half * 16384;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int st = 2 * qt + (i >> 1);
+      const bool avail = lo + 64 * st < hi && (k0 < s_end || k0 >= r_end || st >= rt_stage0);
+      rs[i] = avail ? __builtin_nontemporal_load((const u32x4_t*)(src + 16 * (tid + 256 * i)))
+                    : u32x4_t{0, 0, 0, 0};
+    }
+    vt_gload<DH>(rk, K, ldqkv, kpos, hi, hc, tid);
+  };
+  const int wsw = ds_lds_pos(16 * tid);
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4_t*)(Ss[buf] + wsw + 4096 * i) = rs[i];
+    vt_swrite<DH>(Kt[buf], rk);
+  };
+
+  // transposed dS reads: lane 4r + c of quarter G supplies (key 4g + r of
+  // the k-step half, queries 4c..4c+3 of the quarter's 16)
+  const int G = lane >> 4, qi4 = lane & 15, rr = qi4 >> 2, cc = qi4 & 3;
+  const int rd_base = ds_lds_pos((wave >> 1) * 8192 + (2 * (wave & 1) + (G & 1)) * 1024 + (cc & 1) * 512 +
+                                 (cc >> 1) * 8 + (4 * g + rr) * 16);
+  f32x16_t acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
+
+  if (nsteps > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nsteps; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < nsteps;
+    if (more) gload(it + 1);
+    const uint8_t* sb = Ss[buf] + rd_base;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      // key 16 ks + 8 rd + 4 g + r: stored byte bits 12 (ks / 2), 8 (ks % 2)
+      // and 7 (rd), the last at LDS bit 9
+      const int off = (ks >> 1) * 4096 + (ks & 1) * 256;
+      const uint2 lo2 = lds_read_tr16(sb + off);
+      const uint2 hi2 = lds_read_tr16(sb + off + 512);
+      op8 a;
+      a.v[0] = lo2.x; a.v[1] = lo2.y; a.v[2] = hi2.x; a.v[3] = hi2.y;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(a, vt_operand(Kt[buf], ks, c * 32, lane), acc[c]);
+    }
+    if (more) swrite(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = q0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+      if (row < hi) {
+        float v = acc[c][j] * out_scale;
+        const int col = hc + c * 32 + l32;
+        if (zq) {
+          const float z = from_bits16<T>(zq[(int64_t)row * ldz + col]);
+          v *= silu_grad_from(z, 1.0f / (1.0f + __expf(-z)));
+        }
+        dQ[(int64_t)row * lddq + col] = bits16<T>(v);
       }
     }
 }
@@ -874,11 +1041,27 @@ static void bwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
   const float kexp = -a.alpha * 1.4426950408889634f;
   {
     ProfScope ps("attn_bwd_dkdv", st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH>), dim3(xcd_grid(pv.k.max_tiles, a.H)), dim3(512), 0, st,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
-                       (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv,
-                       (const uint16_t*)a.zk, (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.k.tiles, pv.k.ntiles,
-                       a.H, kexp, a.alpha, a.scale);
+    if (a.ds)
+      hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH, true>), dim3(xcd_grid(pv.k.max_tiles, a.H)), dim3(512), 0,
+                         st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
+                         (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv,
+                         (const uint16_t*)a.zk, (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.k.tiles,
+                         pv.k.ntiles, a.H, kexp, a.alpha, a.scale, (uint8_t*)a.ds, a.ds_cap,
+                         (const int64_t*)pv.tprefix);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH, false>), dim3(xcd_grid(pv.k.max_tiles, a.H)), dim3(512), 0,
+                         st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
+                         (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv,
+                         (const uint16_t*)a.zk, (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.k.tiles,
+                         pv.k.ntiles, a.H, kexp, a.alpha, a.scale, nullptr, (int64_t)0, (const int64_t*)nullptr);
+  }
+  if (a.ds) {
+    ProfScope ps("attn_bwd_dq", st);
+    hipLaunchKernelGGL((attn_bwd_dq_stream<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(256), 0, st,
+                       (const uint16_t*)a.k, a.ldqkv, (const uint8_t*)a.ds, a.ds_cap, (const int64_t*)pv.tprefix,
+                       (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg, pv.q.tiles, pv.q.ntiles,
+                       a.H, a.alpha * a.scale);
+    return;
   }
   ProfScope ps("attn_bwd_dq", st);
   hipLaunchKernelGGL((attn_bwd_dq_mfma<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(512), 0, st,
@@ -904,6 +1087,16 @@ static void bwd_f32(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
                      (const float*)a.v, a.ldqkv, (const float*)a.d_o, a.lddo, (float*)a.dk, (float*)a.dv,
                      a.lddqkv, (const float*)a.zk, (const float*)a.zv, a.ldz, pv.seg, a.B, a.T, a.ts,
                      a.alpha, a.scale);
+}
+
+size_t attn_ds_bytes(int B, int64_t T, int max_len, int H) {
+  if (B <= 0 || T <= 0 || max_len <= 0 || H <= 0) return 0;
+  const int64_t M = max_len < T ? max_len : T;
+  const int64_t ntm = (M + 127) / 128;
+  const int64_t by_rows = (int64_t)B * ntm * ntm;
+  const int64_t by_tokens = (M * T + 254 * T + 16129 * (int64_t)B + 16383) / 16384;
+  const int64_t tiles = by_rows < by_tokens ? by_rows : by_tokens;
+  return align_up((size_t)tiles * H * DS_TILE_BYTES, 256);
 }
 
 int launch_attn_fwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t st) {

@@ -37,6 +37,7 @@ struct PrepView {
   int32_t* seg;      // [B, 5]
   TileList q;        // ATTN_QTILE-row tiles
   TileList k;        // ATTN_KTILE-row tiles
+  int64_t* tprefix;  // [B + 1] exclusive prefix of ceil(L / 128)^2
 };
 int64_t max_tiles(int B, int64_t T, int rows_per_tile);
 size_t prep_workspace_bytes(int B, int64_t T);
@@ -106,7 +107,16 @@ struct AttnArgs {
   const int64_t* ts;
   int B; int64_t T; int H; int dh;
   float alpha, scale;
+  // backward only: dS buffer of ds_cap tile pairs per head (32 KB each in
+  // 16-bit types).  When set, the dK/dV kernel stores dS there and dQ
+  // streams it; when NULL, dQ recomputes S and dA.
+  void* ds; int64_t ds_cap;
 };
+// Bytes of dS storage that a batch of B rows, T tokens and rows of at most
+// max_len tokens can need: H * 32 KB per 128 x 128 tile pair, with
+// sum_b ceil(L_b / 128)^2 <= min(B ceil(M / 128)^2, (M T + 254 T + 16129 B) / 16384).
+size_t attn_ds_bytes(int B, int64_t T, int max_len, int H);
+constexpr size_t DS_TILE_BYTES = 32768;  // one 128-query x 128-key tile of 16-bit dS
 int launch_attn_fwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t stream);
 int launch_attn_bwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t stream);
 

@@ -110,6 +110,51 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
   if (tid == 0) *ntiles = carry;
 }
 
+// One workgroup: exclusive prefix over users (in user order) of n_t^2,
+// n_t = ceil(L / 128); out[B] is the total.  n_t^2 is the number of
+// 128 x 128 (query, key) tile pairs a user's backward keeps dS for, so the
+// prefix places each user's dS tiles in one packed buffer.
+__global__ __launch_bounds__(1024) void tile_square_prefix_kernel(const int32_t* __restrict__ offsets, int B,
+                                                                  int64_t* __restrict__ out) {
+  __shared__ long long warp_sums[16];
+  __shared__ long long carry;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 1024) {
+    const int b = base + tid;
+    long long v0 = 0;
+    if (b < B) {
+      const long long nt = (offsets[b + 1] - offsets[b] + 127) / 128;
+      v0 = nt * nt;
+    }
+    long long v = v0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
+    }
+    if (lane == 63) warp_sums[w] = v;
+    __syncthreads();
+    if (tid < 64) {
+      long long s = tid < 16 ? warp_sums[tid] : 0;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const long long t = __shfl_up(s, off, 64);
+        if (tid >= off) s += t;
+      }
+      if (tid < 16) warp_sums[tid] = s;
+    }
+    __syncthreads();
+    const long long excl = carry + (w > 0 ? warp_sums[w - 1] : 0) + v - v0;
+    if (b < B) out[b] = excl;
+    __syncthreads();
+    if (tid == 1023) carry = excl + v0;
+    __syncthreads();
+  }
+  if (tid == 0) out[B] = carry;
+}
+
 int64_t max_tiles(int B, int64_t T, int rows_per_tile) {
   return (T + rows_per_tile - 1) / rows_per_tile + B;
 }
@@ -121,6 +166,7 @@ size_t prep_workspace_bytes(int B, int64_t T) {
   n += align_up((size_t)B * sizeof(int32_t), 256);           // order scratch
   n += align_up((size_t)max_tiles(B, T, ATTN_QTILE) * sizeof(int2), 256);
   n += align_up((size_t)max_tiles(B, T, ATTN_KTILE) * sizeof(int2), 256);
+  n += align_up((size_t)(B + 1) * sizeof(int64_t), 256);    // dS tile prefix
   return n;
 }
 
@@ -139,6 +185,8 @@ int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t
   p += align_up((size_t)out->q.max_tiles * sizeof(int2), 256);
   out->k.tiles = (int2*)p;
   out->k.max_tiles = max_tiles(B, T, ATTN_KTILE);
+  p += align_up((size_t)out->k.max_tiles * sizeof(int2), 256);
+  out->tprefix = (int64_t*)p;
   if (B > 0) {
     hipLaunchKernelGGL(seg_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, offsets, group_ids, B,
                        out->seg);
@@ -149,6 +197,8 @@ int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t
   MTGR_LAUNCH_CHECK();
   hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, ATTN_KTILE, order,
                      out->k.tiles, out->k.ntiles);
+  MTGR_LAUNCH_CHECK();
+  hipLaunchKernelGGL(tile_square_prefix_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, out->tprefix);
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
 }

@@ -82,9 +82,15 @@ const char* mtgr_version(void);
 const char* mtgr_status_string(int status);
 
 /* Bytes of workspace `op` needs for these sizes (0 = none).  d = model width,
- * H = heads.  The value only grows with B and T, so a workspace sized for the
+ * H = heads, max_len = an upper bound on every row's length (tokens), used
+ * only by the backward ops in bf16/f16: with max_len > 0 their workspace also
+ * holds the score gradients dS of the whole batch (H * 32 KB per 128 x 128
+ * block of a row, bounded from B, T and max_len), which the dK/dV pass writes
+ * and the dQ pass streams instead of recomputing the scores; with
+ * max_len = 0 the dQ pass recomputes them and the workspace is small.  The
+ * value only grows with B, T and max_len, so a workspace sized for the
  * largest batch serves every smaller one. */
-size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t d, int32_t H, int dt);
+size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t max_len, int32_t d, int32_t H, int dt);
 
 /*
  * a1 - jagged segments.  For each user b writes seg[b*5 + 0..4] =
@@ -137,7 +143,7 @@ int mtgr_group_layernorm_bwd(const void* dy, const void* x, const float* mean, c
  *   q, k, v : [T, H*dh] views with row stride ld_qkv elements (they may point
  *             into one fused [T, 4d] buffer); head h = columns h*dh..h*dh+dh-1
  *   o       : [T, H*dh] with row stride ld_o, written
- *   bf16/f16: dh in {64, 128} (MFMA kernels); f32: dh <= 128, dh % 4 == 0.
+ *   bf16/f16: dh in {64, 128} (MFMA kernels); f32: dh in {16, 32, 64, 128}.
  *   workspace : MTGR_OP_ATTN_FWD bytes
  */
 int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv, void* o,
@@ -153,14 +159,20 @@ int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_q
  * weights are recomputed; nothing is saved by the forward.
  *   d_o          : [T, H*dh] with row stride ld_do
  *   dq, dk, dv   : [T, H*dh] with row stride ld_dqkv, OVERWRITTEN
- *   workspace    : MTGR_OP_ATTN_BWD bytes
+ *   max_len      : 0, or an upper bound on every row's length (see
+ *                  mtgr_workspace_size); in bf16/f16 with max_len > 0 the
+ *                  workspace must hold MTGR_OP_ATTN_BWD bytes for that
+ *                  max_len, else MTGR_ERR_WORKSPACE_TOO_SMALL.  A row longer
+ *                  than max_len whose dS blocks then do not fit gets NaN in
+ *                  its dq rows (never an out-of-range access).
+ *   workspace    : MTGR_OP_ATTN_BWD bytes for the same B, T, max_len, H
  */
 int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_qkv,
                        const void* d_o, int64_t ld_do, void* dq, void* dk, void* dv,
                        int64_t ld_dqkv, const int32_t* offsets, const uint8_t* group_ids,
-                       const int64_t* timestamps, int32_t B, int64_t T, int32_t H, int32_t dh,
-                       float alpha, float attn_scale, int dt, void* workspace, size_t ws_bytes,
-                       mtgr_stream_t stream);
+                       const int64_t* timestamps, int32_t B, int64_t T, int32_t max_len, int32_t H,
+                       int32_t dh, float alpha, float attn_scale, int dt, void* workspace,
+                       size_t ws_bytes, mtgr_stream_t stream);
 
 /* Weights of one layer, all device memory of dtype dt. */
 typedef struct {
@@ -238,13 +250,14 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
  *   dx_out      : [T, d] upstream gradient; dx_in : [T, d] written
  *   grads       : fp32 weight gradients, overwritten
  *   extras      : NULL or intermediate gradients to copy out
- *   workspace   : MTGR_OP_LAYER_BWD bytes
+ *   max_len     : as for mtgr_hstu_attn_bwd
+ *   workspace   : MTGR_OP_LAYER_BWD bytes for the same B, T, max_len, d, H
  */
 int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr_layer_saved* saved,
                         const void* dx_out, void* dx_in, const mtgr_layer_grads* grads,
                         const mtgr_layer_bwd_extras* extras, const int32_t* offsets,
                         const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T,
-                        float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                        int32_t max_len, float attn_scale, int dt, void* workspace, size_t ws_bytes,
                         mtgr_stream_t stream);
 
 /*

@@ -63,10 +63,69 @@ def test_workspace_sizes_grow(lib):
     import torch
 
     for op in (b.OP_ATTN_FWD, b.OP_ATTN_BWD, b.OP_LAYER_FWD, b.OP_LAYER_BWD, b.OP_GLN_BWD):
-        a = b.mtgr_workspace_size(op, 8, 1000, 256, 2, torch.bfloat16)
-        c = b.mtgr_workspace_size(op, 80, 65536, 256, 2, torch.bfloat16)
+        a = b.mtgr_workspace_size(op, 8, 1000, 0, 256, 2, torch.bfloat16)
+        c = b.mtgr_workspace_size(op, 80, 65536, 0, 256, 2, torch.bfloat16)
         assert 0 < a <= c
-    assert b.mtgr_workspace_size(b.OP_GLN_FWD, 8, 1000, 256, 2, torch.bfloat16) == 0
+    assert b.mtgr_workspace_size(b.OP_GLN_FWD, 8, 1000, 0, 256, 2, torch.bfloat16) == 0
+
+
+def test_stored_ds_workspace_covers_every_batch(lib):
+    """With a row bound M the backward workspace holds the score gradients of
+    any batch whose rows are at most M long: H * 32 KB per 128 x 128 block,
+    sum_b ceil(L_b / 128)^2 blocks (brute force over random and extreme
+    length mixes); fp32 and M = 0 add nothing."""
+    from generative_recommendation_ranking_grouplayernorm_amd import binding as b
+    import torch
+
+    rng = np.random.default_rng(8)
+    H, d = 8, 1024
+    cases = []
+    for _ in range(300):
+        B = int(rng.integers(1, 200))
+        M = int(rng.integers(1, 5000))
+        kind = rng.integers(0, 4)
+        if kind == 0:
+            L = rng.integers(0, M + 1, size=B)
+        elif kind == 1:
+            L = np.full(B, M)
+        elif kind == 2:
+            L = np.ones(B, dtype=np.int64)
+            L[0] = M
+        else:
+            L = np.minimum(M, rng.geometric(1.0 / max(M / 4, 1), size=B))
+        cases.append((B, int(L.sum()), M, L))
+    for B, T, M, L in cases:
+        need = H * 32768 * int((((L + 127) // 128) ** 2).sum())
+        for op in (b.OP_ATTN_BWD, b.OP_LAYER_BWD):
+            extra = (b.mtgr_workspace_size(op, B, T, M, d, H, torch.bfloat16)
+                     - b.mtgr_workspace_size(op, B, T, 0, d, H, torch.bfloat16))
+            assert extra >= need, (B, T, M, extra, need)
+            assert (b.mtgr_workspace_size(op, B, T, M, d, H, torch.float32)
+                    == b.mtgr_workspace_size(op, B, T, 0, d, H, torch.float32))
+    # monotone in the bound
+    a = b.mtgr_workspace_size(b.OP_ATTN_BWD, 100, 60000, 1000, d, H, torch.bfloat16)
+    c = b.mtgr_workspace_size(b.OP_ATTN_BWD, 100, 60000, 3000, d, H, torch.bfloat16)
+    assert a < c
+
+
+def test_attn_bwd_bound_errors(lib):
+    """A negative row bound is an argument error; a workspace without room
+    for the bound's dS is too small (both before any launch)."""
+    from generative_recommendation_ranking_grouplayernorm_amd import binding as b
+    import torch
+
+    P = ctypes.c_void_p
+    small = b.mtgr_workspace_size(b.OP_ATTN_BWD, 1, 10, 0, 256, 2, torch.bfloat16)
+    big = b.mtgr_workspace_size(b.OP_ATTN_BWD, 1, 10, 10, 256, 2, torch.bfloat16)
+    assert big > small
+
+    def call(max_len, ws_bytes):
+        return lib.mtgr_hstu_attn_bwd(P(8192), P(8192), P(8192), 256, P(8192), 256, P(8192), P(8192), P(8192),
+                                      256, P(4096), P(4096), P(4096), 1, 10, max_len, 2, 128, 1.0, 0.1, 1,
+                                      P(8192), ws_bytes, None)
+
+    assert call(-1, big) == -1
+    assert call(10, small) == -3
 
 
 def _call_attn_fwd(lib, **kw):

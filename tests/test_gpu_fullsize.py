@@ -70,8 +70,10 @@ def test_cfg4_layer_fwd_bwd_sampled_users(mb):
     dx = torch.empty_like(x_out)
     ex = dict(d_uqkv=torch.empty(batch.T, 4 * d, dtype=dtype, device=DEV),
               d_o=torch.empty(batch.T, d, dtype=dtype, device=DEV))
+    ml = int(batch.max_len)
     mb.mtgr_hstu_layer_bwd(prm, xt.to(DEV), mb.make_saved(saved), Rt.to(DEV), dx, grads, off, g, ts, scale,
-                           mb.workspace(mb.OP_LAYER_BWD, batch.B, batch.T, d, H, dtype, DEV), extras=ex)
+                           mb.workspace(mb.OP_LAYER_BWD, batch.B, batch.T, d, H, dtype, DEV, max_len=ml), extras=ex,
+                           max_len=ml)
     torch.cuda.synchronize()
 
     users = shortest_users(batch, 2)
@@ -133,8 +135,9 @@ def test_cfg4_weight_grads_on_user_slice(mb):
                            mb.workspace(mb.OP_LAYER_FWD, sub.B, sub.T, d, H, dtype, DEV))
     grads = mb.alloc_grads(d, G, False, DEV)
     dx = torch.empty_like(x_out)
+    ml = int(np.diff(sub.offsets).max())
     mb.mtgr_hstu_layer_bwd(prm, xt.to(DEV), mb.make_saved(saved), Rt.to(DEV), dx, grads, off, g, ts, scale,
-                           mb.workspace(mb.OP_LAYER_BWD, sub.B, sub.T, d, H, dtype, DEV))
+                           mb.workspace(mb.OP_LAYER_BWD, sub.B, sub.T, d, H, dtype, DEV, max_len=ml), max_len=ml)
     torch.cuda.synchronize()
     _, sv = orc.layer_fwd(q, f64(xt), o2, g2, t2, 1.0, scale)
     _, rg = orc.layer_bwd(q, f64(xt), sv, f64(Rt), o2, g2, t2, 1.0, scale)

@@ -96,15 +96,19 @@ def _attn_case(batch, d, H, dtype, seed, scale_qk=0.35):
     return uqkv, d_o
 
 
-def _run_attention(mb, batch, d, H, dtype, seed, alpha=1.0, with_bwd=True):
+def _run_attention(mb, batch, d, H, dtype, seed, alpha=1.0, with_bwd=True, max_len=None):
+    """max_len None: the batch's longest row (dS stored by the dK/dV pass and
+    streamed by dQ); 0: dQ recomputes the scores."""
     dh = d // H
+    if max_len is None:
+        max_len = int(batch.max_len)
     uqkv, d_o = _attn_case(batch, d, H, dtype, seed)
     scale = 1.0 / max(batch.max_len, 1)
     off, g, ts = meta(batch, DEV)
     U = uqkv.to(DEV)
     q, k, v = U[:, d:2 * d], U[:, 2 * d:3 * d], U[:, 3 * d:]
     o = torch.full((batch.T, d), float("nan"), dtype=dtype, device=DEV)
-    ws = mb.workspace(mb.OP_ATTN_BWD, batch.B, batch.T, d, H, dtype, DEV)
+    ws = mb.workspace(mb.OP_ATTN_BWD, batch.B, batch.T, d, H, dtype, DEV, max_len=max_len)
     mb.mtgr_hstu_attn_fwd(q, k, v, o, off, g, ts, H, dh, alpha, scale, ws)
     qn, kn, vn = (f64(t) for t in (uqkv[:, d:2 * d], uqkv[:, 2 * d:3 * d], uqkv[:, 3 * d:]))
     ro = orc.hstu_attention(qn, kn, vn, batch.offsets, batch.group_ids, batch.timestamps, H, alpha, scale)
@@ -112,7 +116,8 @@ def _run_attention(mb, batch, d, H, dtype, seed, alpha=1.0, with_bwd=True):
     if with_bwd:
         dqkv = torch.full((batch.T, 3 * d), float("nan"), dtype=dtype, device=DEV)
         dq, dk, dv = dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:]
-        mb.mtgr_hstu_attn_bwd(q, k, v, d_o.to(DEV), dq, dk, dv, off, g, ts, H, dh, alpha, scale, ws)
+        mb.mtgr_hstu_attn_bwd(q, k, v, d_o.to(DEV), dq, dk, dv, off, g, ts, H, dh, alpha, scale, ws,
+                              max_len=max_len)
         rq, rk, rv = orc.hstu_attention_bwd(qn, kn, vn, f64(d_o), batch.offsets, batch.group_ids,
                                             batch.timestamps, H, alpha, scale)
         res.update(dq=(f64(dq), rq), dk=(f64(dk), rk), dv=(f64(dv), rv))
@@ -123,10 +128,13 @@ def _run_attention(mb, batch, d, H, dtype, seed, alpha=1.0, with_bwd=True):
 @pytest.mark.parametrize("dtype,d,H", [(torch.float32, 64, 2), (torch.bfloat16, 256, 2),
                                        (torch.float16, 256, 2), (torch.bfloat16, 256, 4)])
 @pytest.mark.parametrize("which", ["cfg1", "edge"])
-def test_attention_parity(mb, dtype, d, H, which):
+@pytest.mark.parametrize("ds", ["stored", "recomputed"])
+def test_attention_parity(mb, dtype, d, H, which, ds):
+    if dtype == torch.float32 and ds == "recomputed":
+        pytest.skip("fp32 has one backward path")
     batch = make_batch(1) if which == "cfg1" else edge_batch()
-    say("attention", which, dtype, d, H, batch.B, batch.T)
-    res = _run_attention(mb, batch, d, H, dtype, seed=3)
+    say("attention", which, dtype, d, H, batch.B, batch.T, ds)
+    res = _run_attention(mb, batch, d, H, dtype, seed=3, max_len=None if ds == "stored" else 0)
     for name, (got, ref) in res.items():
         assert np.isfinite(got).all(), name
         err = rel_l2(got, ref)
@@ -134,15 +142,37 @@ def test_attention_parity(mb, dtype, d, H, which):
         assert err <= TOL[dtype], (name, err)
 
 
-def test_attention_bf16_long_users(mb):
+@pytest.mark.parametrize("ds", ["stored", "recomputed"])
+def test_attention_bf16_long_users(mb, ds):
     """Several 128-row tiles per user, mixed tails, alpha != 1."""
     rng = np.random.default_rng(12)
     lengths = [[8, 700, 40, 20], [8, 333, 64, 20], [8, 50, 3, 180], [4, 1000, 0, 20]]
     batch = make_batch_from_lengths(lengths, rng, ts_max=86400)
-    say("attention long users", batch.T)
-    res = _run_attention(mb, batch, 256, 2, torch.bfloat16, seed=5, alpha=0.7)
+    say("attention long users", batch.T, ds)
+    res = _run_attention(mb, batch, 256, 2, torch.bfloat16, seed=5, alpha=0.7,
+                         max_len=None if ds == "stored" else 0)
     for name, (got, ref) in res.items():
         err = rel_l2(got, ref)
+        say(f"  {name}: rel-L2 {err:.3e}")
+        assert err <= 1e-2, (name, err)
+
+
+def test_attention_bwd_row_longer_than_bound(mb):
+    """A row longer than the declared bound whose dS does not fit the
+    workspace: its dQ rows come back NaN, every other output is right."""
+    rng = np.random.default_rng(21)
+    lengths = [[8, 60, 10, 20], [8, 20, 5, 10], [2, 30, 0, 6], [8, 900, 40, 30]]
+    batch = make_batch_from_lengths(lengths, rng, ts_max=86400)
+    say("attention bwd, bound 128 < longest row", batch.T)
+    res = _run_attention(mb, batch, 256, 2, torch.bfloat16, seed=6, max_len=128)
+    last = slice(int(batch.offsets[3]), int(batch.offsets[4]))
+    head = slice(0, int(batch.offsets[3]))
+    got, ref = res["dq"]
+    assert np.isnan(got[last]).all()
+    assert rel_l2(got[head], ref[head]) <= 1e-2
+    for name in ("o", "dk", "dv"):
+        g_, r_ = res[name]
+        err = rel_l2(g_, r_)
         say(f"  {name}: rel-L2 {err:.3e}")
         assert err <= 1e-2, (name, err)
 

@@ -23,8 +23,10 @@ def mb():
     return b
 
 
-def run_layer(mb, batch, p, x, dtype, R=None, scale=None, extras=True):
-    """GPU forward (+ backward when R is given).  Returns dict of numpy fp64."""
+def run_layer(mb, batch, p, x, dtype, R=None, scale=None, extras=True, stored_ds=True):
+    """GPU forward (+ backward when R is given).  Returns dict of numpy fp64.
+    stored_ds: the backward keeps dS for the dQ pass (row bound given) or
+    recomputes it (no bound)."""
     scale = scale if scale is not None else 1.0 / batch.max_len
     d, H = p.d, p.H
     G = p.gamma1.shape[0]
@@ -47,9 +49,10 @@ def run_layer(mb, batch, p, x, dtype, R=None, scale=None, extras=True):
         if extras:
             ex = dict(d_uqkv=torch.empty(batch.T, 4 * d, dtype=dtype, device=DEV),
                       d_o=torch.empty(batch.T, d, dtype=dtype, device=DEV))
-        wsb = mb.workspace(mb.OP_LAYER_BWD, batch.B, batch.T, d, H, dtype, DEV)
+        ml = int(batch.max_len) if stored_ds else 0
+        wsb = mb.workspace(mb.OP_LAYER_BWD, batch.B, batch.T, d, H, dtype, DEV, max_len=ml)
         mb.mtgr_hstu_layer_bwd(params, xd, mb.make_saved(saved), Rt.to(DEV), dx, grads, off, g, ts, scale, wsb,
-                               extras=ex)
+                               extras=ex, max_len=ml)
         out["dx"] = f64(dx)
         out.update({"g_" + k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()})
         if ex:
@@ -99,16 +102,17 @@ def test_layer_cfg1_fp32_fwd_bwd(mb):
     check(res, oracle_layer(batch, res, True), torch.float32)
 
 
+@pytest.mark.parametrize("stored_ds", [True, False])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_layer_small_halfprec_fwd_bwd(mb, dtype):
+def test_layer_small_halfprec_fwd_bwd(mb, dtype, stored_ds):
     rng = np.random.default_rng(31)
     lengths = [[8, 260, 30, 20], [8, 33, 0, 20], [8, 129, 64, 7], [0, 0, 9, 4], [8, 500, 12, 60]]
     batch = make_batch_from_lengths(lengths, rng, ts_max=86400)
     p = make_layer_params(256, 2, rng, "xavier", False)
     x = rng.normal(0, 1, size=(batch.T, 256))
     R = rng.normal(0, 1, size=x.shape)
-    say("layer small", dtype, batch.T)
-    res = run_layer(mb, batch, p, x, dtype, R=R)
+    say("layer small", dtype, batch.T, "stored dS" if stored_ds else "recomputed dS")
+    res = run_layer(mb, batch, p, x, dtype, R=R, stored_ds=stored_ds)
     check(res, oracle_layer(batch, res, True), dtype)
 
 
