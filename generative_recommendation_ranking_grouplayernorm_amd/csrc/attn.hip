@@ -152,7 +152,7 @@ inline unsigned xcd_grid(int64_t max_tiles, int H) {
 // range is wave-uniform, so advancing a tile changes only scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* P, int64_t ld, int r0, int rlim,
                                                          int col0) {
-  return make_rsrc(P + (int64_t)r0 * ld + col0, (int)((int64_t)(rlim - r0) * ld * 2));
+  return make_rsrc(P + (int64_t)r0 * ld + col0, (int)((int64_t)max(rlim - r0, 0) * ld * 2));
 }
 
 // Tile load: thread chunks c = tid + 256 i, row c / (DH/8), 8 columns.
@@ -250,6 +250,67 @@ __device__ __forceinline__ op8 vt_operand(const uint16_t* s, int u, int col0, in
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue: one wave's 32-row accumulator tile to 16-bit rows
+// ---------------------------------------------------------------------------
+// acc[b] holds column 32 (cb0 + b) + l32 (relative to col0) of rows
+// r0 + 8 (j >> 2) + 4 g + (j & 3).  out[row, col] = acc * scale, times
+// SiLU'(z[row, col]) when z is given; rows at or beyond rlim are not written.
+// Two column blocks at a time pass through a wave-private LDS stage of
+// 32 x 64 floats, so that z is read and out written 16 bytes per lane (all
+// loads of a round issued before any is used) with the buffer range check
+// doing the row bound.  The pitch of 72 floats puts the two lane halves of a
+// stage write on different banks.
+constexpr int EP_PITCH = 72;
+constexpr int EP_FLOATS = 32 * EP_PITCH;  // per wave
+
+template <typename T, int NB>
+__device__ __forceinline__ void wave_store_rows(float* stage, const f32x16_t (&acc)[NB], int cb0, int lane,
+                                                int r0, int rlim, float scale, uint16_t* out, int64_t ldo,
+                                                int col0, const uint16_t* z, int64_t ldz) {
+  constexpr int NBR = NB < 2 ? NB : 2;    // column blocks per round
+  constexpr int CPR = NBR * 4;            // 8-column chunks per row
+  constexpr int RPP = 64 / CPR;           // rows per pass
+  constexpr int NP = 32 / RPP;            // passes per round
+  const int l32 = lane & 31, g = lane >> 5;
+  const __amdgpu_buffer_rsrc_t ro = rows_rsrc(out, ldo, r0, rlim, col0);
+  const __amdgpu_buffer_rsrc_t rz = rows_rsrc(z ? z : out, ldz, r0, rlim, col0);
+  const int pr = lane / CPR, pc = (lane % CPR) * 8;
+#pragma unroll
+  for (int b0 = 0; b0 < NB; b0 += NBR) {
+#pragma unroll
+    for (int b = 0; b < NBR; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        stage[(8 * (j >> 2) + 4 * g + (j & 3)) * EP_PITCH + 32 * b + l32] = acc[b0 + b][j] * scale;
+    const int colb = 32 * (cb0 + b0) + pc;
+    uint4 zz[NP];
+    if (z) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) zz[p] = buf_load16(rz, ((p * RPP + pr) * (int)ldz + colb) * 2);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int rr = p * RPP + pr;
+      const f32x4_t a = *(const f32x4_t*)&stage[rr * EP_PITCH + pc];
+      const f32x4_t c = *(const f32x4_t*)&stage[rr * EP_PITCH + pc + 4];
+      float v[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+      if (z) {
+        const uint32_t zw[4] = {zz[p].x, zz[p].y, zz[p].z, zz[p].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float zf = from_bits16<T>((uint16_t)(zw[e >> 1] >> (16 * (e & 1))));
+          v[e] *= silu_grad_from(zf, 1.0f / (1.0f + __expf(-zf)));
+        }
+      }
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack2<T>(v[2 * e], v[2 * e + 1]);
+      buf_store16(ro, (rr * (int)ldo + colb) * 2, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // forward: 128 queries per workgroup (4 waves x 32), 64 keys per LDS stage,
 // two workgroups per CU so that one wave's SiLU overlaps another's MFMAs.
 // ---------------------------------------------------------------------------
@@ -299,15 +360,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
     int H, float kexp, float out_scale) {
   constexpr int KP = AttnPitch<DH>::B128;
   constexpr int NS = DH / 16, NC = DH / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][F_BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DH * VT_PITCH];
+  struct Smem {
+    uint16_t Ks[2][F_BK * KP];
+    uint16_t Vt[2][DH * VT_PITCH];
+  };
+  __shared__ __attribute__((aligned(16))) union {
+    Smem m;
+    float ep[4 * EP_FLOATS];
+  } sm;
+  auto& Ks = sm.m.Ks;
+  auto& Vt = sm.m.Vt;
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
   const int2 te = tiles[tile];
   const int b = te.x, q0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), l32 = lane & 31, g = lane >> 5;
   const int q_last = min(q0 + F_BQ, hi) - 1;
   const int kv_end = key_end_for(q_last, s_end, r_end);
   const int qi = q0 + wave * 32 + l32;
@@ -369,13 +438,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int row = q0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (row < hi) O[(int64_t)row * ldo + hc + c * 32 + l32] = bits16<T>(oacc[c][j] * out_scale);
-    }
+  wave_store_rows<T, NC>(sm.ep + wave * EP_FLOATS, oacc, 0, lane, q0 + wave * 32, hi, out_scale, O, ldo, hc,
+                         nullptr, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -411,17 +475,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     int H, float kexp, float alpha, float out_scale) {
   constexpr int KP = AttnPitch<DH>::B128;
   constexpr int NS = DH / 16, NC = DH / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][A_BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][A_BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][DH * VT_PITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t Fx[4][32 * 16 * 2];
+  struct Smem {
+    uint16_t Ks[2][A_BK * KP];
+    uint16_t Vs[2][A_BK * KP];
+    uint16_t Kt[2][DH * VT_PITCH];
+    uint32_t Fx[4][32 * 16 * 2];
+  };
+  __shared__ __attribute__((aligned(16))) union {
+    Smem m;
+    float ep[8 * EP_FLOATS];
+  } sm;
+  auto& Ks = sm.m.Ks;
+  auto& Vs = sm.m.Vs;
+  auto& Kt = sm.m.Kt;
+  auto& Fx = sm.m.Fx;
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
   const int2 te = tiles[tile];
   const int b = te.x, q0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), l32 = lane & 31, g = lane >> 5;
   const bool producer = wave < 4;
   const int grp = wave & 3;
   const int ltid = tid & 255;
@@ -538,22 +612,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
-  const int cb = producer ? 0 : NC / 2;
-#pragma unroll
-  for (int c = 0; c < NC / 2; ++c)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int row = q0 + grp * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (row < hi) {
-        float v = acc[c][j] * out_scale;
-        const int col = hc + (cb + c) * 32 + l32;
-        if (zq) {
-          const float z = from_bits16<T>(zq[(int64_t)row * ldz + col]);
-          v *= silu_grad_from(z, 1.0f / (1.0f + __expf(-z)));
-        }
-        dQ[(int64_t)row * lddq + col] = bits16<T>(v);
-      }
-    }
+  wave_store_rows<T, NC / 2>(sm.ep + wave * EP_FLOATS, acc, producer ? 0 : NC / 2, lane, q0 + grp * 32, hi,
+                             out_scale, dQ, lddq, hc, zq, ldz);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,18 +639,29 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     const int64_t* __restrict__ tprefix) {
   constexpr int QP = AttnPitch<DH>::B128;
   constexpr int NS = DH / 16, NC = DH / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][KV_BQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][KV_BQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][DH * VT_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][DH * VT_PITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t Fx[4][32 * 16 * 2];  // per group: 2 x 16 x 32 lanes
+  struct Smem {
+    uint16_t Qs[2][KV_BQ * QP];
+    uint16_t Ds[2][KV_BQ * QP];
+    uint16_t Qt[2][DH * VT_PITCH];
+    uint16_t Dt[2][DH * VT_PITCH];
+    uint32_t Fx[4][32 * 16 * 2];  // per group: 2 x 16 x 32 lanes
+  };
+  __shared__ __attribute__((aligned(16))) union {
+    Smem m;
+    float ep[8 * EP_FLOATS];
+  } sm;
+  auto& Qs = sm.m.Qs;
+  auto& Ds = sm.m.Ds;
+  auto& Qt = sm.m.Qt;
+  auto& Dt = sm.m.Dt;
+  auto& Fx = sm.m.Fx;
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
   const int2 te = tiles[tile];
   const int b = te.x, k0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), l32 = lane & 31, g = lane >> 5;
   const bool producer = wave < 4;   // S-side wave; wave + 4 is its dA-side partner
   const int grp = wave & 3;
   const int ltid = tid & 255;
@@ -732,24 +803,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     __syncthreads();
   }
   // producer holds dV, consumer dK; both scale by alpha * c
-  const float f = alpha * scale;
-  const uint16_t* z = producer ? zv : zk;
-  uint16_t* dst = producer ? dV : dK;
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int row = k0 + grp * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (row < hi) {
-        const int col = hc + c * 32 + l32;
-        float a = acc[c][j] * f;
-        if (z) {
-          const float zz = from_bits16<T>(z[(int64_t)row * ldz + col]);
-          a *= silu_grad_from(zz, 1.0f / (1.0f + __expf(-zz)));
-        }
-        dst[(int64_t)row * lddkv + col] = bits16<T>(a);
-      }
-    }
+  wave_store_rows<T, NC>(sm.ep + wave * EP_FLOATS, acc, 0, lane, k0 + grp * 32, hi, alpha * scale,
+                         producer ? dV : dK, lddkv, hc, producer ? zv : zk, ldz);
 }
 
 // ---------------------------------------------------------------------------
@@ -785,15 +840,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
     const uint16_t* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
     const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles, int H, float out_scale) {
   constexpr int NC = DH / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t Ss[2][16384];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][DH * VT_PITCH];
+  struct Smem {
+    uint8_t Ss[2][16384];
+    uint16_t Kt[2][DH * VT_PITCH];
+  };
+  __shared__ __attribute__((aligned(16))) union {
+    Smem m;
+    float ep[4 * EP_FLOATS];
+  } sm;
+  auto& Ss = sm.m.Ss;
+  auto& Kt = sm.m.Kt;
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
   const int2 te = tiles[tile];
   const int b = te.x, q0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), l32 = lane & 31, g = lane >> 5;
   const int hc = h * DH;
   const int nt = (hi - lo + 127) >> 7;
   const int qt = (q0 - lo) >> 7;
@@ -880,21 +943,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int row = q0 + wave * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-      if (row < hi) {
-        float v = acc[c][j] * out_scale;
-        const int col = hc + c * 32 + l32;
-        if (zq) {
-          const float z = from_bits16<T>(zq[(int64_t)row * ldz + col]);
-          v *= silu_grad_from(z, 1.0f / (1.0f + __expf(-z)));
-        }
-        dQ[(int64_t)row * lddq + col] = bits16<T>(v);
-      }
-    }
+  wave_store_rows<T, NC>(sm.ep + wave * EP_FLOATS, acc, 0, lane, q0 + wave * 32, hi, out_scale, dQ, lddq, hc, zq,
+                         ldz);
 }
 
 // ---------------------------------------------------------------------------

@@ -83,6 +83,16 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
   i32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return __builtin_bit_cast(uint4, x);
 }
+// 16-byte store through a buffer resource: stores at offsets at or beyond
+// the resource's size are dropped by the hardware range check.
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), r, off, 0, 0);
+}
+
+// Index of the calling wave in its workgroup, as a value the compiler knows
+// to be the same on every lane (held in a scalar register, so branches on it
+// are scalar branches and buffer resources built from it stay scalar).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // LDS transpose read of gfx950: the 16 lanes of each quarter-wave together
 // read a 4 (rows) x 16 (columns) block of 16-bit values, lane 4*r + c
