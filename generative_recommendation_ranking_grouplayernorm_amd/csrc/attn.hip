@@ -37,6 +37,16 @@ __device__ __forceinline__ bool mask_visible(int qi, int kj, int s_end, int r_en
   return kj == qi && kj < hi;                                    // candidate key
 }
 
+// Same test with both timestamps at hand (tiles keep them in LDS), without
+// branches: U/S keys are seen by all; a real-time key by real-time and
+// candidate queries with a later timestamp, and by itself; a candidate key
+// only by itself.  Rows beyond the user's end carry zero Q/K/V/dO, so their
+// products vanish without a test.
+__device__ __forceinline__ bool visible_ts(int qi, int kj, int s_end, int r_end, int64_t tq, int64_t tk) {
+  const bool rt = qi >= s_end && (tk < tq || kj == qi);
+  return kj < s_end || (kj < r_end ? rt : kj == qi);
+}
+
 // Key range a query tile [q0, q_last] needs: static queries stop at the end
 // of S, real-time queries at the end of R, candidates at themselves.
 __device__ __forceinline__ int key_end_for(int q_last, int s_end, int r_end) {
@@ -318,10 +328,9 @@ constexpr int F_BQ = 128;
 constexpr int F_BK = 64;
 
 template <typename T, int DH, bool MASKED>
-__device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt, const op8 (&qop)[DH / 16],
-                                         f32x16_t (&oacc)[DH / 32], int k0, int qi, int64_t tq, int s_end,
-                                         int r_end, int hi, const int64_t* __restrict__ ts, float kexp,
-                                         int lane) {
+__device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt, const int64_t* tsk,
+                                         const op8 (&qop)[DH / 16], f32x16_t (&oacc)[DH / 32], int k0, int qi,
+                                         int64_t tq, int s_end, int r_end, float kexp, int lane) {
   constexpr int KP = AttnPitch<DH>::B128;
   const int g = lane >> 5;
   f32x16_t sacc[2];
@@ -339,8 +348,8 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt,
       const float sv = sacc[t][j];
       float pv = sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv * kexp));
       if (MASKED) {
-        const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-        if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) pv = 0.f;
+        const int kk = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+        if (!visible_ts(qi, k0 + kk, s_end, r_end, tq, tsk[kk])) pv = 0.f;
       }
       p[t][j] = pv;
     }
@@ -363,6 +372,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   struct Smem {
     uint16_t Ks[2][F_BK * KP];
     uint16_t Vt[2][DH * VT_PITCH];
+    int64_t Tk[2][F_BK];  // key timestamps of the tile
   };
   __shared__ __attribute__((aligned(16))) union {
     Smem m;
@@ -370,6 +380,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   } sm;
   auto& Ks = sm.m.Ks;
   auto& Vt = sm.m.Vt;
+  auto& Tk = sm.m.Tk;
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
@@ -400,42 +411,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   constexpr int CH = F_BK * (DH / 8) / 256;
   uint4 rk[CH];
   VtLoad<DH> rv;
+  int64_t rt = 0;
   const int nkt = (kv_end - lo + F_BK - 1) / F_BK;
   // leading tiles made only of U/S keys need no mask test
   const int nfull = min(nkt, max(0, (s_end - lo) / F_BK));
+  auto gload = [&](int k0) {
+    tile_gload_rows<DH, F_BK>(rk, K, ldqkv, k0, hi, hc, tid);
+    vt_gload<DH>(rv, V, ldqkv, k0, hi, hc, tid);
+    if (wave == 0) rt = k0 + lane < hi ? ts[k0 + lane] : 0;
+  };
+  auto swrite = [&](int buf) {
+    tile_swrite_rows<DH, F_BK, KP>(Ks[buf], rk, tid);
+    vt_swrite<DH>(Vt[buf], rv);
+    if (wave == 0) Tk[buf][lane] = rt;
+  };
   if (nkt > 0) {
-    tile_gload_rows<DH, F_BK>(rk, K, ldqkv, lo, hi, hc, tid);
-    vt_gload<DH>(rv, V, ldqkv, lo, hi, hc, tid);
-    tile_swrite_rows<DH, F_BK, KP>(Ks[0], rk, tid);
-    vt_swrite<DH>(Vt[0], rv);
+    gload(lo);
+    swrite(0);
   }
   __syncthreads();
   for (int it = 0; it < nfull; ++it) {
     const int buf = it & 1, k0 = lo + it * F_BK;
     const bool more = it + 1 < nkt;
-    if (more) {
-      tile_gload_rows<DH, F_BK>(rk, K, ldqkv, k0 + F_BK, hi, hc, tid);
-      vt_gload<DH>(rv, V, ldqkv, k0 + F_BK, hi, hc, tid);
-    }
-    fwd_tile<T, DH, false>(Ks[buf], Vt[buf], qop, oacc, k0, qi, tq, s_end, r_end, hi, ts, kexp, lane);
-    if (more) {
-      tile_swrite_rows<DH, F_BK, KP>(Ks[buf ^ 1], rk, tid);
-      vt_swrite<DH>(Vt[buf ^ 1], rv);
-    }
+    if (more) gload(k0 + F_BK);
+    fwd_tile<T, DH, false>(Ks[buf], Vt[buf], Tk[buf], qop, oacc, k0, qi, tq, s_end, r_end, kexp, lane);
+    if (more) swrite(buf ^ 1);
     __syncthreads();
   }
   for (int it = nfull; it < nkt; ++it) {
     const int buf = it & 1, k0 = lo + it * F_BK;
     const bool more = it + 1 < nkt;
-    if (more) {
-      tile_gload_rows<DH, F_BK>(rk, K, ldqkv, k0 + F_BK, hi, hc, tid);
-      vt_gload<DH>(rv, V, ldqkv, k0 + F_BK, hi, hc, tid);
-    }
-    fwd_tile<T, DH, true>(Ks[buf], Vt[buf], qop, oacc, k0, qi, tq, s_end, r_end, hi, ts, kexp, lane);
-    if (more) {
-      tile_swrite_rows<DH, F_BK, KP>(Ks[buf ^ 1], rk, tid);
-      vt_swrite<DH>(Vt[buf ^ 1], rv);
-    }
+    if (more) gload(k0 + F_BK);
+    fwd_tile<T, DH, true>(Ks[buf], Vt[buf], Tk[buf], qop, oacc, k0, qi, tq, s_end, r_end, kexp, lane);
+    if (more) swrite(buf ^ 1);
     __syncthreads();
   }
   wave_store_rows<T, NC>(sm.ep + wave * EP_FLOATS, oacc, 0, lane, q0 + wave * 32, hi, out_scale, O, ldo, hc,
@@ -480,6 +488,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     uint16_t Vs[2][A_BK * KP];
     uint16_t Kt[2][DH * VT_PITCH];
     uint32_t Fx[4][32 * 16 * 2];
+    int64_t Tk[2][A_BK];  // key timestamps of the tile
   };
   __shared__ __attribute__((aligned(16))) union {
     Smem m;
@@ -489,6 +498,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   auto& Vs = sm.m.Vs;
   auto& Kt = sm.m.Kt;
   auto& Fx = sm.m.Fx;
+  auto& Tk = sm.m.Tk;
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
@@ -525,9 +535,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
 
   VtLoad<DH> ld;  // producers load K quads (row-major + transposed), consumers V rows
+  int64_t rt = 0;
   auto gload = [&](int k0) {
     if (producer) vt_gload<DH>(ld, K, ldqkv, k0, hi, hc, ltid);
     else tile_gload_rows<DH, A_BK>(ld.x, V, ldqkv, k0, hi, hc, ltid);
+    if (wave == 0) rt = k0 + lane < hi ? ts[k0 + lane] : 0;
   };
   auto swrite = [&](int buf) {
     if (producer) {
@@ -536,6 +548,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     } else {
       tile_swrite_rows<DH, A_BK, KP>(Vs[buf], ld.x, ltid);
     }
+    if (wave == 0) Tk[buf][lane] = rt;
   };
   const int nkt = (kv_end - lo + A_BK - 1) / A_BK;
   const int nfull = min(nkt, max(0, (s_end - lo) / A_BK));
@@ -568,8 +581,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
           const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
           float f = silu_grad_from(alpha * sr, sg);
           if (masked) {
-            const int kj = k0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-            if (!mask_visible(qi, kj, s_end, r_end, hi, tq, ts)) f = 0.f;
+            const int kk = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+            if (!visible_ts(qi, k0 + kk, s_end, r_end, tq, Tk[buf][kk])) f = 0.f;
           }
           x[t][j] = f;
         }
@@ -645,6 +658,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     uint16_t Qt[2][DH * VT_PITCH];
     uint16_t Dt[2][DH * VT_PITCH];
     uint32_t Fx[4][32 * 16 * 2];  // per group: 2 x 16 x 32 lanes
+    int64_t Tq[2][KV_BQ];         // query timestamps of the stage
   };
   __shared__ __attribute__((aligned(16))) union {
     Smem m;
@@ -655,6 +669,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   auto& Qt = sm.m.Qt;
   auto& Dt = sm.m.Dt;
   auto& Fx = sm.m.Fx;
+  auto& Tq = sm.m.Tq;
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
@@ -709,9 +724,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
 
   VtLoad<DH> ld;  // producers load Q quads, consumers dO quads
+  int64_t rt = 0;
   auto gload = [&](int q0) {
     if (producer) vt_gload<DH>(ld, Q, ldqkv, q0, qhi, hc, ltid);
     else vt_gload<DH>(ld, dO, lddo, q0, qhi, hc, ltid);
+    if (!full && wave == 0) rt = q0 + lane < qhi ? ts[q0 + lane] : 0;
   };
   auto swrite = [&](int buf) {
     if (producer) {
@@ -721,6 +738,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
       quad_swrite_rows<DH>(Ds[buf], ld);
       vt_swrite<DH>(Dt[buf], ld);
     }
+    if (!full && wave == 0) Tq[buf][lane] = rt;
   };
   const int nqt = (qhi - qlo + KV_BQ - 1) / KV_BQ;
   if (nqt > 0) {
@@ -754,14 +772,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
           float pv = sr * sg;                          // SiLU(alpha s) / alpha
           float f = silu_grad_from(alpha * sr, sg);    // SiLU'(alpha s)
           if (!full) {
-            const int qi = q0 + t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-            bool vis = qi < qhi && kv;
-            if (vis) {
-              if (kj < s_end) vis = true;
-              else if (kj < r_end) vis = qi >= s_end && (tk < ts[qi] || kj == qi);
-              else vis = kj == qi;
-            }
-            if (!vis) { pv = 0.f; f = 0.f; }
+            const int qq = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+            if (!visible_ts(q0 + qq, kj, s_end, r_end, Tq[buf][qq], tk)) { pv = 0.f; f = 0.f; }
           }
           p[t][j] = pv;
           x[t][j] = f;
