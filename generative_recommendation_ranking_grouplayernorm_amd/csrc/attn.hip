@@ -465,6 +465,69 @@ __device__ __forceinline__ void quad_swrite_rows(uint16_t* s, const VtLoad<DH>& 
 }
 
 // ---------------------------------------------------------------------------
+// Elementwise SiLU terms of a 64 x 32 score tile (two 32 x 32 accumulators),
+// with or without the mask test.  Kept as straight-line code per variant so
+// that the exp / rcp chains of the 32 elements interleave.
+// ---------------------------------------------------------------------------
+// Transposed tile (rows = keys kk of the tile at k0, lane = query qi):
+// f = M * SiLU'(alpha s) goes to the exchange buffer fx as f16 pairs.
+template <bool MASKED>
+__device__ __forceinline__ void silu_grad_rows_keys(const f32x16_t (&x)[2], uint32_t* fx, int lane, float kexp,
+                                                    float alpha, int qi, int k0, int g, int s_end, int r_end,
+                                                    int64_t tq, const int64_t* tsk) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float f[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = 2 * e + h;
+        const float sr = x[t][j];
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
+        f[h] = silu_grad_from(alpha * sr, sg);
+        if (MASKED) {
+          const int kk = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          f[h] = visible_ts(qi, k0 + kk, s_end, r_end, tq, tsk[kk]) ? f[h] : 0.f;
+        }
+      }
+      fx[(t * 8 + e) * 64 + lane] = pack2<f16_t>(f[0], f[1]);
+    }
+}
+
+// Tile with rows = queries qq of the stage at q0, lane = key kj:
+// P = SiLU(alpha s) / alpha packed as the A operands w of P^T dO, and
+// f = M * SiLU'(alpha s) to the exchange buffer fx as f16 pairs.
+template <typename T, bool MASKED>
+__device__ __forceinline__ void silu_terms_rows_queries(const f32x16_t (&x)[2], op8 (&w)[4], uint32_t* fx, int lane,
+                                                        float kexp, float alpha, int q0, int kj, int g, int s_end,
+                                                        int r_end, const int64_t* tsq, int64_t tk) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float pv[2], f[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = 2 * e + h;
+        const float sr = x[t][j];
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
+        pv[h] = sr * sg;
+        f[h] = silu_grad_from(alpha * sr, sg);
+        if (MASKED) {
+          const int qq = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          const bool vis = visible_ts(q0 + qq, kj, s_end, r_end, tsq[qq], tk);
+          pv[h] = vis ? pv[h] : 0.f;
+          f[h] = vis ? f[h] : 0.f;
+        }
+      }
+      // element pair (2e, 2e+1) of subtile t is dword e % 4 of k-step 2t + e / 4
+      w[2 * t + (e >> 2)].v[e & 3] = pack2<T>(pv[0], pv[1]);
+      fx[(t * 8 + e) * 64 + lane] = pack2<f16_t>(f[0], f[1]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // backward, query-major: dQ = alpha * c * sum_j [M SiLU'(S) (dO v_j)] k_j
 // for 128 queries (4 waves x 32), 64 keys per LDS stage.
 // ---------------------------------------------------------------------------
@@ -572,24 +635,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
 #pragma unroll
       for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<KP>(A, t * 32, s, lane), bop[s], x[t]);
     if (producer) {
-      const bool masked = it >= nfull;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float sr = x[t][j];
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
-          float f = silu_grad_from(alpha * sr, sg);
-          if (masked) {
-            const int kk = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-            if (!visible_ts(qi, k0 + kk, s_end, r_end, tq, Tk[buf][kk])) f = 0.f;
-          }
-          x[t][j] = f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          fx[(t * 8 + e) * 64 + lane] = pack2<f16_t>(x[t][2 * e], x[t][2 * e + 1]);
-      }
+      if (it >= nfull)
+        silu_grad_rows_keys<true>(x, fx, lane, kexp, alpha, qi, k0, g, s_end, r_end, tq, Tk[buf]);
+      else
+        silu_grad_rows_keys<false>(x, fx, lane, kexp, alpha, qi, k0, g, s_end, r_end, tq, Tk[buf]);
     }
     __syncthreads();  // f of this tile visible to the consumers
     op8 da[4];
@@ -762,28 +811,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
       for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<QP>(A, t * 32, s, lane), bop[s], x[t]);
     op8 w[4];
     if (producer) {
-      float p[2][16];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float sr = x[t][j];
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
-          float pv = sr * sg;                          // SiLU(alpha s) / alpha
-          float f = silu_grad_from(alpha * sr, sg);    // SiLU'(alpha s)
-          if (!full) {
-            const int qq = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-            if (!visible_ts(q0 + qq, kj, s_end, r_end, Tq[buf][qq], tk)) { pv = 0.f; f = 0.f; }
-          }
-          p[t][j] = pv;
-          x[t][j] = f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          fx[(t * 8 + e) * 64 + lane] = pack2<f16_t>(x[t][2 * e], x[t][2 * e + 1]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = pack_kstep<T>(p, u);
+      if (full)
+        silu_terms_rows_queries<T, false>(x, w, fx, lane, kexp, alpha, q0, kj, g, s_end, r_end, Tq[buf], tk);
+      else
+        silu_terms_rows_queries<T, true>(x, w, fx, lane, kexp, alpha, q0, kj, g, s_end, r_end, Tq[buf], tk);
     }
     __syncthreads();  // f of this stage visible to the consumers
     if (!producer) {
