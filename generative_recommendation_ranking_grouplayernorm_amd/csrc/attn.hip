@@ -485,7 +485,8 @@ __device__ __forceinline__ void silu_grad_rows_keys(const f32x16_t (&x)[2], uint
         const int j = 2 * e + h;
         const float sr = x[t][j];
         const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
-        f[h] = silu_grad_from(alpha * sr, sg);
+        // SiLU'(y) = sigma + y sigma (1 - sigma), y = alpha s
+        f[h] = __builtin_fmaf(alpha * (sr * sg), 1.0f - sg, sg);
         if (MASKED) {
           const int kk = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
           f[h] = visible_ts(qi, k0 + kk, s_end, r_end, tq, tsk[kk]) ? f[h] : 0.f;
@@ -513,7 +514,8 @@ __device__ __forceinline__ void silu_terms_rows_queries(const f32x16_t (&x)[2], 
         const float sr = x[t][j];
         const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
         pv[h] = sr * sg;
-        f[h] = silu_grad_from(alpha * sr, sg);
+        // SiLU'(y) = sigma + y sigma (1 - sigma), y = alpha s
+        f[h] = __builtin_fmaf(alpha * pv[h], 1.0f - sg, sg);
         if (MASKED) {
           const int qq = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
           const bool vis = visible_ts(q0 + qq, kj, s_end, r_end, tsq[qq], tk);
@@ -649,8 +651,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t fv = fx[(t * 8 + e) * 64 + lane];
-          d[t][2 * e] = x[t][2 * e] * from_bits16<f16_t>((uint16_t)(fv & 0xffff));
-          d[t][2 * e + 1] = x[t][2 * e + 1] * from_bits16<f16_t>((uint16_t)(fv >> 16));
+          d[t][2 * e] = __builtin_fmaf(x[t][2 * e], from_bits16<f16_t>((uint16_t)(fv & 0xffff)), 0.0f);
+          d[t][2 * e + 1] = __builtin_fmaf(x[t][2 * e + 1], from_bits16<f16_t>((uint16_t)(fv >> 16)), 0.0f);
         }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -824,8 +826,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t fv = fx[(t * 8 + e) * 64 + lane];
-          d[t][2 * e] = x[t][2 * e] * from_bits16<f16_t>((uint16_t)(fv & 0xffff));
-          d[t][2 * e + 1] = x[t][2 * e + 1] * from_bits16<f16_t>((uint16_t)(fv >> 16));
+          d[t][2 * e] = __builtin_fmaf(x[t][2 * e], from_bits16<f16_t>((uint16_t)(fv & 0xffff)), 0.0f);
+          d[t][2 * e + 1] = __builtin_fmaf(x[t][2 * e + 1], from_bits16<f16_t>((uint16_t)(fv >> 16)), 0.0f);
         }
 #pragma unroll
       for (int u = 0; u < 4; ++u) w[u] = pack_kstep<T>(d, u);
