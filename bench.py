@@ -39,6 +39,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle baseline sample (0 disables it)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, copy MIB MiB device-to-device 3 times (a plain copy kernel "
+                         "of known size, the calibration for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="offline: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --copy-probe N' into profiles/traffic.json and a markdown table")
+    ap.add_argument("--stats-summary", metavar="STATS_CSV",
+                    help="offline: turn a rocprofv3 --stats kernel_stats.csv into a markdown table on stdout")
+    ap.add_argument("--probe-mib", type=int, default=256, help="copy size used by --pmc-summary")
     return ap.parse_args()
 
 
@@ -55,14 +64,15 @@ def profile_summary(lib):
     return {names[i].decode(): (ms[i], cnt[i]) for i in range(min(k, n))}
 
 
-def kernel_work(T, d, P):
+def kernel_work(T, d, P, ds_bytes):
     """Algorithmic work of one launch of each kernel step: (bound, amount)
-    with flops for MFMA-bound steps and HBM bytes for row sweeps."""
+    with flops for MFMA-bound steps and HBM bytes for streaming ones."""
     e = 2  # bf16 bytes
     return {
         "attn_fwd": ("mfma", 4 * d * P),
         "attn_bwd_dkdv": ("mfma", 6 * d * P),   # dV, dA = dO V^T, dK
-        "attn_bwd_dq": ("mfma", 2 * d * P),     # dQ
+        # dQ = dS K from stored dS: streams dS, reads K and the Q pre-activation, writes dQ
+        "attn_bwd_dq": ("hbm", ds_bytes + 3 * T * d * e),
         "gemm_uqkv_silu": ("mfma", 8 * T * d * d),
         "gemm_out_resid": ("mfma", 2 * T * d * d),
         "gemm_dy": ("mfma", 2 * T * d * d),
@@ -74,6 +84,112 @@ def kernel_work(T, d, P):
         "gln2_gate_bwd": ("hbm", T * (6 * e * d + 9)),
         "gln1_bwd": ("hbm", T * (4 * e * d + 9)),
     }
+
+
+# HIP kernel name fragments -> kernel step names used in the JSON line
+KERNEL_STEPS = [
+    ("attn_bwd_dkdv_mfma", "attn_bwd_dkdv"),
+    ("attn_bwd_dq_stream", "attn_bwd_dq"),
+    ("attn_fwd_mfma", "attn_fwd"),
+]
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{kernel name: [value per dispatch]} for one counter (summed over the
+    dimensions rocprofv3 reports it in)."""
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in acc.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def attn_source_hash():
+    """Hash of the attention kernels' source: counters taken on other code are stale."""
+    import hashlib
+
+    path = os.path.join(ROOT, "generative_recommendation_ranking_grouplayernorm_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def pmc_summary(fetch_dir, write_dir, probe_mib):
+    """Per-launch HBM traffic of the attention kernels from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the ratio of the bytes a
+    plain device copy of probe_mib MiB moves to what the same counter reads
+    for it."""
+    fetch = _per_dispatch(_pmc_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch(_pmc_rows(write_dir), "WRITE_SIZE")
+    nbytes = probe_mib * 1024 * 1024
+
+    def copy_kib(tab):
+        # the probe's dispatches: copy-kernel launches that move at least half the probe size
+        # (the same kernel also serves the small copies of the timed steps)
+        cands = {k: [x for x in v if x * 1024 > 0.5 * nbytes] for k, v in tab.items() if "copy" in k.lower()}
+        cands = {k: v for k, v in cands.items() if v}
+        if not cands:
+            raise SystemExit("copy probe kernel not found in the counter runs")
+        k = max(cands, key=lambda n: len(cands[n]))
+        vals = sorted(cands[k])
+        return k, vals[len(vals) // 2]
+
+    ck, cf = copy_kib(fetch)
+    _, cw = copy_kib(write)
+    f_scale = nbytes / (cf * 1024)
+    w_scale = nbytes / (cw * 1024)
+    res = {"_calibration": {"copy_kernel": ck, "copy_bytes": nbytes, "fetch_kib": cf, "write_kib": cw,
+                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+           "_source_sha256": attn_source_hash()}
+    lines = ["| kernel step | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |",
+             "|---|---|---|---|---|"]
+    for frag, step in KERNEL_STEPS:
+        fk = [k for k in fetch if frag in k]
+        wk = [k for k in write if frag in k]
+        if not fk or not wk:
+            continue
+        fv = [v for k in fk for v in fetch[k]]
+        wv = [v for k in wk for v in write[k]]
+        f_avg, w_avg = sum(fv) / len(fv), sum(wv) / len(wv)
+        tot = f_avg * 1024 * f_scale + w_avg * 1024 * w_scale
+        res[step] = round(tot)
+        lines.append(f"| {step} | {len(fv)} | {f_avg:.0f} | {w_avg:.0f} | {tot / 1e9:.3f} GB |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    print("\n".join(lines))
+    print(f"\ncalibration: {ck} moving {nbytes} B reads FETCH_SIZE {cf:.0f} KiB (scale {f_scale:.4f}), "
+          f"WRITE_SIZE {cw:.0f} KiB (scale {w_scale:.4f})")
+
+
+def stats_summary(path):
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    print("| kernel | calls | total us | avg us | % |")
+    print("|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        name = name if len(name) <= 110 else name[:107] + "..."
+        print(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+              f"{float(r['AverageNs']) / 1e3:.1f} | {100 * float(r['TotalDurationNs']) / tot:.1f} |")
 
 
 def cpu_baseline(batch, params, x, R, budget_s):
@@ -130,6 +246,12 @@ def cpu_baseline(batch, params, x, R, budget_s):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.probe_mib)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is a "
               f"design note, not part of this build.", file=sys.stderr)
@@ -195,6 +317,15 @@ def main():
     prof = profile_summary(lib)
     lib.mtgr_profile_enable(0)
     ms_step = ms_total / args.steps
+    if args.copy_probe > 0:
+        n = args.copy_probe * 1024 * 1024 // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: 3 x {args.copy_probe} MiB device-to-device", file=sys.stderr, flush=True)
+        del src, dst
 
     P = fl.visible_pairs(batch.offsets, batch.group_ids, batch.timestamps)
     attn_flops = 12 * d * P
@@ -202,7 +333,7 @@ def main():
     value = attn_flops / (attn_ms / 1e3) / 1e12
     layer_flops = 12 * d * P + fl.layer_gemm_flops(T, d, backward=True)
 
-    work = kernel_work(T, d, P)
+    work = kernel_work(T, d, P, fl.ds_stream_bytes(batch.offsets, batch.group_ids, H))
     kernels = {}
     for name, (tot, n) in prof.items():
         avg = tot / max(n, 1)
@@ -222,7 +353,9 @@ def main():
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         try:
-            traffic = json.load(open(tpath)).get(dom)
+            tj = json.load(open(tpath))
+            # counters describe the kernels they were taken on
+            traffic = tj.get(dom) if tj.get("_source_sha256") == attn_source_hash() else None
         except Exception:
             traffic = None
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],

@@ -40,3 +40,30 @@ def layer_gemm_flops(T: int, d: int, backward: bool) -> int:
     """UQKV (8 T d^2) and output (2 T d^2) projections; backward doubles each."""
     f = 10 * T * d * d
     return 3 * f if backward else f
+
+
+def ds_stream_bytes(offsets, group_ids, heads: int) -> int:
+    """Bytes of stored 16-bit score gradients the dQ pass streams: per
+    128-query tile it visits 64-key steps over the keys its queries can see
+    (static and real-time key tiles, plus the candidate tile on the
+    diagonal), 16 KB per step and head."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    g = np.asarray(group_ids)
+    steps = 0
+    for b in range(offsets.shape[0] - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi <= lo:
+            continue
+        gb = g[lo:hi]
+        s_end = lo + int(np.count_nonzero(gb <= 1))
+        r_end = s_end + int(np.count_nonzero(gb == 2))
+        n_nc = (r_end - lo + 127) // 128
+        for q0 in range(lo, hi, 128):
+            qt = (q0 - lo) // 128
+            q_last = min(q0 + 128, hi) - 1
+            kv_end = s_end if q_last < s_end else (r_end if q_last < r_end else q_last + 1)
+            end_a = min(kv_end, lo + 128 * n_nc)
+            na = (end_a - lo + 63) // 64 if end_a > lo else 0
+            nb = (kv_end - q0 + 63) // 64 if qt >= n_nc else 0
+            steps += na + nb
+    return steps * 16384 * heads
