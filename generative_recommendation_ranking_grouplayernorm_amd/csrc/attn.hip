@@ -126,6 +126,20 @@ __device__ __forceinline__ op8 pack_kstep(const float (&v)[2][16], int u) {
   return o;
 }
 
+// Scheduling hint for a run of N MFMAs each fed by one LDS read: keep AHEAD
+// reads in flight ahead of the MFMA that consumes them, so that a wave does
+// not stall on LDS latency before every MFMA.  Only orders instructions.
+template <int N, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // ---------------------------------------------------------------------------
 // workgroup -> (tile, head), XCD-aware
 // ---------------------------------------------------------------------------
@@ -340,6 +354,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt,
   for (int s = 1; s < DH / 16; ++s)
 #pragma unroll
     for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(row_operand<KP>(Ks, t * 32, s, lane), qop[s], sacc[t]);
+  pipeline_lds_mfma<DH / 8, 8>();
   float p[2][16];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -359,6 +374,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt,
 #pragma unroll
     for (int c = 0; c < DH / 32; ++c) oacc[c] = mfma32<T>(pa, vt_operand(Vt, u, c * 32, lane), oacc[c]);
   }
+  pipeline_lds_mfma<DH / 8, 8>();
 }
 
 template <typename T, int DH>
@@ -811,6 +827,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     for (int s = 1; s < NS; ++s)
 #pragma unroll
       for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<QP>(A, t * 32, s, lane), bop[s], x[t]);
+    pipeline_lds_mfma<2 * NS, 8>();
     op8 w[4];
     if (producer) {
       if (full)
@@ -844,6 +861,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], vt_operand(Bt, u, c * 32, lane), acc[c]);
+    pipeline_lds_mfma<4 * NC, 8>();
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
