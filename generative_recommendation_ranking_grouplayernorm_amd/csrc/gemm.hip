@@ -146,6 +146,25 @@ __device__ __forceinline__ op8 gemm_operand(const uint16_t* s, int r0, int ks, i
   return o;
 }
 
+// Scheduling hint for one K step (four 16-deep slices, eight MFMAs each, R
+// LDS reads feeding each slice): the reads of slice s + 1 are spread between
+// the MFMAs of slice s, so that operands arrive before they are needed.
+template <int R, int I>
+__device__ __forceinline__ void gemm_pipeline_slot() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA I of the slice
+  constexpr int n = (R * (I + 1)) / 8 - (R * I) / 8;
+  if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // DS reads
+  if constexpr (I + 1 < 8) gemm_pipeline_slot<R, I + 1>();
+}
+template <int R>
+__device__ __forceinline__ void gemm_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // DS reads of slice 0
+  gemm_pipeline_slot<R, 0>();
+  gemm_pipeline_slot<R, 0>();
+  gemm_pipeline_slot<R, 0>();
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+}
+
 // Workgroup L -> (row job, N tile).  Workgroups run round-robin on the 8
 // XCDs; every N tile of one row job goes to the same XCD so that the A rows
 // are fetched once into that XCD's L2.
@@ -227,6 +246,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(const uint16_t* __res
 #pragma unroll
         for (int u = 0; u < 2; ++u) acc[t][u] = mfma32<T>(a[t], b[u], acc[t][u]);
     }
+    gemm_pipeline<4 * (AK ? 1 : 2) + 2 * (BKC ? 1 : 2)>();
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
