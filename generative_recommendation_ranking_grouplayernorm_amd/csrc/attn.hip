@@ -323,7 +323,7 @@ __device__ __forceinline__ void wave_store_rows(float* stage, const f32x16_t (&a
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float zf = from_bits16<T>((uint16_t)(zw[e >> 1] >> (16 * (e & 1))));
-          v[e] *= silu_grad_from(zf, 1.0f / (1.0f + __expf(-zf)));
+          v[e] *= silu_grad_from(zf, __builtin_amdgcn_rcpf(1.0f + __expf(-zf)));
         }
       }
       u32x4_t o;

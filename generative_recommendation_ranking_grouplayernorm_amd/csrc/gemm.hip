@@ -15,6 +15,8 @@
 namespace mtgr {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// 16-bit outputs: the hardware reciprocal (1 ulp) is far below the output rounding
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Staged epilogue of 8 consecutive outputs (m, n..n+7), N % 8 == 0.
 constexpr int G_EPI_PITCH = 72;  // floats per staged row
@@ -57,7 +59,7 @@ __device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, fl
     for (int e = 0; e < 8; ++e) z[e] = to_f32(from_f32<T>(v[e]));
     if (ep.Z) store8_t<T>((T*)ep.Z + (int64_t)m * ep.ldz + n, z);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = silu_f(z[e]);
+    for (int e = 0; e < 8; ++e) z[e] = silu_fast(z[e]);
     store8_t<T>((T*)ep.C + (int64_t)m * ep.ldc + n, z);
   } else if (EPI == EPI_BIAS_RESID) {
     float r[8];

@@ -167,6 +167,13 @@ __device__ __forceinline__ float silu_grad_f(float z) {
   float s = 1.0f / (1.0f + __expf(-z));
   return s * (1.0f + z * (1.0f - s));
 }
+// 16-bit storage: the hardware reciprocal (1 ulp) is far below the output rounding
+template <typename T>
+__device__ __forceinline__ float silu_grad_t(float z) {
+  if constexpr (sizeof(T) == 4) return silu_grad_f(z);
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+  return s * (1.0f + z * (1.0f - s));
+}
 
 // Per block: partial[blockIdx.x][0][G][d] = dgamma part, [1][G][d] = dbeta part.
 // Each wave walks 16 consecutive rows; the group rarely changes along them,
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
             float zz[8];
             load8(zu + row * ldzu + c, zz);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) duv[k] *= silu_grad_f(zz[k]);
+            for (int k = 0; k < 8; ++k) duv[k] *= silu_grad_t<T>(zz[k]);
           }
           store8(du + row * lddu + c, duv);
 #pragma unroll
