@@ -27,132 +27,105 @@ __global__ void seg_kernel(const int32_t* __restrict__ offsets, const uint8_t* _
   seg[b * 5 + 4] = hi;
 }
 
-// One workgroup: exclusive scan of per-user tile counts, then every user
-// writes (user, first row) of each of its ROWS_PER_TILE-row tiles.  The
-// list is ordered by descending user length so that the longest rows start
-// first (a longest-processing-time-first schedule across the workgroups).
-__global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restrict__ offsets, int B,
-                                                         int rows_per_tile,
-                                                         int32_t* __restrict__ order_scratch,
-                                                         int2* __restrict__ tiles,
-                                                         int32_t* __restrict__ ntiles) {
-  __shared__ int warp_sums[16];
-  __shared__ int carry;
-  const int tid = threadIdx.x;
-  // Counting sort of users by tile count, descending.  Tile counts are
-  // bounded by the longest row / rows_per_tile; bucket at that granularity.
+// Everything the attention launches need, in one workgroup: segments of
+// every user, the 128-row tile list (longest users first) and the
+// exclusive prefix of n_t^2.  Per-user values are recomputed where needed
+// rather than kept, so any B works with fixed shared memory.
+static_assert(ATTN_QTILE == 128 && ATTN_KTILE == 128, "query and key tile lists are one list");
+
+__global__ __launch_bounds__(1024) void prep_all_kernel(const int32_t* __restrict__ offsets,
+                                                        const uint8_t* __restrict__ g, int B,
+                                                        int32_t* __restrict__ seg,
+                                                        int32_t* __restrict__ order_scratch,
+                                                        int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
+                                                        int64_t* __restrict__ tprefix) {
   __shared__ int hist[1024];
-  for (int i = tid; i < 1024; i += blockDim.x) hist[i] = 0;
+  __shared__ int warp_i[16];
+  __shared__ long long warp_l[16];
+  __shared__ int carry_i;
+  __shared__ long long carry_l;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // segments and the histogram of tile counts
+  for (int i = tid; i < 1024; i += 1024) hist[i] = 0;
   __syncthreads();
-  for (int b = tid; b < B; b += blockDim.x) {
-    int n = offsets[b + 1] - offsets[b];
-    int c = (n + rows_per_tile - 1) / rows_per_tile;
+  for (int b = tid; b < B; b += 1024) {
+    const int lo = offsets[b], hi = offsets[b + 1];
+    seg[b * 5 + 0] = lo;
+    seg[b * 5 + 1] = lower_bound_u8(g, lo, hi, 1);
+    seg[b * 5 + 2] = lower_bound_u8(g, lo, hi, 2);
+    seg[b * 5 + 3] = lower_bound_u8(g, lo, hi, 3);
+    seg[b * 5 + 4] = hi;
+    const int c = (hi - lo + 127) / 128;
     atomicAdd(&hist[min(c, 1023)], 1);
   }
   __syncthreads();
   if (tid == 0) {
-    // exclusive prefix over buckets from the largest count down
-    int run = 0;
+    int run = 0;  // exclusive prefix over buckets from the largest count down
     for (int c = 1023; c >= 0; --c) {
-      int h = hist[c];
+      const int h = hist[c];
       hist[c] = run;
       run += h;
     }
+    carry_i = 0;
+    carry_l = 0;
   }
   __syncthreads();
-  // Stable placement is not needed: any order inside a bucket is fine.
-  for (int b = tid; b < B; b += blockDim.x) {
-    int n = offsets[b + 1] - offsets[b];
-    int c = min((n + rows_per_tile - 1) / rows_per_tile, 1023);
-    int pos = atomicAdd(&hist[c], 1);
-    order_scratch[pos] = b;
+  for (int b = tid; b < B; b += 1024) {
+    const int c = min((offsets[b + 1] - offsets[b] + 127) / 128, 1023);
+    order_scratch[atomicAdd(&hist[c], 1)] = b;
   }
   __syncthreads();
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += blockDim.x) {
-    int i = base + tid;
-    int b = i < B ? order_scratch[i] : 0;
-    int cnt = 0;
-    if (i < B) {
-      int n = offsets[b + 1] - offsets[b];
-      cnt = (n + rows_per_tile - 1) / rows_per_tile;
-    }
-    // block-wide inclusive scan of cnt
-    int v = cnt;
-    const int lane = tid & 63, w = tid >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      int t = __shfl_up(v, off, 64);
-      if (lane >= off) v += t;
-    }
-    if (lane == 63) warp_sums[w] = v;
-    __syncthreads();
-    if (tid < 64) {
-      int s = tid < (int)(blockDim.x >> 6) ? warp_sums[tid] : 0;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        int t = __shfl_up(s, off, 64);
-        if (tid >= off) s += t;
-      }
-      if (tid < 16) warp_sums[tid] = s;
-    }
-    __syncthreads();
-    int excl = carry + (w > 0 ? warp_sums[w - 1] : 0) + v - cnt;
-    if (i < B) {
-      int lo = offsets[b];
-      for (int t = 0; t < cnt; ++t) tiles[excl + t] = make_int2(b, lo + t * rows_per_tile);
-    }
-    __syncthreads();
-    if (tid == blockDim.x - 1) carry = excl + cnt;
-    __syncthreads();
-  }
-  if (tid == 0) *ntiles = carry;
-}
-
-// One workgroup: exclusive prefix over users (in user order) of n_t^2,
-// n_t = ceil(L / 128); out[B] is the total.  n_t^2 is the number of
-// 128 x 128 (query, key) tile pairs a user's backward keeps dS for, so the
-// prefix places each user's dS tiles in one packed buffer.
-__global__ __launch_bounds__(1024) void tile_square_prefix_kernel(const int32_t* __restrict__ offsets, int B,
-                                                                  int64_t* __restrict__ out) {
-  __shared__ long long warp_sums[16];
-  __shared__ long long carry;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid == 0) carry = 0;
-  __syncthreads();
+  // tile list in sorted order and the n_t^2 prefix in user order, one
+  // 1024-user chunk at a time
   for (int base = 0; base < B; base += 1024) {
-    const int b = base + tid;
-    long long v0 = 0;
-    if (b < B) {
-      const long long nt = (offsets[b + 1] - offsets[b] + 127) / 128;
-      v0 = nt * nt;
+    const int i = base + tid;
+    const int bs = i < B ? order_scratch[i] : 0;
+    const int cnt = i < B ? (offsets[bs + 1] - offsets[bs] + 127) / 128 : 0;
+    long long sq = 0;
+    if (i < B) {
+      const long long nt = (offsets[i + 1] - offsets[i] + 127) / 128;
+      sq = nt * nt;
     }
-    long long v = v0;
+    int v = cnt;
+    long long vl = sq;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const long long t = __shfl_up(v, off, 64);
-      if (lane >= off) v += t;
+      const int t = __shfl_up(v, off, 64);
+      const long long tl = __shfl_up(vl, off, 64);
+      if (lane >= off) { v += t; vl += tl; }
     }
-    if (lane == 63) warp_sums[w] = v;
+    if (lane == 63) { warp_i[w] = v; warp_l[w] = vl; }
     __syncthreads();
     if (tid < 64) {
-      long long s = tid < 16 ? warp_sums[tid] : 0;
+      int si = tid < 16 ? warp_i[tid] : 0;
+      long long sl = tid < 16 ? warp_l[tid] : 0;
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) {
-        const long long t = __shfl_up(s, off, 64);
-        if (tid >= off) s += t;
+        const int t = __shfl_up(si, off, 64);
+        const long long tl = __shfl_up(sl, off, 64);
+        if (tid >= off) { si += t; sl += tl; }
       }
-      if (tid < 16) warp_sums[tid] = s;
+      if (tid < 16) { warp_i[tid] = si; warp_l[tid] = sl; }
     }
     __syncthreads();
-    const long long excl = carry + (w > 0 ? warp_sums[w - 1] : 0) + v - v0;
-    if (b < B) out[b] = excl;
+    const int excl = carry_i + (w > 0 ? warp_i[w - 1] : 0) + v - cnt;
+    const long long exl = carry_l + (w > 0 ? warp_l[w - 1] : 0) + vl - sq;
+    if (i < B) {
+      const int lo = offsets[bs];
+      for (int t = 0; t < cnt; ++t) tiles[excl + t] = make_int2(bs, lo + t * 128);
+      tprefix[i] = exl;
+    }
     __syncthreads();
-    if (tid == 1023) carry = excl + v0;
+    if (tid == 1023) {
+      carry_i = excl + cnt;
+      carry_l = exl + sq;
+    }
     __syncthreads();
   }
-  if (tid == 0) out[B] = carry;
+  if (tid == 0) {
+    *ntiles = carry_i;
+    tprefix[B] = carry_l;
+  }
 }
 
 int64_t max_tiles(int B, int64_t T, int rows_per_tile) {
@@ -187,18 +160,11 @@ int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t
   out->k.max_tiles = max_tiles(B, T, ATTN_KTILE);
   p += align_up((size_t)out->k.max_tiles * sizeof(int2), 256);
   out->tprefix = (int64_t*)p;
-  if (B > 0) {
-    hipLaunchKernelGGL(seg_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, offsets, group_ids, B,
-                       out->seg);
-    MTGR_LAUNCH_CHECK();
-  }
-  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, ATTN_QTILE, order,
-                     out->q.tiles, out->q.ntiles);
-  MTGR_LAUNCH_CHECK();
-  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, ATTN_KTILE, order,
-                     out->k.tiles, out->k.ntiles);
-  MTGR_LAUNCH_CHECK();
-  hipLaunchKernelGGL(tile_square_prefix_kernel, dim3(1), dim3(1024), 0, stream, offsets, B, out->tprefix);
+  // query and key tiles are both 128 rows: one list serves both
+  out->k.tiles = out->q.tiles;
+  out->k.ntiles = out->q.ntiles;
+  hipLaunchKernelGGL(prep_all_kernel, dim3(1), dim3(1024), 0, stream, offsets, group_ids, B, out->seg, order,
+                     out->q.tiles, out->q.ntiles, out->tprefix);
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
 }
