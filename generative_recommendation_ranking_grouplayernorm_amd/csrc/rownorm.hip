@@ -161,7 +161,12 @@ int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, con
 }
 
 // ---- backward ---------------------------------------------------------------
-constexpr int GLN_BWD_ROWS_PER_BLOCK = 64;  // 16 consecutive rows per wave
+// The grid is sized to the blocks the GPU holds at once (one round, no tail),
+// each block taking an equal share of the rows, 4 waves x consecutive rows.
+// Partial gamma/beta sums: one [2][G][d] slice per block, at most
+// GLN_BWD_MAX_BLOCKS blocks (and never fewer than 16 rows per block).
+constexpr int GLN_BWD_MAX_BLOCKS = 2048;
+constexpr int GLN_BWD_MIN_ROWS = 16;
 
 __device__ __forceinline__ float silu_grad_f(float z) {
   float s = 1.0f / (1.0f + __expf(-z));
@@ -185,14 +190,17 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
     const float* __restrict__ mean, const float* __restrict__ rstd, const T* __restrict__ gamma,
     const T* __restrict__ beta, const uint8_t* __restrict__ g, int64_t nrows, int d, int G, T* dx,
     int64_t lddx, const T* __restrict__ resid, int64_t ldr, const T* __restrict__ u, int64_t ldu,
-    T* du, int64_t lddu, const T* __restrict__ zu, int64_t ldzu, float* __restrict__ partial) {
+    T* du, int64_t lddu, const T* __restrict__ zu, int64_t ldzu, float* __restrict__ partial,
+    int64_t rows_per_block) {
   extern __shared__ float acc[];  // [2][G][d]
   const int Gd = G * d;
   for (int i = threadIdx.x; i < 2 * Gd; i += blockDim.x) acc[i] = 0.f;
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  constexpr int RPW = GLN_BWD_ROWS_PER_BLOCK / 4;
-  const int64_t r0 = (int64_t)blockIdx.x * GLN_BWD_ROWS_PER_BLOCK + (int64_t)w * RPW;
+  const int64_t RPW = (rows_per_block + 3) / 4;
+  const int64_t blk_end = min((int64_t)(blockIdx.x + 1) * rows_per_block, nrows);
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block + (int64_t)w * RPW;
+  const int64_t r1 = min(r0 + RPW, blk_end);
   const float inv_d = 1.0f / (float)d;
   float ag[NCH][8], ab[NCH][8];
 #pragma unroll
@@ -214,9 +222,7 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
       }
     }
   };
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int64_t row = r0 + rr;
-    if (row >= nrows) break;
+  for (int64_t row = r0; row < r1; ++row) {
     const int grp = g[row];
     if (grp != cur) {
       if (cur >= 0) flush();
@@ -313,9 +319,26 @@ __global__ __launch_bounds__(1024) void reduce_partials_kernel(const float* __re
   }
 }
 
+static int64_t gln_bwd_block_bound(int64_t T_) {
+  const int64_t b = (T_ + GLN_BWD_MIN_ROWS - 1) / GLN_BWD_MIN_ROWS;
+  return b < 1 ? 1 : (b > GLN_BWD_MAX_BLOCKS ? GLN_BWD_MAX_BLOCKS : b);
+}
+
 size_t gln_bwd_workspace_bytes(int64_t T_, int d, int G) {
-  const int64_t nblk = (T_ + GLN_BWD_ROWS_PER_BLOCK - 1) / GLN_BWD_ROWS_PER_BLOCK;
-  return align_up((size_t)(nblk > 0 ? nblk : 1) * 2 * G * d * sizeof(float), 256);
+  return align_up((size_t)gln_bwd_block_bound(T_) * 2 * G * d * sizeof(float), 256);
+}
+
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <typename T, bool GATE>
@@ -323,13 +346,24 @@ static int gln_bwd_dispatch(const void* dy, int64_t lddy, const void* x, int64_t
                             const float* rstd, const void* gamma, const void* beta, const uint8_t* g,
                             int64_t T_, int d, int G, void* dx, int64_t lddx, const void* resid,
                             int64_t ldr, const void* u, int64_t ldu, void* du, int64_t lddu,
-                            const void* zu, int64_t ldzu, float* partial, hipStream_t st) {
-  const int64_t nblk = (T_ + GLN_BWD_ROWS_PER_BLOCK - 1) / GLN_BWD_ROWS_PER_BLOCK;
+                            const void* zu, int64_t ldzu, float* partial, int* nparts, hipStream_t st) {
   const size_t lds = (size_t)2 * G * d * sizeof(float);
   const int nch = (d + 511) / 512;
+  const void* fn = nch <= 1 ? (const void*)gln_bwd_kernel<T, 1, GATE>
+                 : nch <= 2 ? (const void*)gln_bwd_kernel<T, 2, GATE>
+                 : nch <= 4 ? (const void*)gln_bwd_kernel<T, 4, GATE>
+                            : (const void*)gln_bwd_kernel<T, 8, GATE>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+  int64_t nblk = (int64_t)per_cu * device_cu_count();
+  const int64_t bound = gln_bwd_block_bound(T_);
+  if (nblk > bound) nblk = bound;
+  const int64_t rpb = (T_ + nblk - 1) / nblk;
+  nblk = (T_ + rpb - 1) / rpb;
+  *nparts = (int)nblk;
 #define GLN_BWD_ARGS                                                                                 \
   (const T*)dy, lddy, (const T*)x, ldx, mean, rstd, (const T*)gamma, (const T*)beta, g, T_, d, G,   \
-      (T*)dx, lddx, (const T*)resid, ldr, (const T*)u, ldu, (T*)du, lddu, (const T*)zu, ldzu, partial
+      (T*)dx, lddx, (const T*)resid, ldr, (const T*)u, ldu, (T*)du, lddu, (const T*)zu, ldzu, partial, rpb
   if (nch <= 1)
     hipLaunchKernelGGL((gln_bwd_kernel<T, 1, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
   else if (nch <= 2)
@@ -358,9 +392,10 @@ int launch_gln_bwd(int dt, const void* dy, int64_t lddy, const void* x, int64_t 
   float* partial = (float*)ws;
   const bool gate = u != nullptr;
   int r = MTGR_ERR_UNSUPPORTED;
+  int nparts = 0;
 #define GLN_BWD_CALL(TT, GG)                                                                         \
   gln_bwd_dispatch<TT, GG>(dy, lddy, x, ldx, mean, rstd, gamma, beta, g, T_, d, G, dx, lddx, resid, \
-                           ldr, u, ldu, du, lddu, zu, ldzu, partial, stream)
+                           ldr, u, ldu, du, lddu, zu, ldzu, partial, &nparts, stream)
   switch (dt) {
     case MTGR_F32: r = gate ? GLN_BWD_CALL(float, true) : GLN_BWD_CALL(float, false); break;
     case MTGR_BF16: r = gate ? GLN_BWD_CALL(bf16_t, true) : GLN_BWD_CALL(bf16_t, false); break;
@@ -368,9 +403,8 @@ int launch_gln_bwd(int dt, const void* dy, int64_t lddy, const void* x, int64_t 
   }
 #undef GLN_BWD_CALL
   if (r) return r;
-  const int nblk = (int)((T_ + GLN_BWD_ROWS_PER_BLOCK - 1) / GLN_BWD_ROWS_PER_BLOCK);
   hipLaunchKernelGGL(reduce_partials_kernel, dim3((2 * Gd + 63) / 64), dim3(1024), 0, stream, partial,
-                     nblk, 2 * Gd, dgamma, dbeta, Gd);
+                     nparts, 2 * Gd, dgamma, dbeta, Gd);
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
 }
