@@ -47,6 +47,30 @@ __device__ __forceinline__ void store8_16(H* p, const float* v) {
 __device__ __forceinline__ void store8(bf16_t* p, const float* v) { store8_16(p, v); }
 __device__ __forceinline__ void store8(f16_t* p, const float* v) { store8_16(p, v); }
 
+// 8 consecutive elements held raw in registers (loaded ahead, converted later).
+template <typename T> struct Chunk8 {
+  uint4 v;
+  __device__ __forceinline__ void load(const T* p) { v = *(const uint4*)p; }
+  __device__ __forceinline__ void get(float* o) const {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = from_bits16<T>((uint16_t)(w[i] & 0xffff));
+      o[2 * i + 1] = from_bits16<T>((uint16_t)(w[i] >> 16));
+    }
+  }
+};
+template <> struct Chunk8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *(const float4*)p;
+    b = *(const float4*)(p + 4);
+  }
+  __device__ __forceinline__ void get(float* o) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+
 // ---- forward ---------------------------------------------------------------
 // NCH = number of 512-column chunks a lane covers (lane owns columns
 // lane*8 + 512*i .. +7).
@@ -184,7 +208,8 @@ __device__ __forceinline__ float silu_grad_t(float z) {
 // Each wave walks 16 consecutive rows; the group rarely changes along them,
 // so the per-group sums stay in registers and are flushed to LDS (atomic
 // adds) only on a change.
-template <typename T, int NCH, bool GATE>
+// EXACT: d == 512 NCH, so every lane owns full chunks (no per-lane tests).
+template <typename T, int NCH, bool GATE, bool EXACT>
 __global__ __launch_bounds__(256) void gln_bwd_kernel(
     const T* __restrict__ dy, int64_t lddy, const T* __restrict__ x, int64_t ldx,
     const float* __restrict__ mean, const float* __restrict__ rstd, const T* __restrict__ gamma,
@@ -212,7 +237,7 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane * 8 + i * 512;
-      if (c < d) {
+      if (EXACT || c < d) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           atomicAdd(&acc[cur * d + c + e], ag[i][e]);
@@ -222,34 +247,68 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
       }
     }
   };
-  for (int64_t row = r0; row < r1; ++row) {
-    const int grp = g[row];
+  // The streamed inputs of row + 1 are loaded (raw) while row is computed.
+  struct Raw {
+    Chunk8<T> x[NCH], dy[NCH], u[NCH], zu[NCH], r[NCH];
+    float mu, rs;
+    int grp;
+  };
+  auto load_raw = [&](Raw& R, int64_t row) {
+    R.mu = mean[row];
+    R.rs = rstd[row];
+    R.grp = g[row];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane * 8 + i * 512;
+      if (EXACT || c < d) {
+        R.x[i].load(x + row * ldx + c);
+        R.dy[i].load(dy + row * lddy + c);
+        if (GATE) {
+          R.u[i].load(u + row * ldu + c);
+          if (zu) R.zu[i].load(zu + row * ldzu + c);
+        } else if (resid) {
+          R.r[i].load(resid + row * ldr + c);
+        }
+      }
+    }
+  };
+  Chunk8<T> gam[NCH], bet[NCH];  // the current group's gamma / beta, reloaded on a change
+  auto process = [&](const Raw& R, int64_t row) {
+    const int grp = R.grp;
     if (grp != cur) {
       if (cur >= 0) flush();
       cur = grp;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = lane * 8 + i * 512;
+        if (EXACT || c < d) {
+          gam[i].load(gamma + (int64_t)grp * d + c);
+          if (GATE) bet[i].load(beta + (int64_t)grp * d + c);
+        }
+      }
     }
-    const float mu = mean[row], rs = rstd[row];
+    const float mu = R.mu, rs = R.rs;
     float n[NCH][8], e[NCH][8];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane * 8 + i * 512;
-      if (c < d) {
+      if (EXACT || c < d) {
         float dyv[8], ga[8];
-        load8(x + row * ldx + c, n[i]);
-        load8(dy + row * lddy + c, dyv);
-        load8(gamma + (int64_t)grp * d + c, ga);
+        R.x[i].get(n[i]);
+        R.dy[i].get(dyv);
+        gam[i].get(ga);
 #pragma unroll
         for (int k = 0; k < 8; ++k) n[i][k] = (n[i][k] - mu) * rs;
         if (GATE) {
           float uu[8], be[8], duv[8];
-          load8(u + row * ldu + c, uu);
-          load8(beta + (int64_t)grp * d + c, be);
+          R.u[i].get(uu);
+          bet[i].get(be);
 #pragma unroll
           for (int k = 0; k < 8; ++k) duv[k] = dyv[k] * (n[i][k] * ga[k] + be[k]);
           if (zu) {
             float zz[8];
-            load8(zu + row * ldzu + c, zz);
+            R.zu[i].get(zz);
 #pragma unroll
             for (int k = 0; k < 8; ++k) duv[k] *= silu_grad_t<T>(zz[k]);
           }
@@ -272,19 +331,29 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane * 8 + i * 512;
-      if (c < d) {
+      if (EXACT || c < d) {
         float out[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) out[k] = rs * (e[i][k] - s1 - n[i][k] * s2);
-        if (resid) {
+        if (!GATE && resid) {
           float rv[8];
-          load8(resid + row * ldr + c, rv);
+          R.r[i].get(rv);
 #pragma unroll
           for (int k = 0; k < 8; ++k) out[k] += rv[k];
         }
         store8(dx + row * lddx + c, out);
       }
     }
+  };
+  // two row buffers used in turn, so that no loaded register is ever copied
+  Raw ra, rb;
+  if (r0 < r1) load_raw(ra, r0);
+  for (int64_t row = r0; row < r1; row += 2) {
+    if (row + 1 < r1) load_raw(rb, row + 1);
+    process(ra, row);
+    if (row + 1 >= r1) break;
+    if (row + 2 < r1) load_raw(ra, row + 2);
+    process(rb, row + 1);
   }
   if (cur >= 0) flush();
   __syncthreads();
@@ -349,30 +418,26 @@ static int gln_bwd_dispatch(const void* dy, int64_t lddy, const void* x, int64_t
                             const void* zu, int64_t ldzu, float* partial, int* nparts, hipStream_t st) {
   const size_t lds = (size_t)2 * G * d * sizeof(float);
   const int nch = (d + 511) / 512;
-  const void* fn = nch <= 1 ? (const void*)gln_bwd_kernel<T, 1, GATE>
-                 : nch <= 2 ? (const void*)gln_bwd_kernel<T, 2, GATE>
-                 : nch <= 4 ? (const void*)gln_bwd_kernel<T, 4, GATE>
-                            : (const void*)gln_bwd_kernel<T, 8, GATE>;
+  const int N = nch <= 1 ? 1 : nch <= 2 ? 2 : nch <= 4 ? 4 : 8;
+  const bool exact = d == N * 512;
+  using KernelFn = decltype(&gln_bwd_kernel<T, 1, GATE, true>);
+#define GLN_BWD_SEL(NN) (exact ? (KernelFn)gln_bwd_kernel<T, NN, GATE, true> : (KernelFn)gln_bwd_kernel<T, NN, GATE, false>)
+  const KernelFn fn = N == 1 ? GLN_BWD_SEL(1) : N == 2 ? GLN_BWD_SEL(2) : N == 4 ? GLN_BWD_SEL(4) : GLN_BWD_SEL(8);
+#undef GLN_BWD_SEL
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)fn, 256, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
   int64_t nblk = (int64_t)per_cu * device_cu_count();
   const int64_t bound = gln_bwd_block_bound(T_);
   if (nblk > bound) nblk = bound;
   const int64_t rpb = (T_ + nblk - 1) / nblk;
   nblk = (T_ + rpb - 1) / rpb;
   *nparts = (int)nblk;
-#define GLN_BWD_ARGS                                                                                 \
-  (const T*)dy, lddy, (const T*)x, ldx, mean, rstd, (const T*)gamma, (const T*)beta, g, T_, d, G,   \
-      (T*)dx, lddx, (const T*)resid, ldr, (const T*)u, ldu, (T*)du, lddu, (const T*)zu, ldzu, partial, rpb
-  if (nch <= 1)
-    hipLaunchKernelGGL((gln_bwd_kernel<T, 1, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
-  else if (nch <= 2)
-    hipLaunchKernelGGL((gln_bwd_kernel<T, 2, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
-  else if (nch <= 4)
-    hipLaunchKernelGGL((gln_bwd_kernel<T, 4, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
-  else
-    hipLaunchKernelGGL((gln_bwd_kernel<T, 8, GATE>), dim3((unsigned)nblk), dim3(256), lds, st, GLN_BWD_ARGS);
-#undef GLN_BWD_ARGS
+  const T* dyp = (const T*)dy;
+  const T* xp = (const T*)x;
+  hipLaunchKernelGGL(fn, dim3((unsigned)nblk), dim3(256), lds, st, dyp, lddy, xp, ldx, mean, rstd,
+                     (const T*)gamma, (const T*)beta, g, T_, d, G, (T*)dx, lddx, (const T*)resid, ldr,
+                     (const T*)u, ldu, (T*)du, lddu, (const T*)zu, ldzu, partial, rpb);
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
 }
