@@ -179,6 +179,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* P, i
   return make_rsrc(P + (int64_t)r0 * ld + col0, (int)((int64_t)max(rlim - r0, 0) * ld * 2));
 }
 
+// Timestamp of token r0 + lane, or 0 at or beyond rlim, as a range-checked
+// buffer load: no select on the loaded value, so the load stays in flight
+// until the value is used.
+__device__ __forceinline__ int64_t ts_load(const int64_t* ts, int r0, int rlim, int lane) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(ts + r0, max(rlim - r0, 0) * 8);
+  return __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, 0));
+}
+
 // Tile load: thread chunks c = tid + 256 i, row c / (DH/8), 8 columns.
 template <int DH, int ROWS>
 __device__ __forceinline__ void tile_gload_rows(uint4* r, const uint16_t* __restrict__ P, int64_t ld, int r0,
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   auto gload = [&](int k0) {
     tile_gload_rows<DH, F_BK>(rk, K, ldqkv, k0, hi, hc, tid);
     vt_gload<DH>(rv, V, ldqkv, k0, hi, hc, tid);
-    if (wave == 0) rt = k0 + lane < hi ? ts[k0 + lane] : 0;
+    if (wave == 0) rt = ts_load(ts, k0, hi, lane);
   };
   auto swrite = [&](int buf) {
     tile_swrite_rows<DH, F_BK, KP>(Ks[buf], rk, tid);
@@ -478,6 +486,34 @@ __device__ __forceinline__ void quad_swrite_rows(uint16_t* s, const VtLoad<DH>& 
   if (!L.on) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) *(uint4*)(s + (4 * L.kq + r) * KP + 8 * L.c) = L.x[r];
+}
+
+// Row-major 64-row tile written from quads with a bank swizzle: for DH = 128
+// a row is 256 unpadded bytes and its 16-byte chunk c sits at position
+// c ^ ((r >> 2) ^ 4 (r & 3)) mod 16, which keeps both the quad writes (16
+// lanes = 16 quads, one chunk) and the A-operand reads (16 consecutive rows,
+// one chunk) on distinct banks; with a padded pitch the quad writes collide
+// four ways.  DH = 64 keeps the padded pitch.
+template <int DH> struct QuadRows {
+  static constexpr int PITCH = DH == 128 ? 128 : DH + 8;  // elements per row
+  static constexpr int SIZE = 64 * PITCH;
+  static __device__ __forceinline__ int off(int row, int ch) {
+    if (DH == 128) return row * 128 + 8 * (ch ^ (((row >> 2) ^ ((row & 3) << 2)) & 15));
+    return row * PITCH + 8 * ch;
+  }
+};
+template <int DH>
+__device__ __forceinline__ void quad_swrite_swz(uint16_t* s, const VtLoad<DH>& L) {
+  if (!L.on) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) *(uint4*)(s + QuadRows<DH>::off(4 * L.kq + r, L.c)) = L.x[r];
+}
+// A operand from a QuadRows tile: row r0 + l32, 8 columns at 16 ks + 8 g.
+template <int DH>
+__device__ __forceinline__ op8 row_operand_swz(const uint16_t* s, int r0, int ks, int lane) {
+  op8 o;
+  o.v = *(const u32x4_t*)(s + QuadRows<DH>::off(r0 + (lane & 31), 2 * ks + (lane >> 5)));
+  return o;
 }
 
 // ---------------------------------------------------------------------------
@@ -620,7 +656,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   auto gload = [&](int k0) {
     if (producer) vt_gload<DH>(ld, K, ldqkv, k0, hi, hc, ltid);
     else tile_gload_rows<DH, A_BK>(ld.x, V, ldqkv, k0, hi, hc, ltid);
-    if (wave == 0) rt = k0 + lane < hi ? ts[k0 + lane] : 0;
+    if (wave == 0) rt = ts_load(ts, k0, hi, lane);
   };
   auto swrite = [&](int buf) {
     if (producer) {
@@ -717,11 +753,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
     int H, float kexp, float alpha, float scale, uint8_t* __restrict__ dS, int64_t ds_cap,
     const int64_t* __restrict__ tprefix) {
-  constexpr int QP = AttnPitch<DH>::B128;
   constexpr int NS = DH / 16, NC = DH / 32;
   struct Smem {
-    uint16_t Qs[2][KV_BQ * QP];
-    uint16_t Ds[2][KV_BQ * QP];
+    uint16_t Qs[2][QuadRows<DH>::SIZE];
+    uint16_t Ds[2][QuadRows<DH>::SIZE];
     uint16_t Qt[2][DH * VT_PITCH];
     uint16_t Dt[2][DH * VT_PITCH];
     uint32_t Fx[4][32 * 16 * 2];  // per group: 2 x 16 x 32 lanes
@@ -795,14 +830,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   auto gload = [&](int q0) {
     if (producer) vt_gload<DH>(ld, Q, ldqkv, q0, qhi, hc, ltid);
     else vt_gload<DH>(ld, dO, lddo, q0, qhi, hc, ltid);
-    if (!full && wave == 0) rt = q0 + lane < qhi ? ts[q0 + lane] : 0;
+    if (!full && wave == 0) rt = ts_load(ts, q0, qhi, lane);
   };
   auto swrite = [&](int buf) {
     if (producer) {
-      quad_swrite_rows<DH>(Qs[buf], ld);
+      quad_swrite_swz<DH>(Qs[buf], ld);
       vt_swrite<DH>(Qt[buf], ld);
     } else {
-      quad_swrite_rows<DH>(Ds[buf], ld);
+      quad_swrite_swz<DH>(Ds[buf], ld);
       vt_swrite<DH>(Dt[buf], ld);
     }
     if (!full && wave == 0) Tq[buf][lane] = rt;
@@ -816,17 +851,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   uint32_t* fx = Fx[grp];
   for (int it = 0; it < nqt; ++it) {
     const int buf = it & 1, q0 = qlo + it * KV_BQ;
-    const bool more = it + 1 < nqt;
-    if (more) gload(q0 + KV_BQ);
+    gload(q0 + KV_BQ);  // past the query range: zeros, never used
     // phase 1: S (producer) or dA (consumer) for 64 queries x 32 keys
     const uint16_t* A = producer ? Qs[buf] : Ds[buf];
     f32x16_t x[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<QP>(A, t * 32, 0, lane), bop[0], f32x16_t{});
+    for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand_swz<DH>(A, t * 32, 0, lane), bop[0], f32x16_t{});
 #pragma unroll
     for (int s = 1; s < NS; ++s)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand<QP>(A, t * 32, s, lane), bop[s], x[t]);
+      for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand_swz<DH>(A, t * 32, s, lane), bop[s], x[t]);
     pipeline_lds_mfma<2 * NS, 8>();
     op8 w[4];
     if (producer) {
@@ -862,7 +896,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], vt_operand(Bt, u, c * 32, lane), acc[c]);
     pipeline_lds_mfma<4 * NC, 8>();
-    if (more) swrite(buf ^ 1);
+    swrite(buf ^ 1);
     __syncthreads();
   }
   // producer holds dV, consumer dK; both scale by alpha * c
