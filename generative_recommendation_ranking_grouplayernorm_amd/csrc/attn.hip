@@ -980,7 +980,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
   const int nsteps = na + nb;
   const int rt_stage0 = (s_end - lo) >> 6;
 
-  // per-thread pieces of the 16 KB dS step: chunks tid + 256 i, stage i >> 1
+  // Per-thread pieces of the 16 KB dS step: 16-byte chunk cidx + 256 i
+  // (stage i >> 1).  The chunk of each lane is chosen so that the LDS
+  // positions ds_lds_pos of the 16 lanes of each write group fall on 16
+  // distinct 16-byte bank groups (lane bits 0-3 land on position bits 4-7);
+  // lanes 0-1 of every quad still read one full 64-byte global segment.
+  const int cidx = (lane & 3) | (((lane >> 4) & 3) << 2) | ((wave & 1) << 4) | (((lane >> 2) & 3) << 5) |
+                   ((wave >> 1) << 7);
   u32x4_t rs[4];
   VtLoad<DH> rk;
   auto gload = [&](int it) {
@@ -992,12 +998,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
     for (int i = 0; i < 4; ++i) {
       const int st = 2 * qt + (i >> 1);
       const bool avail = lo + 64 * st < hi && (k0 < s_end || k0 >= r_end || st >= rt_stage0);
-      rs[i] = avail ? __builtin_nontemporal_load((const u32x4_t*)(src + 16 * (tid + 256 * i)))
+      rs[i] = avail ? __builtin_nontemporal_load((const u32x4_t*)(src + 16 * (cidx + 256 * i)))
                     : u32x4_t{0, 0, 0, 0};
     }
     vt_gload<DH>(rk, K, ldqkv, kpos, hi, hc, tid);
   };
-  const int wsw = ds_lds_pos(16 * tid);
+  const int wsw = ds_lds_pos(16 * cidx);
   auto swrite = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) *(u32x4_t*)(Ss[buf] + wsw + 4096 * i) = rs[i];
