@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle baseline sample (0 disables it)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--serving", action="store_true",
+                    help="time the 22-layer fp16 one-request serving forward per candidate count instead "
+                         "(eager layer calls, one stack call, graph replay)")
+    ap.add_argument("--requests", type=int, default=200, help="timed requests per K and mode (--serving)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy MIB MiB device-to-device 3 times (a plain copy kernel "
                          "of known size, the calibration for HBM byte counters)")
@@ -256,6 +260,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is a "
               f"design note, not part of this build.", file=sys.stderr)
         sys.exit(2)
+    if args.serving:
+        serving_bench(args)
+        return
     import numpy as np
     import torch
 
@@ -390,6 +397,121 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def serving_bench(args):
+    """One request (one user, 1000 history tokens, 32 real-time tokens, K
+    candidates) through 22 fp16 layers of d_model 1024, per K in the sweep.
+    Three ways to issue it: 22 single-layer calls from Python, one stack
+    call, one graph launch.  Latency = host clock from the first call to the
+    end of a stream synchronisation, one request at a time; throughput =
+    requests issued back to back on one stream, then one synchronisation.
+    GPU time = the summed kernel durations of one request (HIP events around
+    every kernel step, a separate pass)."""
+    import numpy as np
+    import torch
+
+    import generative_recommendation_ranking_grouplayernorm_amd.binding as mb
+    from generative_recommendation_ranking_grouplayernorm_amd import flops as fl
+    from mtgr_inputs import CONFIGS, config_inputs
+
+    cfg_id = 5
+    cfg = CONFIGS[cfg_id]
+    dev = torch.device("cuda:0")
+    lib = mb.load_library()
+    dt = torch.float16
+    d, H, L = cfg["d"], cfg["H"], cfg["layers"]
+    _, params, _ = config_inputs(cfg_id, seed=args.seed)
+
+    def to(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(dev)
+
+    keep = [{k: to(getattr(p, k)) for k in ("W_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o")}
+            for p in params]
+    lps = [mb.make_params(t, H) for t in keep]
+    stream = torch.cuda.current_stream()
+    n = max(args.requests, 10)
+    results = {}
+    for K in cfg["K_sweep"]:
+        batch, _, x = config_inputs(cfg_id, seed=args.seed, K=K)
+        T = batch.T
+        scale = 1.0 / batch.max_len
+        xd = to(x)
+        y = torch.empty_like(xd)
+        off = torch.from_numpy(batch.offsets).to(dev)
+        g = torch.from_numpy(batch.group_ids).to(dev)
+        ts = torch.from_numpy(batch.timestamps).to(dev)
+        ws_l = mb.workspace(mb.OP_LAYER_FWD, 1, T, d, H, dt, dev)
+        ws_s = mb.workspace(mb.OP_STACK_FWD, 1, T, d, H, dt, dev)
+        h2 = torch.empty_like(xd)
+        graph = mb.mtgr_stack_graph_create(lps, xd, y, off, g, ts, scale, ws_s)
+
+        def layers():
+            src, dst = xd, (y if L % 2 == 1 else h2)
+            for i, lp in enumerate(lps):
+                mb.mtgr_hstu_layer_fwd(lp, src, dst, None, off, g, ts, scale, ws_l, stream)
+                src, dst = dst, (h2 if dst is y else y)
+
+        def stack():
+            mb.mtgr_hstu_stack_fwd(lps, xd, y, off, g, ts, scale, ws_s, stream)
+
+        def replay():
+            graph.launch(stream)
+
+        modes = {"layer_calls": layers, "stack_call": stack, "graph": replay}
+        res = {}
+        for name, fn in modes.items():
+            for _ in range(max(args.warmup, 3)):
+                fn()
+            torch.cuda.synchronize()
+            lat = []
+            for _ in range(n):
+                t0 = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                lat.append((time.perf_counter() - t0) * 1e3)
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            thr = n / (time.perf_counter() - t0)
+            lat = np.array(lat)
+            res[name] = {"p50_ms": round(float(np.percentile(lat, 50)), 4),
+                         "p99_ms": round(float(np.percentile(lat, 99)), 4),
+                         "mean_ms": round(float(lat.mean()), 4),
+                         "requests_per_sec": round(thr, 1)}
+        # kernel time of one request, measured on the eager stack call
+        lib.mtgr_profile_enable(1)
+        for _ in range(5):
+            stack()
+        torch.cuda.synchronize()
+        prof = profile_summary(lib)
+        lib.mtgr_profile_enable(0)
+        res["gpu_ms_per_request"] = round(sum(v[0] for v in prof.values()) / 5, 4)
+        res["kernels_ms_per_request"] = {k: round(v[0] / 5, 4) for k, v in sorted(prof.items())}
+        P = fl.visible_pairs(batch.offsets, batch.group_ids, batch.timestamps)
+        res["tokens"] = T
+        res["fwd_gflop"] = round(L * (4 * d * P + fl.layer_gemm_flops(T, d, backward=False)) / 1e9, 2)
+        graph.close()
+        results[K] = res
+        print(f"[bench] K={K}: " + ", ".join(f"{m} p50 {res[m]['p50_ms']} ms" for m in modes),
+              file=sys.stderr, flush=True)
+    g20 = results[min(results)]
+    out = {
+        "metric": "serving request latency, 22-layer fp16 forward, one request",
+        "value": g20["graph"]["p50_ms"],
+        "unit": "ms (P50, K=20, graph replay)",
+        "n_gpus": 1,
+        "requests": n,
+        "higher_is_better": False,
+        "dtype": "f16",
+        "data": "synthetic (seeded request, random-init weights)",
+        "config": {"workload": "MTGR serving forward, 1 user x (8 profile + 1000 history + 32 real-time + K "
+                               "candidates), 22 layers, d_model 1024, 8 heads of 128",
+                   "K_sweep": list(results)},
+        "per_K": results,
     }
     print(json.dumps(out))
 

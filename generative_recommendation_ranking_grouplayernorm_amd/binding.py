@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Dict, Optional
+from typing import Dict, Optional, Sequence
 
 import torch
 
@@ -18,14 +18,15 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmtgr.so")
 
 MTGR_F32, MTGR_BF16, MTGR_F16 = 0, 1, 2
-OP_PREP, OP_GLN_FWD, OP_GLN_BWD, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD = range(7)
+OP_PREP, OP_GLN_FWD, OP_GLN_BWD, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_STACK_FWD = range(8)
 
 _DT = {torch.float32: MTGR_F32, torch.bfloat16: MTGR_BF16, torch.float16: MTGR_F16}
 
 EXPORTED = (
     "mtgr_version", "mtgr_status_string", "mtgr_workspace_size", "mtgr_jagged_prep",
     "mtgr_group_layernorm", "mtgr_group_layernorm_bwd", "mtgr_hstu_attn_fwd", "mtgr_hstu_attn_bwd",
-    "mtgr_hstu_layer_fwd", "mtgr_hstu_layer_bwd",
+    "mtgr_hstu_layer_fwd", "mtgr_hstu_layer_bwd", "mtgr_hstu_stack_fwd", "mtgr_stack_graph_create",
+    "mtgr_stack_graph_launch", "mtgr_stack_graph_destroy",
 )
 
 
@@ -90,6 +91,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mtgr_hstu_layer_bwd": ([ctypes.POINTER(LayerParams), P, ctypes.POINTER(LayerSaved), P, P,
                                  ctypes.POINTER(LayerGrads), ctypes.POINTER(LayerBwdExtras), P, P, P, I32, I64,
                                  I32, F, ctypes.c_int, P, SZ, P], ctypes.c_int),
+        "mtgr_hstu_stack_fwd": ([ctypes.POINTER(LayerParams), I32, P, P, P, P, P, I32, I64, F, ctypes.c_int, P,
+                                 SZ, P], ctypes.c_int),
+        "mtgr_stack_graph_create": ([ctypes.POINTER(LayerParams), I32, P, P, P, P, P, I32, I64, F, ctypes.c_int,
+                                     P, SZ, ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
+        "mtgr_stack_graph_launch": ([P, P], ctypes.c_int),
+        "mtgr_stack_graph_destroy": ([P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -251,3 +258,63 @@ def mtgr_hstu_layer_bwd(params: LayerParams, x_in, saved: LayerSaved, dx_out, dx
         ctypes.byref(params), _p(x_in), ctypes.byref(saved), _p(dx_out), _p(dx_in), ctypes.byref(g), ex,
         _p(offsets), _p(group_ids), _p(timestamps), B, T, max_len, attn_scale, dtype_code(x_in.dtype), _p(ws),
         ws.numel(), _stream(stream)))
+
+
+def _layer_array(layers: Sequence[LayerParams]):
+    arr = (LayerParams * len(layers))(*layers)
+    return arr, len(layers)
+
+
+def mtgr_hstu_stack_fwd(layers: Sequence[LayerParams], x_in, x_out, offsets, group_ids, timestamps, attn_scale, ws,
+                        stream=None) -> None:
+    arr, L = _layer_array(layers)
+    B = offsets.numel() - 1
+    T = x_in.shape[0]
+    _check("mtgr_hstu_stack_fwd", load_library().mtgr_hstu_stack_fwd(
+        arr, L, _p(x_in), _p(x_out), _p(offsets), _p(group_ids), _p(timestamps), B, T, attn_scale,
+        dtype_code(x_in.dtype), _p(ws), ws.numel(), _stream(stream)))
+
+
+class StackGraph:
+    """Handle of mtgr_stack_graph_create.  Holds references to the tensors the
+    graph reads and writes so they outlive it; ``close`` (or garbage
+    collection) calls mtgr_stack_graph_destroy."""
+
+    def __init__(self, handle: int, keep: tuple):
+        self.handle = handle
+        self._keep = keep
+
+    def launch(self, stream=None) -> None:
+        mtgr_stack_graph_launch(self, stream)
+
+    def close(self) -> None:
+        if self.handle:
+            load_library().mtgr_stack_graph_destroy(self.handle)
+            self.handle = None
+            self._keep = ()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def mtgr_stack_graph_create(layers: Sequence[LayerParams], x_in, x_out, offsets, group_ids, timestamps, attn_scale,
+                            ws) -> StackGraph:
+    arr, L = _layer_array(layers)
+    B = offsets.numel() - 1
+    T = x_in.shape[0]
+    h = ctypes.c_void_p()
+    _check("mtgr_stack_graph_create", load_library().mtgr_stack_graph_create(
+        arr, L, _p(x_in), _p(x_out), _p(offsets), _p(group_ids), _p(timestamps), B, T, attn_scale,
+        dtype_code(x_in.dtype), _p(ws), ws.numel(), ctypes.byref(h)))
+    return StackGraph(h.value, (x_in, x_out, offsets, group_ids, timestamps, ws))
+
+
+def mtgr_stack_graph_launch(graph: StackGraph, stream=None) -> None:
+    _check("mtgr_stack_graph_launch", load_library().mtgr_stack_graph_launch(graph.handle, _stream(stream)))
+
+
+def mtgr_stack_graph_destroy(graph: StackGraph) -> None:
+    graph.close()

@@ -56,6 +56,11 @@ size_t layer_fwd_ws(int B, int64_t T, int d, int dt) {
   return n;
 }
 
+// The layer intermediates plus one hidden-state buffer between layers.
+size_t stack_fwd_ws(int B, int64_t T, int d, int dt) {
+  return layer_fwd_ws(B, T, d, dt) + align_up((size_t)T * d * elt(dt), 256);
+}
+
 // dS storage of the backward (bf16/f16 with a declared row bound only).
 size_t ds_ws(int B, int64_t T, int max_len, int H, int dt) {
   return dt == MTGR_F32 ? 0 : attn_ds_bytes(B, T, max_len, H);
@@ -131,6 +136,7 @@ size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t max_len, int32_
     case MTGR_OP_ATTN_BWD: return attn_bwd_ws(B, T, max_len, H, dt);
     case MTGR_OP_LAYER_FWD: return layer_fwd_ws(B, T, d, dt);
     case MTGR_OP_LAYER_BWD: return layer_bwd_ws(B, T, max_len, d, H, dt);
+    case MTGR_OP_STACK_FWD: return stack_fwd_ws(B, T, d, dt);
     default: return 0;
   }
 }
@@ -251,40 +257,15 @@ static int layer_param_checks(const mtgr_layer_params* p, int dt) {
   return MTGR_OK;
 }
 
-int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_out, const mtgr_layer_saved* saved,
-                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
-                        int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
-                        mtgr_stream_t stream) {
-  int r = layer_param_checks(p, dt);
-  if (r) return r;
-  if (!jagged_ok(offsets, group_ids, timestamps, B, T)) return MTGR_ERR_INVALID_ARG;
+// a2..a6 of one layer on a prepared batch (the tile lists in pv); xhat,
+// uqkv and o are the layer's intermediates, y may alias xhat.
+static int layer_fwd_body(const mtgr_layer_params* p, const void* x_in, void* x_out, const mtgr_layer_saved* saved,
+                          const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T,
+                          float attn_scale, int dt, const PrepView& pv, void* xhat, void* uqkv, void* o, void* y,
+                          hipStream_t st) {
   const int d = p->d;
-  if (T > 0 && (!x_in || !x_out)) return MTGR_ERR_INVALID_ARG;
-  if (x_in == x_out && T > 0) return MTGR_ERR_INVALID_ARG;
-  if (!vec_ok(x_in, d, dt) || !vec_ok(x_out, d, dt)) return MTGR_ERR_INVALID_ARG;
-  if (saved && (!saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->z || !saved->uqkv || !saved->o ||
-                !saved->mean2 || !saved->rstd2 || !saved->y))
-    return MTGR_ERR_INVALID_ARG;
-  if (ws_bytes < layer_fwd_ws(B, T, d, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
-  if (T == 0 || B == 0) return MTGR_OK;
-  hipStream_t st = S(stream);
   const size_t e = elt(dt);
-  Carver cv{(char*)workspace, ws_bytes};
-  void* ws_prep = cv.take(attn_ws(B, T));
-  void* ws_xhat = cv.take((size_t)T * d * e);
-  void* ws_uqkv = cv.take((size_t)T * 4 * d * e);
-  void* ws_o = cv.take((size_t)T * d * e);
-  if (!cv.ok) return MTGR_ERR_WORKSPACE_TOO_SMALL;
-  void* xhat = saved ? saved->xhat : ws_xhat;
-  void* uqkv = saved ? saved->uqkv : ws_uqkv;
-  void* o = saved ? saved->o : ws_o;
-  void* y = saved ? saved->y : ws_xhat;  // xhat is dead once the projection has run
-  PrepView pv;
-  {
-    ProfScope ps("prep", st);
-    r = launch_prep(offsets, group_ids, B, T, ws_prep, st, &pv);
-  }
-  if (r) return r;
+  int r;
   // a2: input group norm
   {
     ProfScope ps("gln1_fwd", st);
@@ -323,6 +304,107 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
   eo.C = x_out; eo.ldc = d; eo.bias = p->b_o; eo.R = x_in; eo.ldr = d;
   ProfScope ps("gemm_out_resid", st);
   return launch_gemm(dt, y, d, true, p->W_o, d, true, (int)T, d, d, eo, 1, st);
+}
+
+int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_out, const mtgr_layer_saved* saved,
+                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                        int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                        mtgr_stream_t stream) {
+  int r = layer_param_checks(p, dt);
+  if (r) return r;
+  if (!jagged_ok(offsets, group_ids, timestamps, B, T)) return MTGR_ERR_INVALID_ARG;
+  const int d = p->d;
+  if (T > 0 && (!x_in || !x_out)) return MTGR_ERR_INVALID_ARG;
+  if (x_in == x_out && T > 0) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(x_in, d, dt) || !vec_ok(x_out, d, dt)) return MTGR_ERR_INVALID_ARG;
+  if (saved && (!saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->z || !saved->uqkv || !saved->o ||
+                !saved->mean2 || !saved->rstd2 || !saved->y))
+    return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < layer_fwd_ws(B, T, d, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  if (T == 0 || B == 0) return MTGR_OK;
+  hipStream_t st = S(stream);
+  const size_t e = elt(dt);
+  Carver cv{(char*)workspace, ws_bytes};
+  void* ws_prep = cv.take(attn_ws(B, T));
+  void* ws_xhat = cv.take((size_t)T * d * e);
+  void* ws_uqkv = cv.take((size_t)T * 4 * d * e);
+  void* ws_o = cv.take((size_t)T * d * e);
+  if (!cv.ok) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  void* xhat = saved ? saved->xhat : ws_xhat;
+  void* uqkv = saved ? saved->uqkv : ws_uqkv;
+  void* o = saved ? saved->o : ws_o;
+  void* y = saved ? saved->y : ws_xhat;  // xhat is dead once the projection has run
+  PrepView pv;
+  {
+    ProfScope ps("prep", st);
+    r = launch_prep(offsets, group_ids, B, T, ws_prep, st, &pv);
+  }
+  if (r) return r;
+  return layer_fwd_body(p, x_in, x_out, saved, group_ids, timestamps, B, T, attn_scale, dt, pv, xhat, uqkv, o, y,
+                        st);
+}
+
+}  // extern "C"
+
+namespace mtgr {
+
+int stack_fwd_validate(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                       const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                       int64_t T, int dt, const void* workspace, size_t ws_bytes) {
+  if (L < 1 || !layers) return MTGR_ERR_INVALID_ARG;
+  for (int l = 0; l < L; ++l) {
+    const int r = layer_param_checks(&layers[l], dt);
+    if (r) return r;
+    if (layers[l].d != layers[0].d || layers[l].H != layers[0].H || layers[l].G != layers[0].G)
+      return MTGR_ERR_INVALID_ARG;
+  }
+  if (!jagged_ok(offsets, group_ids, timestamps, B, T)) return MTGR_ERR_INVALID_ARG;
+  const int d = layers[0].d;
+  if (T > 0 && (!x_in || !x_out)) return MTGR_ERR_INVALID_ARG;
+  if (x_in == x_out && T > 0) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(x_in, d, dt) || !vec_ok(x_out, d, dt)) return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < stack_fwd_ws(B, T, d, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  return MTGR_OK;
+}
+
+}  // namespace mtgr
+
+extern "C" {
+
+int mtgr_hstu_stack_fwd(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                        int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                        mtgr_stream_t stream) {
+  int r = stack_fwd_validate(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, dt, workspace, ws_bytes);
+  if (r) return r;
+  if (T == 0 || B == 0) return MTGR_OK;
+  const int d = layers[0].d;
+  hipStream_t st = S(stream);
+  const size_t e = elt(dt);
+  Carver cv{(char*)workspace, ws_bytes};
+  void* ws_prep = cv.take(attn_ws(B, T));
+  void* xhat = cv.take((size_t)T * d * e);
+  void* uqkv = cv.take((size_t)T * 4 * d * e);
+  void* o = cv.take((size_t)T * d * e);
+  void* h = cv.take((size_t)T * d * e);
+  if (!cv.ok) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  PrepView pv;
+  {
+    ProfScope ps("prep", st);
+    r = launch_prep(offsets, group_ids, B, T, ws_prep, st, &pv);
+  }
+  if (r) return r;
+  // Layer l writes x_out when L-1-l is even and the spare buffer h otherwise,
+  // so consecutive layers alternate and the last one lands in x_out.
+  const void* src = x_in;
+  for (int l = 0; l < L; ++l) {
+    void* dst = ((L - 1 - l) % 2 == 0) ? x_out : h;
+    r = layer_fwd_body(&layers[l], src, dst, nullptr, group_ids, timestamps, B, T, attn_scale, dt, pv, xhat, uqkv,
+                       o, xhat, st);
+    if (r) return r;
+    src = dst;
+  }
+  return MTGR_OK;
 }
 
 int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr_layer_saved* saved,

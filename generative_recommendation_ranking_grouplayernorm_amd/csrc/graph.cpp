@@ -1,0 +1,83 @@
+// Captured stack forwards: one mtgr_hstu_stack_fwd call recorded as a HIP
+// graph on a private stream, then replayed with a single launch.
+#include <new>
+
+#include "kernels.h"
+
+using namespace mtgr;
+
+struct mtgr_graph_s {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+void release(mtgr_graph_s* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtgr_stack_graph_create(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                            const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                            int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                            mtgr_graph* out) {
+  if (!out) return MTGR_ERR_INVALID_ARG;
+  *out = nullptr;
+  // Timing events recorded during capture would become graph nodes.
+  if (profiling_enabled()) return MTGR_ERR_INVALID_ARG;
+  // Empty batches launch nothing; refuse them here so that every handle
+  // holds a graph with work in it.
+  if (T <= 0 || B <= 0) return MTGR_ERR_INVALID_ARG;
+  int r = stack_fwd_validate(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, dt, workspace, ws_bytes);
+  if (r) return r;
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MTGR_ERR_HIP;
+  mtgr_graph_s* g = new (std::nothrow) mtgr_graph_s;
+  if (!g) {
+    (void)hipStreamDestroy(cs);
+    return MTGR_ERR_HIP;
+  }
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    r = MTGR_ERR_HIP;
+  } else {
+    r = mtgr_hstu_stack_fwd(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt,
+                            workspace, ws_bytes, (mtgr_stream_t)cs);
+    // End the capture whatever happened, so the stream is usable again.
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(cs, &graph);
+    g->graph = graph;
+    if (r == MTGR_OK && (e != hipSuccess || !graph)) r = MTGR_ERR_HIP;
+  }
+  if (r == MTGR_OK && hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0) != hipSuccess) {
+    g->exec = nullptr;
+    r = MTGR_ERR_HIP;
+  }
+  (void)hipStreamDestroy(cs);
+  if (r != MTGR_OK) {
+    release(g);
+    // A failed capture can leave a sticky launch error behind.
+    (void)hipGetLastError();
+    return r;
+  }
+  *out = g;
+  return MTGR_OK;
+}
+
+int mtgr_stack_graph_launch(mtgr_graph g, mtgr_stream_t stream) {
+  if (!g || !g->exec) return MTGR_ERR_INVALID_ARG;
+  return hipGraphLaunch(g->exec, (hipStream_t)stream) == hipSuccess ? MTGR_OK : MTGR_ERR_HIP;
+}
+
+int mtgr_stack_graph_destroy(mtgr_graph g) {
+  release(g);
+  return MTGR_OK;
+}
+
+}  // extern "C"

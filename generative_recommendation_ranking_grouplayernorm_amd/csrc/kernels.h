@@ -21,6 +21,13 @@ class ProfScope {
   hipStream_t stream_;
   void* begin_;
 };
+// True while mtgr_profile_enable(1) is in effect.
+bool profiling_enabled();
+
+// Host-side argument checks of mtgr_hstu_stack_fwd (MTGR_OK or a status).
+int stack_fwd_validate(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                       const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                       int64_t T, int dt, const void* workspace, size_t ws_bytes);
 
 // Rows per attention tile: queries per forward / dQ workgroup, keys per
 // dK/dV workgroup.

@@ -32,6 +32,11 @@ hipEvent_t get_event() {
 
 }  // namespace
 
+bool profiling_enabled() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_on;
+}
+
 ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), stream_(s), begin_(nullptr) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on) return;

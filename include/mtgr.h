@@ -18,11 +18,15 @@
  *          训练数据怎么组织 (jagged rows, timestamps kept for the mask).
  *   [fr]   "MTGR：混合范式建模" (fun-rec 7.3): 7.3.3 (GLN formula),
  *          7.3.4 (the three mask rules).
+ *   [dr]   paper-daily deep reading of the Meituan blog post: 2 方法详解
+ *          (extra norm on every layer's input), 3 核心技术贡献 and
+ *          4 实验结果分析 / 工程指标 (fp16 serving, graph replay, P99).
  *
  * Conventions shared by every call
  *   - All pointers are caller-owned DEVICE memory unless stated otherwise.
- *     The library never allocates or frees memory; scratch space comes only
- *     through `workspace`, sized by mtgr_workspace_size().
+ *     The library never allocates or frees device memory; scratch space
+ *     comes only through `workspace`, sized by mtgr_workspace_size().  (The
+ *     graph handles below hold host-side runtime objects only.)
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronises.
  *   - `dt` is one mtgr_dtype for every floating tensor of a call; statistics
@@ -70,7 +74,8 @@ typedef enum {
   MTGR_OP_ATTN_FWD = 3,
   MTGR_OP_ATTN_BWD = 4,
   MTGR_OP_LAYER_FWD = 5,
-  MTGR_OP_LAYER_BWD = 6
+  MTGR_OP_LAYER_BWD = 6,
+  MTGR_OP_STACK_FWD = 7
 } mtgr_op;
 
 typedef void* mtgr_stream_t; /* hipStream_t */
@@ -241,6 +246,54 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
                         const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T,
                         float attn_scale, int dt, void* workspace, size_t ws_bytes,
                         mtgr_stream_t stream);
+
+/*
+ * Serving forward of an L-layer encoder stack: the L identical blocks of
+ * [blog] 7 and [pd] 模型怎么搭, each exactly as mtgr_hstu_layer_fwd, with
+ * the jagged tile lists built once for all layers.  The serving reading of
+ * [pd] 计算量涨了 65 倍，训练成本怎么压住 (one pass per request, all
+ * candidates together, fp16) is a batch with B = 1.
+ *   layers      : HOST array of L >= 1 parameter sets (device pointers
+ *                 inside), all with the same d, H and G; read during the
+ *                 call only
+ *   x_in        : [T, d] input, not modified; x_out : [T, d] output of the
+ *                 last layer, must not alias x_in
+ *   workspace   : MTGR_OP_STACK_FWD bytes (independent of L)
+ *   Results are bit-identical to L chained mtgr_hstu_layer_fwd calls.
+ */
+int mtgr_hstu_stack_fwd(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
+                        int32_t B, int64_t T, float attn_scale, int dt, void* workspace,
+                        size_t ws_bytes, mtgr_stream_t stream);
+
+/*
+ * A stack forward captured once as a HIP graph and replayed with one launch
+ * (the graph replay of the serving path: [pd] 计算量涨了 65 倍，训练成本怎么压住
+ * and [dr] 4 工程指标 report its throughput and P99 gains).
+ *   mtgr_stack_graph_create: records mtgr_hstu_stack_fwd with exactly these
+ *     arguments on a private stream and instantiates the graph; no kernel
+ *     runs.  Argument errors are those of mtgr_hstu_stack_fwd; B = 0 or
+ *     T = 0 is MTGR_ERR_INVALID_ARG; so is a call while mtgr_profile_enable(1)
+ *     is in effect.  Capture or instantiation failure: MTGR_ERR_HIP.  On
+ *     error *out is NULL.
+ *   The graph keeps every device pointer and the values B, T, L,
+ *   attn_scale, dt and each layer's scalars (eps, alpha, shapes).  Between
+ *   launches the caller may rewrite the CONTENTS of the buffers (a new
+ *   request of the same B and T: x_in, offsets, group_ids, timestamps,
+ *   weights) but must neither free nor move them while the handle lives.
+ *   One graph per (B, T) shape: a serving loop keeps one per candidate count.
+ *   mtgr_stack_graph_launch: enqueues one replay on `stream`; replays that
+ *     share a workspace must not overlap.  NULL handle: MTGR_ERR_INVALID_ARG.
+ *   mtgr_stack_graph_destroy: releases the handle (NULL is accepted); the
+ *     caller ensures no launch of it is still pending.
+ */
+typedef struct mtgr_graph_s* mtgr_graph;
+int mtgr_stack_graph_create(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                            const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
+                            int32_t B, int64_t T, float attn_scale, int dt, void* workspace,
+                            size_t ws_bytes, mtgr_graph* out);
+int mtgr_stack_graph_launch(mtgr_graph g, mtgr_stream_t stream);
+int mtgr_stack_graph_destroy(mtgr_graph g);
 
 /*
  * a6..a2 backward (a8 plus the attention backward a7): from dx_out computes

@@ -37,7 +37,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for n in ("mtgr_group_layernorm", "mtgr_hstu_attn_fwd", "mtgr_hstu_attn_bwd", "mtgr_hstu_layer_fwd",
               "mtgr_hstu_layer_bwd", "mtgr_group_layernorm_bwd", "mtgr_jagged_prep", "mtgr_workspace_size",
-              "mtgr_status_string", "mtgr_version"):
+              "mtgr_status_string", "mtgr_version", "mtgr_hstu_stack_fwd", "mtgr_stack_graph_create",
+              "mtgr_stack_graph_launch", "mtgr_stack_graph_destroy"):
         assert n in names
 
 
@@ -62,7 +63,7 @@ def test_workspace_sizes_grow(lib):
     from generative_recommendation_ranking_grouplayernorm_amd import binding as b
     import torch
 
-    for op in (b.OP_ATTN_FWD, b.OP_ATTN_BWD, b.OP_LAYER_FWD, b.OP_LAYER_BWD, b.OP_GLN_BWD):
+    for op in (b.OP_ATTN_FWD, b.OP_ATTN_BWD, b.OP_LAYER_FWD, b.OP_LAYER_BWD, b.OP_GLN_BWD, b.OP_STACK_FWD):
         a = b.mtgr_workspace_size(op, 8, 1000, 0, 256, 2, torch.bfloat16)
         c = b.mtgr_workspace_size(op, 80, 65536, 0, 256, 2, torch.bfloat16)
         assert 0 < a <= c
@@ -178,6 +179,57 @@ def test_layer_param_errors(lib):
     assert call(H=4, dh=64, d=256, G=9) == -1
     assert call(W_o=None) == -1
     assert call(H=2, dh=96, d=192) == -2
+
+
+def test_stack_and_graph_argument_errors(lib):
+    """The serving entry points validate on the host before any HIP call
+    (the graph constructor before it creates its capture stream)."""
+    from generative_recommendation_ranking_grouplayernorm_amd import binding as b
+    import torch
+
+    P = ctypes.c_void_p
+    d, H, T = 256, 2, 10
+    ws_need = b.mtgr_workspace_size(b.OP_STACK_FWD, 1, T, 0, d, H, torch.bfloat16)
+    assert ws_need == (b.mtgr_workspace_size(b.OP_LAYER_FWD, 1, T, 0, d, H, torch.bfloat16)
+                       + ((T * d * 2 + 255) // 256) * 256)
+
+    def lp(**kw):
+        p = dict(W_uqkv=8192, b_uqkv=None, gamma1=8192, beta1=8192, gamma2=8192, beta2=8192, W_o=8192, b_o=None,
+                 d=d, H=H, dh=d // H, G=4, eps=1e-5, alpha=1.0)
+        p.update(kw)
+        return b.LayerParams(*(p[k] for k in ("W_uqkv", "b_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o",
+                                              "b_o", "d", "H", "dh", "G", "eps", "alpha")))
+
+    def stack(layers, x_in=8192, x_out=16384, B=1, n=T, ws=1 << 30, L=None):
+        arr = (b.LayerParams * len(layers))(*layers)
+        return lib.mtgr_hstu_stack_fwd(arr, len(layers) if L is None else L, P(x_in), P(x_out), P(4096), P(4096),
+                                       P(4096), B, n, 0.1, 1, P(8192), ws, None)
+
+    def create(layers, x_in=8192, x_out=16384, B=1, n=T, ws=1 << 30, L=None):
+        arr = (b.LayerParams * len(layers))(*layers)
+        h = ctypes.c_void_p(1234)
+        r = lib.mtgr_stack_graph_create(arr, len(layers) if L is None else L, P(x_in), P(x_out), P(4096),
+                                        P(4096), P(4096), B, n, 0.1, 1, P(8192), ws, ctypes.byref(h))
+        assert h.value is None, "handle must be NULL on error"
+        return r
+
+    for fn in (stack, create):
+        assert fn([lp()], L=0) == -1                              # no layers
+        assert fn([lp(), lp(H=4, dh=64)]) == -1                   # layers disagree on H
+        assert fn([lp(), lp(W_o=None)]) == -1                     # a later layer is incomplete
+        assert fn([lp(), lp(H=2, dh=96, d=192)]) == -2            # unsupported head size in layer 2
+        assert fn([lp()], x_out=8192) == -1                       # output aliases input
+        assert fn([lp()], x_in=8200) == -1                        # misaligned input
+        assert fn([lp()], ws=ws_need - 1) == -3                   # workspace one byte short
+    # empty batches: a no-op for the call, refused by the graph constructor
+    assert stack([lp()], n=0, B=1, x_in=0, x_out=0) == 0
+    assert create([lp()], n=0) == -1
+    assert create([lp()], B=0, n=0) == -1
+    arr = (b.LayerParams * 1)(lp())
+    assert lib.mtgr_stack_graph_create(arr, 1, P(8192), P(16384), P(4096), P(4096), P(4096), 1, T, 0.1, 1,
+                                       P(8192), 1 << 30, None) == -1  # no handle slot
+    assert lib.mtgr_stack_graph_launch(None, None) == -1
+    assert lib.mtgr_stack_graph_destroy(None) == 0
 
 
 @pytest.mark.parametrize("cfg", [1, 2])
