@@ -47,18 +47,48 @@ struct Carver {
   }
 };
 
-size_t layer_fwd_ws(int B, int64_t T, int d, int dt) {
+// Forward attention: the tile lists plus, for short batches, the fp32
+// partial sums of the key runs.
+size_t attn_fwd_ws(int B, int64_t T, int H, int dh, int dt) {
+  return align_up(attn_ws(B, T), 256) + align_up(attn_fwd_part_bytes(dt, B, T, H, dh), 256);
+}
+
+size_t layer_fwd_ws(int B, int64_t T, int d, int H, int dt) {
   const size_t e = elt(dt);
-  size_t n = align_up(attn_ws(B, T), 256);
+  size_t n = attn_fwd_ws(B, T, H, H > 0 ? d / H : 0, dt);
   n += align_up((size_t)T * d * e, 256);       // xhat, then y
   n += align_up((size_t)T * 4 * d * e, 256);   // uqkv
   n += align_up((size_t)T * d * e, 256);       // o
   return n;
 }
 
-// The layer intermediates plus one hidden-state buffer between layers.
-size_t stack_fwd_ws(int B, int64_t T, int d, int dt) {
-  return layer_fwd_ws(B, T, d, dt) + align_up((size_t)T * d * elt(dt), 256);
+// Split-K planes of the stack's output projections: used for 16-bit batches
+// whose projection has too few tiles to occupy the GPU (0: not split).
+int stack_out_planes(int64_t T, int d, int dt) {
+  if (dt == MTGR_F32 || T <= 0) return 0;
+  const int s = gemm_plane_splits((int)T, d, d);
+  return s > 1 ? s : 0;
+}
+
+// fp32 partial planes of a stack forward: the attention's key runs and the
+// output projections' split-K planes share one region.
+size_t stack_part_bytes(int B, int64_t T, int d, int H, int dt) {
+  const size_t a = attn_fwd_part_bytes(dt, B, T, H, H > 0 ? d / H : 0);
+  const size_t g = (size_t)stack_out_planes(T, d, dt) * (size_t)T * d * sizeof(float);
+  return a > g ? a : g;
+}
+
+// Tile lists, partial planes, the layer intermediates and one hidden-state
+// buffer between layers.
+size_t stack_fwd_ws(int B, int64_t T, int d, int H, int dt) {
+  const size_t e = elt(dt);
+  size_t n = align_up(attn_ws(B, T), 256);
+  n += align_up(stack_part_bytes(B, T, d, H, dt), 256);
+  n += align_up((size_t)T * d * e, 256);       // xhat, then y
+  n += align_up((size_t)T * 4 * d * e, 256);   // uqkv
+  n += align_up((size_t)T * d * e, 256);       // o
+  n += align_up((size_t)T * d * e, 256);       // h
+  return n;
 }
 
 // dS storage of the backward (bf16/f16 with a declared row bound only).
@@ -132,11 +162,11 @@ size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t max_len, int32_
     case MTGR_OP_PREP: return 0;
     case MTGR_OP_GLN_FWD: return 0;
     case MTGR_OP_GLN_BWD: return gln_bwd_workspace_bytes(T, d, kMaxG);
-    case MTGR_OP_ATTN_FWD: return attn_ws(B, T);
+    case MTGR_OP_ATTN_FWD: return H > 0 ? attn_fwd_ws(B, T, H, d / H, dt) : attn_ws(B, T);
     case MTGR_OP_ATTN_BWD: return attn_bwd_ws(B, T, max_len, H, dt);
-    case MTGR_OP_LAYER_FWD: return layer_fwd_ws(B, T, d, dt);
+    case MTGR_OP_LAYER_FWD: return layer_fwd_ws(B, T, d, H, dt);
     case MTGR_OP_LAYER_BWD: return layer_bwd_ws(B, T, max_len, d, H, dt);
-    case MTGR_OP_STACK_FWD: return stack_fwd_ws(B, T, d, dt);
+    case MTGR_OP_STACK_FWD: return stack_fwd_ws(B, T, d, H, dt);
     default: return 0;
   }
 }
@@ -203,15 +233,28 @@ int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_q
                              ws_bytes);
   if (r) return r;
   if (ld_o < (int64_t)H * dh || (T > 0 && !o) || !vec_ok(o, ld_o, dt)) return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < attn_fwd_ws(B, T, H, dh, dt)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   if (B == 0 || T == 0) return MTGR_OK;
+  Carver cv{(char*)workspace, ws_bytes};
+  void* ws_prep = cv.take(attn_ws(B, T));
+  const size_t pb = attn_fwd_part_bytes(dt, B, T, H, dh);
+  void* ws_part = pb ? cv.take(pb) : nullptr;
+  if (!cv.ok) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   PrepView pv;
-  r = launch_prep(offsets, group_ids, B, T, workspace, S(stream), &pv);
+  r = launch_prep(offsets, group_ids, B, T, ws_prep, S(stream), &pv);
   if (r) return r;
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v; a.ldqkv = ld_qkv;
   a.o = o; a.ldo = ld_o;
   a.ts = timestamps; a.B = B; a.T = T; a.H = H; a.dh = dh; a.alpha = alpha; a.scale = attn_scale;
-  return launch_attn_fwd(dt, a, pv, S(stream));
+  a.part = (float*)ws_part; a.nsplit = attn_fwd_splits(dt, B, T, H);
+  r = launch_attn_fwd(dt, a, pv, S(stream));
+  if (r || !ws_part || a.nsplit < 2) return r;
+  PartialRows pr = {};
+  pr.part = (const float*)ws_part; pr.n = a.nsplit; pr.plane = T * H * dh; pr.ldp = (int64_t)H * dh;
+  pr.xs = o; pr.ldxs = ld_o;
+  ProfScope ps("attn_fwd_sum", S(stream));
+  return launch_partial_reduce(dt, pr, T, H * dh, S(stream));
 }
 
 int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_qkv, const void* d_o,
@@ -258,19 +301,30 @@ static int layer_param_checks(const mtgr_layer_params* p, int dt) {
 }
 
 // a2..a6 of one layer on a prepared batch (the tile lists in pv); xhat,
-// uqkv and o are the layer's intermediates, y may alias xhat.
+// uqkv and o are the layer's intermediates, y may alias xhat.  part: fp32
+// partial planes for the split-key attention of short batches (the group
+// norm of a5 adds them) and, with out_planes > 0, for the output projection.
+// in_planes: when set, the layer input is the sum it describes (the previous
+// layer's projection planes plus bias and residual, stored to in_planes->xs
+// on the way) instead of x_in.  With out_planes > 0 the projection writes
+// out_planes fp32 planes of y W_o^T into part and x_out is not written: the
+// next step adds bias and residual.
 static int layer_fwd_body(const mtgr_layer_params* p, const void* x_in, void* x_out, const mtgr_layer_saved* saved,
                           const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T,
-                          float attn_scale, int dt, const PrepView& pv, void* xhat, void* uqkv, void* o, void* y,
-                          hipStream_t st) {
+                          float attn_scale, int dt, const PrepView& pv, void* part, void* xhat, void* uqkv, void* o,
+                          void* y, const PartialRows* in_planes, int out_planes, hipStream_t st) {
   const int d = p->d;
   const size_t e = elt(dt);
   int r;
   // a2: input group norm
   {
     ProfScope ps("gln1_fwd", st);
-    r = launch_gln_fwd(dt, x_in, d, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->eps,
-                       saved ? saved->mean1 : nullptr, saved ? saved->rstd1 : nullptr, nullptr, 0, st);
+    if (in_planes)
+      r = launch_gln_fwd_part(dt, *in_planes, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->eps,
+                              saved ? saved->mean1 : nullptr, saved ? saved->rstd1 : nullptr, nullptr, 0, st);
+    else
+      r = launch_gln_fwd(dt, x_in, d, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->eps,
+                         saved ? saved->mean1 : nullptr, saved ? saved->rstd1 : nullptr, nullptr, 0, st);
   }
   if (r) return r;
   // a3: [U|Q|K|V] = SiLU(xhat W^T + b)
@@ -289,20 +343,36 @@ static int layer_fwd_body(const mtgr_layer_params* p, const void* x_in, void* x_
   a.q = base + (size_t)d * e; a.k = base + (size_t)2 * d * e; a.v = base + (size_t)3 * d * e;
   a.ldqkv = 4 * d; a.o = o; a.ldo = d;
   a.ts = timestamps; a.B = B; a.T = T; a.H = p->H; a.dh = p->dh; a.alpha = p->alpha; a.scale = attn_scale;
+  a.part = (float*)part; a.nsplit = attn_fwd_splits(dt, B, T, p->H);
+  const bool attn_planes = part && a.nsplit > 1;
   r = launch_attn_fwd(dt, a, pv, st);
   if (r) return r;
-  // a5: y = GLN2(o) * U
+  // a5: y = GLN2(o) * U, o summed from the key-run planes when split (and
+  // stored only when it is kept for the backward)
   {
     ProfScope ps("gln2_gate_fwd", st);
-    r = launch_gln_fwd(dt, o, d, y, d, p->gamma2, p->beta2, group_ids, T, d, p->eps,
-                       saved ? saved->mean2 : nullptr, saved ? saved->rstd2 : nullptr, uqkv, 4 * d, st);
+    if (attn_planes) {
+      PartialRows pr = {};
+      pr.part = (const float*)part; pr.n = a.nsplit; pr.plane = T * d; pr.ldp = d;
+      pr.xs = saved ? saved->o : nullptr; pr.ldxs = d;
+      r = launch_gln_fwd_part(dt, pr, y, d, p->gamma2, p->beta2, group_ids, T, d, p->eps,
+                              saved ? saved->mean2 : nullptr, saved ? saved->rstd2 : nullptr, uqkv, 4 * d, st);
+    } else {
+      r = launch_gln_fwd(dt, o, d, y, d, p->gamma2, p->beta2, group_ids, T, d, p->eps,
+                         saved ? saved->mean2 : nullptr, saved ? saved->rstd2 : nullptr, uqkv, 4 * d, st);
+    }
   }
   if (r) return r;
   // a6: x_out = x + y W_o^T + b_o
   GemmEpiArgs eo = {};
+  ProfScope ps("gemm_out_resid", st);
+  if (out_planes > 0) {
+    eo.kind = EPI_F32_PLANES;
+    eo.C = part; eo.ldc = d; eo.plane = T * d;
+    return launch_gemm(dt, y, d, true, p->W_o, d, true, (int)T, d, d, eo, out_planes, st);
+  }
   eo.kind = EPI_BIAS_RESID;
   eo.C = x_out; eo.ldc = d; eo.bias = p->b_o; eo.R = x_in; eo.ldr = d;
-  ProfScope ps("gemm_out_resid", st);
   return launch_gemm(dt, y, d, true, p->W_o, d, true, (int)T, d, d, eo, 1, st);
 }
 
@@ -320,12 +390,14 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
   if (saved && (!saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->z || !saved->uqkv || !saved->o ||
                 !saved->mean2 || !saved->rstd2 || !saved->y))
     return MTGR_ERR_INVALID_ARG;
-  if (ws_bytes < layer_fwd_ws(B, T, d, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < layer_fwd_ws(B, T, d, p->H, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   if (T == 0 || B == 0) return MTGR_OK;
   hipStream_t st = S(stream);
   const size_t e = elt(dt);
   Carver cv{(char*)workspace, ws_bytes};
   void* ws_prep = cv.take(attn_ws(B, T));
+  const size_t pb = attn_fwd_part_bytes(dt, B, T, p->H, p->dh);
+  void* ws_part = pb ? cv.take(pb) : nullptr;
   void* ws_xhat = cv.take((size_t)T * d * e);
   void* ws_uqkv = cv.take((size_t)T * 4 * d * e);
   void* ws_o = cv.take((size_t)T * d * e);
@@ -340,8 +412,8 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
     r = launch_prep(offsets, group_ids, B, T, ws_prep, st, &pv);
   }
   if (r) return r;
-  return layer_fwd_body(p, x_in, x_out, saved, group_ids, timestamps, B, T, attn_scale, dt, pv, xhat, uqkv, o, y,
-                        st);
+  return layer_fwd_body(p, x_in, x_out, saved, group_ids, timestamps, B, T, attn_scale, dt, pv, ws_part, xhat, uqkv,
+                        o, y, nullptr, 0, st);
 }
 
 }  // extern "C"
@@ -363,7 +435,8 @@ int stack_fwd_validate(const mtgr_layer_params* layers, int32_t L, const void* x
   if (T > 0 && (!x_in || !x_out)) return MTGR_ERR_INVALID_ARG;
   if (x_in == x_out && T > 0) return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(x_in, d, dt) || !vec_ok(x_out, d, dt)) return MTGR_ERR_INVALID_ARG;
-  if (ws_bytes < stack_fwd_ws(B, T, d, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < stack_fwd_ws(B, T, d, layers[0].H, dt) || (T > 0 && !workspace))
+    return MTGR_ERR_WORKSPACE_TOO_SMALL;
   return MTGR_OK;
 }
 
@@ -381,8 +454,11 @@ int mtgr_hstu_stack_fwd(const mtgr_layer_params* layers, int32_t L, const void* 
   const int d = layers[0].d;
   hipStream_t st = S(stream);
   const size_t e = elt(dt);
+  const int H = layers[0].H;
   Carver cv{(char*)workspace, ws_bytes};
   void* ws_prep = cv.take(attn_ws(B, T));
+  const size_t pb = stack_part_bytes(B, T, d, H, dt);
+  void* ws_part = pb ? cv.take(pb) : nullptr;
   void* xhat = cv.take((size_t)T * d * e);
   void* uqkv = cv.take((size_t)T * 4 * d * e);
   void* o = cv.take((size_t)T * d * e);
@@ -394,13 +470,36 @@ int mtgr_hstu_stack_fwd(const mtgr_layer_params* layers, int32_t L, const void* 
     r = launch_prep(offsets, group_ids, B, T, ws_prep, st, &pv);
   }
   if (r) return r;
+  const int so = stack_out_planes(T, d, dt);
+  if (so > 0) {
+    // Short batches: each output projection leaves so fp32 planes; the next
+    // layer's input norm (or the final sum) adds them with bias and
+    // residual and stores the new residual stream in x_out (in place from
+    // the second layer on).
+    PartialRows pr = {};
+    pr.part = (const float*)ws_part; pr.n = so; pr.plane = T * d; pr.ldp = d;
+    pr.ldr = d; pr.xs = x_out; pr.ldxs = d;
+    for (int l = 0; l < L; ++l) {
+      if (l > 0) {
+        pr.bias = layers[l - 1].b_o;
+        pr.resid = l == 1 ? x_in : x_out;
+      }
+      r = layer_fwd_body(&layers[l], x_in, nullptr, nullptr, group_ids, timestamps, B, T, attn_scale, dt, pv, ws_part,
+                         xhat, uqkv, o, xhat, l > 0 ? &pr : nullptr, so, st);
+      if (r) return r;
+    }
+    pr.bias = layers[L - 1].b_o;
+    pr.resid = L == 1 ? x_in : x_out;
+    ProfScope ps("out_sum", st);
+    return launch_partial_reduce(dt, pr, T, d, st);
+  }
   // Layer l writes x_out when L-1-l is even and the spare buffer h otherwise,
   // so consecutive layers alternate and the last one lands in x_out.
   const void* src = x_in;
   for (int l = 0; l < L; ++l) {
     void* dst = ((L - 1 - l) % 2 == 0) ? x_out : h;
-    r = layer_fwd_body(&layers[l], src, dst, nullptr, group_ids, timestamps, B, T, attn_scale, dt, pv, xhat, uqkv,
-                       o, xhat, st);
+    r = layer_fwd_body(&layers[l], src, dst, nullptr, group_ids, timestamps, B, T, attn_scale, dt, pv, ws_part, xhat,
+                       uqkv, o, xhat, nullptr, 0, st);
     if (r) return r;
     src = dst;
   }

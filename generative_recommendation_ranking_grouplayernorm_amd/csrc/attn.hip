@@ -385,12 +385,17 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt,
   pipeline_lds_mfma<DH / 8, 8>();
 }
 
+// With nsplit > 1 (short batches), the key tiles of each (query tile, head)
+// are shared out in nsplit contiguous runs, one workgroup each: workgroup
+// L = split * base + L'.  Each writes its scaled fp32 partial sum to
+// part[split][row][col] (rows of its query tile, zeros when its run is
+// empty); the consumer of O adds the planes in split order.
 template <typename T, int DH>
 __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t ldqkv, uint16_t* __restrict__ O, int64_t ldo, const int32_t* __restrict__ seg,
     const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-    int H, float kexp, float out_scale) {
+    int H, float kexp, float out_scale, int nsplit, int base, float* __restrict__ part, int64_t T_rows) {
   constexpr int KP = AttnPitch<DH>::B128;
   constexpr int NS = DH / 16, NC = DH / 32;
   struct Smem {
@@ -405,8 +410,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   auto& Ks = sm.m.Ks;
   auto& Vt = sm.m.Vt;
   auto& Tk = sm.m.Tk;
-  int tile, h;
-  xcd_tile_head(blockIdx.x, H, tile, h);
+  int tile, h, split = 0, L = blockIdx.x;
+  if (nsplit > 1) {
+    split = L / base;
+    L -= split * base;
+  }
+  xcd_tile_head(L, H, tile, h);
   if (tile >= *ntiles) return;
   const int2 te = tiles[tile];
   const int b = te.x, q0 = te.y;
@@ -437,6 +446,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   VtLoad<DH> rv;
   int64_t rt = 0;
   const int nkt = (kv_end - lo + F_BK - 1) / F_BK;
+  // this workgroup's run of key tiles [it0, it1)
+  int it0 = 0, it1 = nkt;
+  if (nsplit > 1) {
+    const int per = (nkt + nsplit - 1) / nsplit;
+    it0 = min(nkt, split * per);
+    it1 = min(nkt, it0 + per);
+  }
   // leading tiles made only of U/S keys need no mask test
   const int nfull = min(nkt, max(0, (s_end - lo) / F_BK));
   auto gload = [&](int k0) {
@@ -449,26 +465,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
     vt_swrite<DH>(Vt[buf], rv);
     if (wave == 0) Tk[buf][lane] = rt;
   };
-  if (nkt > 0) {
-    gload(lo);
+  if (it0 < it1) {
+    gload(lo + it0 * F_BK);
     swrite(0);
   }
   __syncthreads();
-  for (int it = 0; it < nfull; ++it) {
-    const int buf = it & 1, k0 = lo + it * F_BK;
-    const bool more = it + 1 < nkt;
+  const int mid = max(it0, min(it1, nfull));
+  for (int it = it0; it < mid; ++it) {
+    const int buf = (it - it0) & 1, k0 = lo + it * F_BK;
+    const bool more = it + 1 < it1;
     if (more) gload(k0 + F_BK);
     fwd_tile<T, DH, false>(Ks[buf], Vt[buf], Tk[buf], qop, oacc, k0, qi, tq, s_end, r_end, kexp, lane);
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
-  for (int it = nfull; it < nkt; ++it) {
-    const int buf = it & 1, k0 = lo + it * F_BK;
-    const bool more = it + 1 < nkt;
+  for (int it = mid; it < it1; ++it) {
+    const int buf = (it - it0) & 1, k0 = lo + it * F_BK;
+    const bool more = it + 1 < it1;
     if (more) gload(k0 + F_BK);
     fwd_tile<T, DH, true>(Ks[buf], Vt[buf], Tk[buf], qop, oacc, k0, qi, tq, s_end, r_end, kexp, lane);
     if (more) swrite(buf ^ 1);
     __syncthreads();
+  }
+  if (nsplit > 1) {
+    // fp32 partial: accumulator element (c, j) is column 32 c + l32 of row
+    // 8 (j / 4) + 4 g + j % 4 of the wave's 32 rows
+    float* pp = part + (int64_t)split * T_rows * (H * DH) + hc;
+    const int r0 = q0 + wave * 32;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = r0 + 8 * (j >> 2) + 4 * g + (j & 3);
+      if (row < hi) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) pp[(int64_t)row * (H * DH) + 32 * c + l32] = oacc[c][j] * out_scale;
+      }
+    }
+    return;
   }
   wave_store_rows<T, NC>(sm.ep + wave * EP_FLOATS, oacc, 0, lane, q0 + wave * 32, hi, out_scale, O, ldo, hc,
                          nullptr, 0);
@@ -1183,10 +1215,28 @@ static void fwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
   // SiLU(alpha s) = alpha * s * sigmoid(alpha s); sigmoid via exp2 with the
   // factor -alpha*log2(e) folded in; alpha and the normaliser scale O once.
   const float kexp = -a.alpha * 1.4426950408889634f;
-  ProfScope ps("attn_fwd", st);
-  hipLaunchKernelGGL((attn_fwd_mfma<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(256), 0, st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (uint16_t*)a.o,
-                     a.ldo, pv.seg, a.ts, pv.q.tiles, pv.q.ntiles, a.H, kexp, a.alpha * a.scale);
+  const unsigned base = xcd_grid(pv.q.max_tiles, a.H);
+  const int ns = a.part ? a.nsplit : 1;
+  {
+    ProfScope ps("attn_fwd", st);
+    hipLaunchKernelGGL((attn_fwd_mfma<T, DH>), dim3(base * ns), dim3(256), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (uint16_t*)a.o, a.ldo, pv.seg, a.ts,
+                       pv.q.tiles, pv.q.ntiles, a.H, kexp, a.alpha * a.scale, ns, (int)base, a.part, a.T);
+  }
+}
+
+int attn_fwd_splits(int dt, int B, int64_t T, int H) {
+  if (dt == MTGR_F32 || B <= 0 || T <= 0) return 1;
+  // two forward workgroups fit on each of the 256 compute units
+  const int64_t wgs = (int64_t)xcd_grid(max_tiles(B, T, ATTN_QTILE), H);
+  if (wgs >= 512) return 1;
+  const int64_t s = (512 + wgs - 1) / wgs;
+  return (int)(s < ATTN_MAX_SPLITS ? s : ATTN_MAX_SPLITS);
+}
+
+size_t attn_fwd_part_bytes(int dt, int B, int64_t T, int H, int dh) {
+  const int s = attn_fwd_splits(dt, B, T, H);
+  return s > 1 ? (size_t)s * (size_t)T * (size_t)H * dh * sizeof(float) : 0;
 }
 
 template <typename T, int DH>

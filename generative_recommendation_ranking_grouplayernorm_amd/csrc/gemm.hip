@@ -4,8 +4,9 @@
 // backward products (data gradients and fp32 weight gradients).
 //
 // bf16 / f16: 256x256 output tile per 512-thread workgroup, 8 waves in 2x4,
-// each wave 128x64 = 4x2 MFMA 32x32x16 tiles; K staged through LDS 64 deep,
-// double-buffered, one barrier per K step.  Operands stored K-contiguous are
+// each wave 128x64 = 4x2 MFMA 32x32x16 tiles (128x128 tiles of 4 waves for
+// short batches); K staged through LDS 64 deep, double-buffered, one barrier
+// per K step.  Operands stored K-contiguous are
 // read with 16-byte LDS loads; operands stored M/N-contiguous (the transposed
 // products of the backward) are read with gfx950's LDS transpose load, so no
 // operand is ever transposed in memory.
@@ -96,17 +97,43 @@ __device__ __forceinline__ void epi_apply(const GemmEpiArgs& ep, int m, int n, f
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel: 256 x 256 output tile, 512 threads = 8 waves as 2 (M) x 4 (N),
-// each wave 128 x 64 = 4 x 2 MFMA 32x32x16 tiles; K staged 64 deep through
-// LDS, double-buffered with register prefetch, one barrier per K step.
-// Global reads are buffer loads whose range check zero-fills rows past the
-// matrix edge; advancing a K step changes only scalar registers.
+// MFMA kernel.  Output tile BM x BN per workgroup of WAVES_M x WAVES_N waves,
+// each wave TM x TN MFMA 32x32x16 tiles; K staged 64 deep through LDS,
+// double-buffered with register prefetch, one barrier per K step.  Global
+// reads are buffer loads whose range check zero-fills rows past the matrix
+// edge; advancing a K step changes only scalar registers.
+//   large: 256 x 256, 8 waves as 2 x 4, 128 x 64 per wave (every batch of
+//          more than a few thousand rows);
+//   small: 128 x 128, 4 waves as 2 x 2, 64 x 64 per wave, two workgroups per
+//          compute unit (forward products of short batches, such as one
+//          serving request, where the large tiles would leave most compute
+//          units idle).  With few workgroups per unit the load latency is
+//          what shows, so the small tiles keep two K steps of global loads
+//          in flight (two register sets, the K loop unrolled by two).
 // ---------------------------------------------------------------------------
-constexpr int G_BM = 256, G_BN = 256, G_BK = 64;
-constexpr int G_KC_PITCH = G_BK + 8;    // K-contiguous tile [256][72]
-constexpr int G_MN_PITCH = G_BM + 16;   // M/N-contiguous tile [64][272]
-constexpr int G_TILE_ELEMS = G_BM * G_KC_PITCH;  // >= G_BK * G_MN_PITCH
-static_assert(G_BK * G_MN_PITCH <= G_TILE_ELEMS, "tile size");
+constexpr int G_BK = 64;
+constexpr int G_KC_PITCH = G_BK + 8;  // K-contiguous rows: 64 + 8 halves
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int MIN_BLOCKS_, bool DEEP_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, MIN_BLOCKS = MIN_BLOCKS_;
+  static constexpr bool DEEP = DEEP_;  // two K steps of loads in flight
+  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int TM = BM / WAVES_M / 32, TN = BN / WAVES_N / 32;
+};
+using GemmLarge = GemmCfg<256, 256, 2, 4, 1, false>;
+using GemmSmall = GemmCfg<128, 128, 2, 2, 2, true>;
+
+// LDS tile of one operand with ROWS rows (its M or N extent).  K-contiguous:
+// [ROWS][72]; M/N-contiguous: [64][ROWS + 16].  Both layouts get the larger
+// of the two sizes so that A and B sit at fixed offsets.
+template <int ROWS>
+struct GTile {
+  static constexpr int KC_ELEMS = ROWS * G_KC_PITCH;
+  static constexpr int MN_PITCH = ROWS + 16;
+  static constexpr int MN_ELEMS = G_BK * MN_PITCH;
+  static constexpr int ELEMS = KC_ELEMS > MN_ELEMS ? KC_ELEMS : MN_ELEMS;
+};
 
 // Buffer resource over one operand's K step.  K-contiguous: rows r0.. (the
 // M or N index), columns k0..; M/N-contiguous: rows k0.. (the K index),
@@ -118,53 +145,57 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const uint16_t* P, i
   return make_rsrc(P + (int64_t)k0 * ld + r0, (int)((int64_t)(kend - k0) * ld * 2 - (int64_t)r0 * 2));
 }
 
-template <bool KC>
+// 16-byte chunk c of a K step: K-contiguous, 8 chunks per row of 64;
+// M/N-contiguous, ROWS / 8 chunks per K row.
+template <bool KC, int ROWS>
 __device__ __forceinline__ int gemm_voff(int64_t ld, int c) {
-  if (KC) return ((c >> 3) * (int)ld + (c & 7) * 8) * 2;
-  return ((c >> 5) * (int)ld + (c & 31) * 8) * 2;
+  constexpr int CPR = KC ? 8 : ROWS / 8;
+  return ((c / CPR) * (int)ld + (c % CPR) * 8) * 2;
 }
 
-template <bool KC>
+template <bool KC, int ROWS>
 __device__ __forceinline__ void gemm_swrite(uint16_t* s, int c, uint4 v) {
-  if (KC) *(uint4*)(s + (c >> 3) * G_KC_PITCH + (c & 7) * 8) = v;
-  else *(uint4*)(s + (c >> 5) * G_MN_PITCH + (c & 31) * 8) = v;
+  constexpr int CPR = KC ? 8 : ROWS / 8;
+  constexpr int PITCH = KC ? G_KC_PITCH : GTile<ROWS>::MN_PITCH;
+  *(uint4*)(s + (c / CPR) * PITCH + (c % CPR) * 8) = v;
 }
 
 // MFMA operand for 32 rows starting at r0 (within the tile), k-step ks.
-template <bool KC>
+template <bool KC, int ROWS>
 __device__ __forceinline__ op8 gemm_operand(const uint16_t* s, int r0, int ks, int lane) {
   op8 o;
   if (KC) {
     const int row = r0 + (lane & 31), kk = ks * 16 + 8 * (lane >> 5);
     o.v = *(const u32x4_t*)(s + row * G_KC_PITCH + kk);
   } else {
+    constexpr int PITCH = GTile<ROWS>::MN_PITCH;
     const int G = lane >> 4, i = lane & 15;
     const int kr = ks * 16 + 8 * (G >> 1) + (i >> 2);
     const int col = r0 + 16 * (G & 1) + 4 * (i & 3);
-    uint2 lo = lds_read_tr16(s + kr * G_MN_PITCH + col);
-    uint2 hi = lds_read_tr16(s + (kr + 4) * G_MN_PITCH + col);
+    uint2 lo = lds_read_tr16(s + kr * PITCH + col);
+    uint2 hi = lds_read_tr16(s + (kr + 4) * PITCH + col);
     o.v[0] = lo.x; o.v[1] = lo.y; o.v[2] = hi.x; o.v[3] = hi.y;
   }
   return o;
 }
 
-// Scheduling hint for one K step (four 16-deep slices, eight MFMAs each, R
+// Scheduling hint for one K step (four 16-deep slices of NM MFMAs each, R
 // LDS reads feeding each slice): the reads of slice s + 1 are spread between
 // the MFMAs of slice s, so that operands arrive before they are needed.
-template <int R, int I>
+template <int R, int NM, int I>
 __device__ __forceinline__ void gemm_pipeline_slot() {
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA I of the slice
-  constexpr int n = (R * (I + 1)) / 8 - (R * I) / 8;
+  constexpr int n = (R * (I + 1)) / NM - (R * I) / NM;
   if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // DS reads
-  if constexpr (I + 1 < 8) gemm_pipeline_slot<R, I + 1>();
+  if constexpr (I + 1 < NM) gemm_pipeline_slot<R, NM, I + 1>();
 }
-template <int R>
+template <int R, int NM>
 __device__ __forceinline__ void gemm_pipeline() {
   __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // DS reads of slice 0
-  gemm_pipeline_slot<R, 0>();
-  gemm_pipeline_slot<R, 0>();
-  gemm_pipeline_slot<R, 0>();
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  gemm_pipeline_slot<R, NM, 0>();
+  gemm_pipeline_slot<R, NM, 0>();
+  gemm_pipeline_slot<R, NM, 0>();
+  __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
 }
 
 // Workgroup L -> (row job, N tile).  Workgroups run round-robin on the 8
@@ -177,99 +208,133 @@ __device__ __forceinline__ bool gemm_tile_of(int L, int NT, int R, int& rr, int&
   return rr < R;
 }
 
-template <typename T, bool AK, bool BKC, int EPI>
-__global__ __launch_bounds__(512, 1) void gemm_mfma_kernel(const uint16_t* __restrict__ A, int64_t lda,
-                                                           const uint16_t* __restrict__ B, int64_t ldb,
-                                                           int M, int N, int K, int k_per_split, int MT,
-                                                           int NT, int R, GemmEpiArgs ep) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2 * G_TILE_ELEMS];
+template <typename T, bool AK, bool BKC, int EPI, typename C>
+__global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb, int M, int N, int K,
+    int k_per_split, int MT, int NT, int R, GemmEpiArgs ep) {
+  constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, NTH = C::THREADS;
+  constexpr int A_ELEMS = GTile<BM>::ELEMS, B_ELEMS = GTile<BN>::ELEMS;
+  constexpr int A_LOADS = BM * G_BK / 8 / NTH, B_LOADS = BN * G_BK / 8 / NTH;
+  static_assert(A_LOADS * NTH * 8 == BM * G_BK && B_LOADS * NTH * 8 == BN * G_BK, "load split");
+  static_assert(TN == 2 && TM % 2 == 0, "epilogue stages 64 x 64 blocks");
+  static_assert((NTH / 64) * 64 * G_EPI_PITCH * 4 <= 2 * (A_ELEMS + B_ELEMS) * 2, "epilogue staging fits");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][A_ELEMS + B_ELEMS];
   int rr, nt;
   if (!gemm_tile_of(blockIdx.x, NT, R, rr, nt)) return;
   const int mt = rr % MT, split = rr / MT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int m0 = mt * G_BM, n0 = nt * G_BN;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int m0 = mt * BM, n0 = nt * BN;
   const int kbeg = split * k_per_split;
   const int kend = min(K, kbeg + k_per_split);
   const int nk = kend > kbeg ? (kend - kbeg + G_BK - 1) / G_BK : 0;
   if (EPI == EPI_F32_ATOMIC && nk == 0) return;
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[TM][TN];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < TM; ++t)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < TN; ++u)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[t][u][j] = 0.f;
 
-  int va[4], vb[4];
+  int va[A_LOADS], vb[B_LOADS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    va[i] = gemm_voff<AK>(lda, tid + 512 * i);
-    vb[i] = gemm_voff<BKC>(ldb, tid + 512 * i);
-  }
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
+  for (int i = 0; i < A_LOADS; ++i) va[i] = gemm_voff<AK, BM>(lda, tid + NTH * i);
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) vb[i] = gemm_voff<BKC, BN>(ldb, tid + NTH * i);
+  auto mma = [&](const uint16_t* sa, const uint16_t* sb) {
+#pragma unroll
+    for (int ks = 0; ks < G_BK / 16; ++ks) {
+      op8 a[TM], b[TN];
+#pragma unroll
+      for (int t = 0; t < TM; ++t) a[t] = gemm_operand<AK, BM>(sa, wm * (TM * 32) + t * 32, ks, lane);
+#pragma unroll
+      for (int u = 0; u < TN; ++u) b[u] = gemm_operand<BKC, BN>(sb, wn * (TN * 32) + u * 32, ks, lane);
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int u = 0; u < TN; ++u) acc[t][u] = mfma32<T>(a[t], b[u], acc[t][u]);
+    }
+    gemm_pipeline<TM * (AK ? 1 : 2) + TN * (BKC ? 1 : 2), TM * TN>();
+  };
+  auto gload_to = [&](uint4 (&ra)[A_LOADS], uint4 (&rb)[B_LOADS], int k0) {
     const __amdgpu_buffer_rsrc_t sa = gemm_rsrc<AK>(A, lda, m0, M, k0, kend);
     const __amdgpu_buffer_rsrc_t sb = gemm_rsrc<BKC>(B, ldb, n0, N, k0, kend);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = buf_load16(sa, va[i]);
-      rb[i] = buf_load16(sb, vb[i]);
-    }
+    for (int i = 0; i < A_LOADS; ++i) ra[i] = buf_load16(sa, va[i]);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) rb[i] = buf_load16(sb, vb[i]);
   };
-  auto swrite = [&](int buf) {
+  auto swrite_from = [&](const uint4 (&ra)[A_LOADS], const uint4 (&rb)[B_LOADS], int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gemm_swrite<AK>(smem[buf], tid + 512 * i, ra[i]);
-      gemm_swrite<BKC>(smem[buf] + G_TILE_ELEMS, tid + 512 * i, rb[i]);
-    }
+    for (int i = 0; i < A_LOADS; ++i) gemm_swrite<AK, BM>(smem[buf], tid + NTH * i, ra[i]);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) gemm_swrite<BKC, BN>(smem[buf] + A_ELEMS, tid + NTH * i, rb[i]);
   };
-  if (nk > 0) {
-    gload(kbeg);
-    swrite(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < nk;
-    if (more) gload(kbeg + (it + 1) * G_BK);
-    const uint16_t* sa = smem[buf];
-    const uint16_t* sb = smem[buf] + G_TILE_ELEMS;
-#pragma unroll
-    for (int ks = 0; ks < G_BK / 16; ++ks) {
-      op8 a[4], b[2];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) a[t] = gemm_operand<AK>(sa, wm * 128 + t * 32, ks, lane);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) b[u] = gemm_operand<BKC>(sb, wn * 64 + u * 32, ks, lane);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) acc[t][u] = mfma32<T>(a[t], b[u], acc[t][u]);
+  if constexpr (C::DEEP) {
+    // Data of K step j travels in register set j % 2 and LDS buffer j % 2;
+    // its loads are issued two steps ahead.  Prefetches past the last step
+    // re-read the last step (in bounds) and are never written to LDS.
+    uint4 ra0[A_LOADS], rb0[B_LOADS], ra1[A_LOADS], rb1[B_LOADS];
+    const int klast = kbeg + (nk - 1) * G_BK;
+    auto kat = [&](int j) { return min(kbeg + j * G_BK, klast); };
+    if (nk > 0) {
+      gload_to(ra0, rb0, kat(0));
+      gload_to(ra1, rb1, kat(1));
+      swrite_from(ra0, rb0, 0);
+      gload_to(ra0, rb0, kat(2));
     }
-    gemm_pipeline<4 * (AK ? 1 : 2) + 2 * (BKC ? 1 : 2)>();
-    if (more) swrite(buf ^ 1);
     __syncthreads();
+    for (int it = 0; it < nk; it += 2) {
+      mma(smem[0], smem[0] + A_ELEMS);
+      if (it + 1 < nk) swrite_from(ra1, rb1, 1);
+      gload_to(ra1, rb1, kat(it + 3));
+      __syncthreads();
+      if (it + 1 >= nk) break;
+      mma(smem[1], smem[1] + A_ELEMS);
+      if (it + 2 < nk) swrite_from(ra0, rb0, 0);
+      gload_to(ra0, rb0, kat(it + 4));
+      __syncthreads();
+    }
+  } else {
+    uint4 ra[A_LOADS], rb[B_LOADS];
+    if (nk > 0) {
+      gload_to(ra, rb, kbeg);
+      swrite_from(ra, rb, 0);
+    }
+    __syncthreads();
+    for (int it = 0; it < nk; ++it) {
+      const int buf = it & 1;
+      const bool more = it + 1 < nk;
+      if (more) gload_to(ra, rb, kbeg + (it + 1) * G_BK);
+      mma(smem[buf], smem[buf] + A_ELEMS);
+      if (more) swrite_from(ra, rb, buf ^ 1);
+      __syncthreads();
+    }
   }
-  if constexpr (EPI == EPI_F32_STORE || EPI == EPI_F32_ATOMIC) {
+  if constexpr (EPI == EPI_F32_STORE || EPI == EPI_F32_ATOMIC || EPI == EPI_F32_PLANES) {
+    float* planeC = (float*)ep.C + (EPI == EPI_F32_PLANES ? (int64_t)split * ep.plane : 0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TM; ++t)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < TN; ++u)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int m = m0 + wm * 128 + t * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-          const int n = n0 + wn * 64 + u * 32 + (lane & 31);
-          if (m < M && n < N) epi_apply<T, EPI>(ep, m, n, acc[t][u][j]);
+          const int m = m0 + wm * (TM * 32) + t * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+          const int n = n0 + wn * (TN * 32) + u * 32 + (lane & 31);
+          if (m < M && n < N) {
+            if (EPI == EPI_F32_PLANES) planeC[(int64_t)m * ep.ldc + n] = acc[t][u][j];
+            else epi_apply<T, EPI>(ep, m, n, acc[t][u][j]);
+          }
         }
   } else {
     // 16-bit outputs: stage each wave's tile through its own LDS region (64
     // rows at a time, fp32) and write whole 128-byte row segments.
     float* st = (float*)&smem[0][0] + wave * (64 * G_EPI_PITCH);
-    const int wr0 = m0 + wm * 128, wc0 = n0 + wn * 64;
+    const int wr0 = m0 + wm * (TM * 32), wc0 = n0 + wn * (TN * 32);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < TM / 2; ++half) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -328,16 +393,34 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(const T* __restrict__ 
   if (m < M && n < N) epi_apply<T, EPI>(ep, m, n, acc);
 }
 
+template <typename T, bool AK, bool BKC, int EPI, typename C>
+static void gemm_launch_cfg(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, int kps,
+                            int splits, const GemmEpiArgs& ep, hipStream_t st) {
+  const int MT = (M + C::BM - 1) / C::BM, NT = (N + C::BN - 1) / C::BN, R = MT * splits;
+  const unsigned grid = (unsigned)((R + 7) / 8 * 8 * NT);
+  hipLaunchKernelGGL((gemm_mfma_kernel<T, AK, BKC, EPI, C>), dim3(grid), dim3(C::THREADS), 0, st,
+                     (const uint16_t*)A, lda, (const uint16_t*)B, ldb, M, N, K, kps, MT, NT, R, ep);
+}
+
+// Products whose large-tile grid would not give every compute unit a
+// workgroup use the small tiles (only the forward layout, both operands
+// K-contiguous, has them).
+constexpr int G_SMALL_BELOW = 256;
+
 template <typename T, bool AK, bool BKC, int EPI>
 static void gemm_launch_t(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K,
                           int splits, const GemmEpiArgs& ep, hipStream_t st) {
   int kps = (K + splits - 1) / splits;
   if constexpr (sizeof(T) == 2) {
     kps = (kps + G_BK - 1) / G_BK * G_BK;
-    const int MT = (M + G_BM - 1) / G_BM, NT = (N + G_BN - 1) / G_BN, R = MT * splits;
-    const unsigned grid = (unsigned)((R + 7) / 8 * 8 * NT);
-    hipLaunchKernelGGL((gemm_mfma_kernel<T, AK, BKC, EPI>), dim3(grid), dim3(512), 0, st, (const uint16_t*)A,
-                       lda, (const uint16_t*)B, ldb, M, N, K, kps, MT, NT, R, ep);
+    const int64_t large = (int64_t)((M + 255) / 256) * ((N + 255) / 256) * splits;
+    if constexpr (AK && BKC) {
+      if (large < G_SMALL_BELOW) {
+        gemm_launch_cfg<T, AK, BKC, EPI, GemmSmall>(A, lda, B, ldb, M, N, K, kps, splits, ep, st);
+        return;
+      }
+    }
+    gemm_launch_cfg<T, AK, BKC, EPI, GemmLarge>(A, lda, B, ldb, M, N, K, kps, splits, ep, st);
   } else {
     dim3 grid((N + 15) / 16, (M + 15) / 16, splits);
     hipLaunchKernelGGL((gemm_simple_kernel<T, AK, BKC, EPI>), grid, dim3(256), 0, st, (const T*)A, lda,
@@ -362,8 +445,18 @@ static void gemm_launch_epi(const void* A, int64_t lda, bool ak, const void* B, 
     case EPI_BIAS_SILU: gemm_launch_layout<T, EPI_BIAS_SILU>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
     case EPI_BIAS_RESID: gemm_launch_layout<T, EPI_BIAS_RESID>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
     case EPI_F32_STORE: gemm_launch_layout<T, EPI_F32_STORE>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
+    case EPI_F32_PLANES: gemm_launch_layout<T, EPI_F32_PLANES>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
     default: gemm_launch_layout<T, EPI_F32_ATOMIC>(A, lda, ak, B, ldb, bk, M, N, K, splits, ep, st); break;
   }
+}
+
+int gemm_plane_splits(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  int s = (int)((256 + tiles - 1) / tiles);
+  const int maxs = K / (2 * G_BK);
+  if (s > maxs) s = maxs;
+  if (s > 4) s = 4;
+  return s < 1 ? 1 : s;
 }
 
 int launch_gemm(int dt, const void* A, int64_t lda, bool a_kcontig, const void* B, int64_t ldb,

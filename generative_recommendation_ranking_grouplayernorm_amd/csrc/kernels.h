@@ -58,6 +58,23 @@ int launch_seg_only(const int32_t* offsets, const uint8_t* group_ids, int B, int
 int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,
                    const void* beta, const uint8_t* g, int64_t T, int d, float eps, float* mean,
                    float* rstd, const void* u, int64_t ldu, hipStream_t stream);
+// Row inputs given as fp32 partial sums (split-K products, split-key
+// attention): x[row, col] = round_T(sum_{s < n} part[s * plane + row * ldp +
+// col] (+ bias[col]) (+ resid[row * ldr + col])), the planes added in order,
+// then the bias, then the residual.  When xs is set, x is also stored there
+// (xs may alias resid: each element is read before it is written, by the
+// same thread).
+struct PartialRows {
+  const float* part; int n; int64_t plane; int64_t ldp;
+  const void* bias; const void* resid; int64_t ldr;
+  void* xs; int64_t ldxs;
+};
+// launch_gln_fwd with x taken from partial sums.
+int launch_gln_fwd_part(int dt, const PartialRows& in, void* y, int64_t ldy, const void* gamma, const void* beta,
+                        const uint8_t* g, int64_t T, int d, float eps, float* mean, float* rstd, const void* u,
+                        int64_t ldu, hipStream_t stream);
+// Only the sum: xs = x (in.xs must be set).
+int launch_partial_reduce(int dt, const PartialRows& in, int64_t T, int d, hipStream_t stream);
 // Backward.  Plain: dx = GLN'(dy) [+ resid].  Gate (u != NULL): the forward
 // was y = GLN(x) * u, so du = dy * GLN(x) [* SiLU'(zu) if zu != NULL] and
 // dx = GLN'(dy * u).  dgamma/dbeta fp32 [G, d] overwritten.
@@ -78,7 +95,8 @@ enum GemmEpi {
   EPI_BIAS_SILU = 1,   // z = acc + bias; Z = z (if given); C = SiLU(z)
   EPI_BIAS_RESID = 2,  // C = acc + bias + R
   EPI_F32_STORE = 3,   // Cf = acc (fp32)
-  EPI_F32_ATOMIC = 4   // Cf += acc (fp32, for split-K)
+  EPI_F32_ATOMIC = 4,  // Cf += acc (fp32, for split-K)
+  EPI_F32_PLANES = 5   // Cf[split * plane + m * ldc + n] = acc (split-K, one fp32 plane per split)
 };
 struct GemmEpiArgs {
   int kind;
@@ -89,7 +107,11 @@ struct GemmEpiArgs {
   int64_t ldz;
   const void* R;     // residual (EPI_BIAS_RESID)
   int64_t ldr;
+  int64_t plane;     // elements between split planes (EPI_F32_PLANES)
 };
+// K splits for an EPI_F32_PLANES product of short batches: enough 128 x 128
+// tile jobs for one per compute unit, each at least two K steps deep.
+int gemm_plane_splits(int M, int N, int K);
 int launch_gemm(int dt, const void* A, int64_t lda, bool a_kcontig, const void* B, int64_t ldb,
                 bool b_kcontig, int M, int N, int K, const GemmEpiArgs& ep, int splits,
                 hipStream_t stream);
@@ -118,7 +140,17 @@ struct AttnArgs {
   // 16-bit types).  When set, the dK/dV kernel stores dS there and dQ
   // streams it; when NULL, dQ recomputes S and dA.
   void* ds; int64_t ds_cap;
+  // forward only: fp32 partial sums of nsplit key runs ([nsplit][T][H dh],
+  // O itself is then not written: the caller adds the planes), or NULL for
+  // one workgroup per (query tile, head) writing O
+  float* part; int nsplit;
 };
+// Key runs per (query tile, head) of the 16-bit forward: more than one only
+// when the batch has too few query tiles to give every compute unit two
+// workgroups.  attn_fwd_part_bytes: the partial-sum storage that needs.
+constexpr int ATTN_MAX_SPLITS = 4;
+int attn_fwd_splits(int dt, int B, int64_t T, int H);
+size_t attn_fwd_part_bytes(int dt, int B, int64_t T, int H, int dh);
 // Bytes of dS storage that a batch of B rows, T tokens and rows of at most
 // max_len tokens can need: H * 32 KB per 128 x 128 tile pair, with
 // sum_b ceil(L_b / 128)^2 <= min(B ceil(M / 128)^2, (M T + 254 T + 16129 B) / 16384).

@@ -74,11 +74,43 @@ template <> struct Chunk8<float> {
 // ---- forward ---------------------------------------------------------------
 // NCH = number of 512-column chunks a lane covers (lane owns columns
 // lane*8 + 512*i .. +7).
-template <typename T, int NCH, bool GATE>
+// Sum of partial planes (+ bias, + residual) for the 8 columns c..c+7 of
+// row, rounded to T; stored to xs when given.
+template <typename T>
+__device__ __forceinline__ void partial_row8(const PartialRows& pr, int64_t row, int c, float* v) {
+  const float* p = pr.part + row * pr.ldp + c;
+  load8(p, v);
+  for (int s = 1; s < pr.n; ++s) {
+    float w[8];
+    load8(p + s * pr.plane, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += w[e];
+  }
+  if (pr.bias) {
+    float b[8];
+    load8((const T*)pr.bias + c, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += b[e];
+  }
+  if (pr.resid) {
+    float r[8];
+    load8((const T*)pr.resid + row * pr.ldr + c, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += r[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = to_f32(from_f32<T>(v[e]));
+  if (pr.xs) store8((T*)pr.xs + row * pr.ldxs + c, v);
+}
+
+// NCH = number of 512-column chunks a lane covers (lane owns columns
+// lane*8 + 512*i .. +7).  PART: x comes from fp32 partial sums (pr).
+template <typename T, int NCH, bool GATE, bool PART>
 __global__ __launch_bounds__(256) void gln_fwd_kernel(
     const T* x, int64_t ldx, T* y, int64_t ldy, const T* __restrict__ gamma,
     const T* __restrict__ beta, const uint8_t* __restrict__ g, int64_t nrows, int d, float eps,
-    float* __restrict__ mean_out, float* __restrict__ rstd_out, const T* __restrict__ u, int64_t ldu) {
+    float* __restrict__ mean_out, float* __restrict__ rstd_out, const T* __restrict__ u, int64_t ldu,
+    PartialRows pr) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= nrows) return;
@@ -88,7 +120,8 @@ __global__ __launch_bounds__(256) void gln_fwd_kernel(
   for (int i = 0; i < NCH; ++i) {
     const int c = lane * 8 + i * 512;
     if (c < d) {
-      load8(x + row * ldx + c, v[i]);
+      if (PART) partial_row8<T>(pr, row, c, v[i]);
+      else load8(x + row * ldx + c, v[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += v[i][e];
     } else {
@@ -137,30 +170,52 @@ __global__ __launch_bounds__(256) void gln_fwd_kernel(
   }
 }
 
-template <typename T, bool GATE>
+template <typename T, bool GATE, bool PART>
 static int gln_fwd_dispatch(const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,
                             const void* beta, const uint8_t* g, int64_t T_, int d, float eps,
-                            float* mean, float* rstd, const void* u, int64_t ldu, hipStream_t st) {
+                            float* mean, float* rstd, const void* u, int64_t ldu, const PartialRows& pr,
+                            hipStream_t st) {
   dim3 grid((unsigned)((T_ + 3) / 4)), block(256);
   const int nch = (d + 511) / 512;
-#define GLN_FWD_CASE(N)                                                                              \
-  case N:                                                                                            \
-    hipLaunchKernelGGL((gln_fwd_kernel<T, N, GATE>), grid, block, 0, st, (const T*)x, ldx, (T*)y,   \
-                       ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, \
-                       ldu);                                                                         \
+  const int n = nch <= 2 ? nch : nch <= 4 ? 4 : nch <= 8 ? 8 : 16;
+#define GLN_FWD_CASE(N)                                                                                 \
+  case N:                                                                                               \
+    hipLaunchKernelGGL((gln_fwd_kernel<T, N, GATE, PART>), grid, block, 0, st, (const T*)x, ldx, (T*)y, \
+                       ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, ldu, \
+                       pr);                                                                             \
     break;
-  switch (nch) {
+  switch (n) {
     GLN_FWD_CASE(1)
     GLN_FWD_CASE(2)
     GLN_FWD_CASE(4)
     GLN_FWD_CASE(8)
-    GLN_FWD_CASE(16)
-    case 3: hipLaunchKernelGGL((gln_fwd_kernel<T, 4, GATE>), grid, block, 0, st, (const T*)x, ldx, (T*)y, ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, ldu); break;
-    default:
-      if (nch <= 8) hipLaunchKernelGGL((gln_fwd_kernel<T, 8, GATE>), grid, block, 0, st, (const T*)x, ldx, (T*)y, ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, ldu);
-      else hipLaunchKernelGGL((gln_fwd_kernel<T, 16, GATE>), grid, block, 0, st, (const T*)x, ldx, (T*)y, ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, ldu);
+    default: GLN_FWD_CASE(16)
   }
 #undef GLN_FWD_CASE
+  MTGR_LAUNCH_CHECK();
+  return MTGR_OK;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void partial_reduce_kernel(PartialRows pr, int64_t nrows, int d) {
+  const int cpr = d / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nrows * cpr) return;
+  float v[8];
+  partial_row8<T>(pr, idx / cpr, (int)(idx % cpr) * 8, v);
+}
+
+int launch_partial_reduce(int dt, const PartialRows& in, int64_t T_, int d, hipStream_t stream) {
+  if (T_ <= 0) return MTGR_OK;
+  if (!in.xs || !in.part || in.n < 1 || d % 8) return MTGR_ERR_INVALID_ARG;
+  const int64_t n = T_ * (d / 8);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  switch (dt) {
+    case MTGR_F32: hipLaunchKernelGGL(partial_reduce_kernel<float>, grid, dim3(256), 0, stream, in, T_, d); break;
+    case MTGR_BF16: hipLaunchKernelGGL(partial_reduce_kernel<bf16_t>, grid, dim3(256), 0, stream, in, T_, d); break;
+    case MTGR_F16: hipLaunchKernelGGL(partial_reduce_kernel<f16_t>, grid, dim3(256), 0, stream, in, T_, d); break;
+    default: return MTGR_ERR_UNSUPPORTED;
+  }
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
 }
@@ -170,17 +225,38 @@ int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, con
                    float* rstd, const void* u, int64_t ldu, hipStream_t stream) {
   if (T_ <= 0) return MTGR_OK;
   const bool gate = u != nullptr;
+  const PartialRows none = {};
+#define GLN_FWD_DT(TY)                                                                                        \
+  return gate ? gln_fwd_dispatch<TY, true, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, \
+                                                  ldu, none, stream)                                         \
+              : gln_fwd_dispatch<TY, false, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, \
+                                                   ldu, none, stream);
   switch (dt) {
-    case MTGR_F32:
-      return gate ? gln_fwd_dispatch<float, true>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream)
-                  : gln_fwd_dispatch<float, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream);
-    case MTGR_BF16:
-      return gate ? gln_fwd_dispatch<bf16_t, true>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream)
-                  : gln_fwd_dispatch<bf16_t, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream);
-    case MTGR_F16:
-      return gate ? gln_fwd_dispatch<f16_t, true>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream)
-                  : gln_fwd_dispatch<f16_t, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, stream);
+    case MTGR_F32: GLN_FWD_DT(float)
+    case MTGR_BF16: GLN_FWD_DT(bf16_t)
+    case MTGR_F16: GLN_FWD_DT(f16_t)
   }
+#undef GLN_FWD_DT
+  return MTGR_ERR_UNSUPPORTED;
+}
+
+int launch_gln_fwd_part(int dt, const PartialRows& in, void* y, int64_t ldy, const void* gamma, const void* beta,
+                        const uint8_t* g, int64_t T_, int d, float eps, float* mean, float* rstd, const void* u,
+                        int64_t ldu, hipStream_t stream) {
+  if (T_ <= 0) return MTGR_OK;
+  if (!in.part || in.n < 1) return MTGR_ERR_INVALID_ARG;
+  const bool gate = u != nullptr;
+#define GLN_FWD_DT(TY)                                                                                             \
+  return gate ? gln_fwd_dispatch<TY, true, true>(nullptr, 0, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, \
+                                                 in, stream)                                                       \
+              : gln_fwd_dispatch<TY, false, true>(nullptr, 0, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u,    \
+                                                  ldu, in, stream);
+  switch (dt) {
+    case MTGR_F32: GLN_FWD_DT(float)
+    case MTGR_BF16: GLN_FWD_DT(bf16_t)
+    case MTGR_F16: GLN_FWD_DT(f16_t)
+  }
+#undef GLN_FWD_DT
   return MTGR_ERR_UNSUPPORTED;
 }
 

@@ -149,7 +149,12 @@ int mtgr_group_layernorm_bwd(const void* dy, const void* x, const float* mean, c
  *             into one fused [T, 4d] buffer); head h = columns h*dh..h*dh+dh-1
  *   o       : [T, H*dh] with row stride ld_o, written
  *   bf16/f16: dh in {64, 128} (MFMA kernels); f32: dh in {16, 32, 64, 128}.
- *   workspace : MTGR_OP_ATTN_FWD bytes
+ *   workspace : MTGR_OP_ATTN_FWD bytes (sized with the call's d = H*dh and
+ *               H).  For 16-bit batches too short to occupy the GPU (one
+ *               serving request) the key range of every query tile is split
+ *               and fp32 partial sums are kept in the workspace, so a short
+ *               batch can need more workspace than a long one; the sum is
+ *               taken in a fixed order (results are deterministic).
  */
 int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv, void* o,
                        int64_t ld_o, const int32_t* offsets, const uint8_t* group_ids,
@@ -259,7 +264,11 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
  *   x_in        : [T, d] input, not modified; x_out : [T, d] output of the
  *                 last layer, must not alias x_in
  *   workspace   : MTGR_OP_STACK_FWD bytes (independent of L)
- *   Results are bit-identical to L chained mtgr_hstu_layer_fwd calls.
+ *   fp32 results are bit-identical to L chained mtgr_hstu_layer_fwd calls.
+ *   16-bit batches too short to occupy the GPU (one serving request) split
+ *   each output projection over K into fp32 planes that the next layer's
+ *   input norm adds together with bias and residual, so their results agree
+ *   with chained calls up to the order of fp32 additions.
  */
 int mtgr_hstu_stack_fwd(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
                         const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,

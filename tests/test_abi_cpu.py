@@ -63,10 +63,22 @@ def test_workspace_sizes_grow(lib):
     from generative_recommendation_ranking_grouplayernorm_amd import binding as b
     import torch
 
-    for op in (b.OP_ATTN_FWD, b.OP_ATTN_BWD, b.OP_LAYER_FWD, b.OP_LAYER_BWD, b.OP_GLN_BWD, b.OP_STACK_FWD):
+    for op in (b.OP_ATTN_BWD, b.OP_LAYER_BWD, b.OP_GLN_BWD):
         a = b.mtgr_workspace_size(op, 8, 1000, 0, 256, 2, torch.bfloat16)
         c = b.mtgr_workspace_size(op, 80, 65536, 0, 256, 2, torch.bfloat16)
         assert 0 < a <= c
+    # forward ops: fp32 never splits the key range, so its sizes grow with the
+    # batch; a short 16-bit batch adds at least two fp32 partial planes, a
+    # long one none
+    for op in (b.OP_ATTN_FWD, b.OP_LAYER_FWD, b.OP_STACK_FWD):
+        a = b.mtgr_workspace_size(op, 8, 1000, 0, 256, 2, torch.float32)
+        c = b.mtgr_workspace_size(op, 80, 65536, 0, 256, 2, torch.float32)
+        assert 0 < a <= c
+    short32 = b.mtgr_workspace_size(b.OP_ATTN_FWD, 8, 1000, 0, 256, 2, torch.float32)
+    short16 = b.mtgr_workspace_size(b.OP_ATTN_FWD, 8, 1000, 0, 256, 2, torch.bfloat16)
+    assert short16 >= short32 + 2 * 1000 * 256 * 4
+    assert (b.mtgr_workspace_size(b.OP_ATTN_FWD, 80, 65536, 0, 1024, 8, torch.bfloat16)
+            == b.mtgr_workspace_size(b.OP_ATTN_FWD, 80, 65536, 0, 1024, 8, torch.float32))
     assert b.mtgr_workspace_size(b.OP_GLN_FWD, 8, 1000, 0, 256, 2, torch.bfloat16) == 0
 
 

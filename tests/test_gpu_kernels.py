@@ -109,7 +109,10 @@ def _run_attention(mb, batch, d, H, dtype, seed, alpha=1.0, with_bwd=True, max_l
     q, k, v = U[:, d:2 * d], U[:, 2 * d:3 * d], U[:, 3 * d:]
     o = torch.full((batch.T, d), float("nan"), dtype=dtype, device=DEV)
     ws = mb.workspace(mb.OP_ATTN_BWD, batch.B, batch.T, d, H, dtype, DEV, max_len=max_len)
-    mb.mtgr_hstu_attn_fwd(q, k, v, o, off, g, ts, H, dh, alpha, scale, ws)
+    # short 16-bit batches split the forward's key range: fp32 partial sums
+    # in the forward workspace
+    ws_f = mb.workspace(mb.OP_ATTN_FWD, batch.B, batch.T, d, H, dtype, DEV)
+    mb.mtgr_hstu_attn_fwd(q, k, v, o, off, g, ts, H, dh, alpha, scale, ws_f)
     qn, kn, vn = (f64(t) for t in (uqkv[:, d:2 * d], uqkv[:, 2 * d:3 * d], uqkv[:, 3 * d:]))
     ro = orc.hstu_attention(qn, kn, vn, batch.offsets, batch.group_ids, batch.timestamps, H, alpha, scale)
     res = {"o": (f64(o), ro)}

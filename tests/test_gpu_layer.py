@@ -116,6 +116,20 @@ def test_layer_small_halfprec_fwd_bwd(mb, dtype, stored_ds):
     check(res, oracle_layer(batch, res, True), dtype)
 
 
+def test_layer_odd_k_steps_three_heads_f16(mb):
+    """d = 192 (three 64-wide heads): the projections take an odd number of
+    64-deep K steps, and three heads use the plain head-to-workgroup map."""
+    rng = np.random.default_rng(57)
+    lengths = [[8, 150, 17, 20], [8, 41, 0, 13], [3, 300, 33, 5]]
+    batch = make_batch_from_lengths(lengths, rng, ts_max=86400)
+    p = make_layer_params(192, 3, rng, "xavier", True)
+    x = rng.normal(0, 1, size=(batch.T, 192))
+    R = rng.normal(0, 1, size=x.shape)
+    say("layer d=192 H=3 f16", batch.T)
+    res = run_layer(mb, batch, p, x, torch.float16, R=R)
+    check(res, oracle_layer(batch, res, True), torch.float16)
+
+
 def test_layer_bias_bf16_no_extras(mb):
     """Biases present and the fused SiLU' path (no intermediate gradients)."""
     rng = np.random.default_rng(41)

@@ -76,6 +76,38 @@ def test_stack_fwd_tiny_fp32_matches_oracle_and_chained_layers(mb):
         assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_stack_fwd_short_halfprec_with_biases_matches_oracle(mb, dtype):
+    """A short multi-user 16-bit batch with biases: the output projections
+    are split over K into fp32 planes that the next layer's input norm (and
+    the final sum) add with bias and residual.  L = 1, 2, 3 against the
+    oracle, and close to chained layer calls."""
+    rng = np.random.default_rng([0, 5, 61])
+    lengths = [[8, 300, 20, 20], [8, 57, 0, 9], [2, 130, 64, 33]]
+    batch = make_batch_from_lengths(lengths, rng, ts_max=86400)
+    d, H = 256, 2
+    params = [make_layer_params(d, H, rng, "xavier", True) for _ in range(3)]
+    x = rng.normal(0, 1, size=(batch.T, d))
+    scale = 1.0 / batch.max_len
+    off, g, ts = meta(batch, DEV)
+    lps, keep, qs = device_layers(mb, params, dtype)
+    x_in = rounded(x, dtype).to(DEV)
+    for L in (1, 2, 3):
+        out = torch.full_like(x_in, float("nan"))
+        ws = mb.workspace(mb.OP_STACK_FWD, batch.B, batch.T, d, H, dtype, DEV)
+        x_copy = x_in.clone()
+        mb.mtgr_hstu_stack_fwd(lps[:L], x_in, out, off, g, ts, scale, ws)
+        ch = chained(mb, lps[:L], x_in, off, g, ts, scale, dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(x_in, x_copy), "input modified"
+        ref = orc.stack_fwd(qs[:L], f64(x_in), batch.offsets, batch.group_ids, batch.timestamps, 1.0, scale)
+        err = rel_l2(f64(out), ref)
+        err_ch = rel_l2(f64(out), f64(ch))
+        say(f"  {dtype} L={L}: rel-L2 vs oracle {err:.3e}, vs chained layer calls {err_ch:.3e}")
+        assert err <= TOL[dtype]
+        assert err_ch <= TOL[dtype]
+
+
 def _serving_request(K: int, seed: int, n_s: int, n_r: int):
     """A one-user request with history n_s, n_r real-time actions and K
     candidates, drawn like the serving sweep (candidates after every
@@ -98,8 +130,9 @@ def test_serving_graph_replay_matches_eager(mb):
     equal the eager stack call bit for bit: three replays with eager work and
     host synchronisations between them, then a different request of the same
     length (another history / real-time split, new timestamps and features)
-    written into the captured buffers.  The eager stack call equals chained
-    layer calls, and at K=20 the replay matches the oracle."""
+    written into the captured buffers.  The eager stack call agrees with
+    chained layer calls up to fp32 addition order, and at K=20 the replay matches
+    the oracle."""
     cfg = CONFIGS[5]
     dtype = torch.float16
     d, H = cfg["d"], cfg["H"]
@@ -135,7 +168,11 @@ def test_serving_graph_replay_matches_eager(mb):
         mb.mtgr_hstu_stack_fwd(lps, e_x, e_y, e_off, e_g, e_ts, scale, e_ws)
         ch = chained(mb, lps, e_x, e_off, e_g, e_ts, scale, dtype)
         torch.cuda.synchronize()
-        assert torch.equal(e_y, ch), f"K={K}: stack call differs from chained layer calls"
+        # the stack splits the output projections of short batches over K:
+        # same values up to the order of fp32 additions
+        err_ch = rel_l2(f64(e_y), f64(ch))
+        say(f"  K={K}: stack vs chained layer calls rel-L2 {err_ch:.3e}")
+        assert err_ch <= TOL[dtype], f"K={K}: stack call differs from chained layer calls"
         for rep in range(3):
             ys.fill_(float("nan"))
             graphs[K].launch()
