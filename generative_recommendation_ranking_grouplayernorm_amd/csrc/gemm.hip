@@ -107,22 +107,19 @@ __device__ __forceinline__ void epi_apply(const GemmEpiArgs& ep, int m, int n, f
 //   small: 128 x 128, 4 waves as 2 x 2, 64 x 64 per wave, two workgroups per
 //          compute unit (forward products of short batches, such as one
 //          serving request, where the large tiles would leave most compute
-//          units idle).  With few workgroups per unit the load latency is
-//          what shows, so the small tiles keep two K steps of global loads
-//          in flight (two register sets, the K loop unrolled by two).
+//          units idle).
 // ---------------------------------------------------------------------------
 constexpr int G_BK = 64;
 constexpr int G_KC_PITCH = G_BK + 8;  // K-contiguous rows: 64 + 8 halves
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int MIN_BLOCKS_, bool DEEP_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int MIN_BLOCKS_>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, MIN_BLOCKS = MIN_BLOCKS_;
-  static constexpr bool DEEP = DEEP_;  // two K steps of loads in flight
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   static constexpr int TM = BM / WAVES_M / 32, TN = BN / WAVES_N / 32;
 };
-using GemmLarge = GemmCfg<256, 256, 2, 4, 1, false>;
-using GemmSmall = GemmCfg<128, 128, 2, 2, 2, true>;
+using GemmLarge = GemmCfg<256, 256, 2, 4, 1>;
+using GemmSmall = GemmCfg<128, 128, 2, 2, 2>;
 
 // LDS tile of one operand with ROWS rows (its M or N extent).  K-contiguous:
 // [ROWS][72]; M/N-contiguous: [64][ROWS + 16].  Both layouts get the larger
@@ -272,46 +269,19 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) gemm_swrite<BKC, BN>(smem[buf] + A_ELEMS, tid + NTH * i, rb[i]);
   };
-  if constexpr (C::DEEP) {
-    // Data of K step j travels in register set j % 2 and LDS buffer j % 2;
-    // its loads are issued two steps ahead.  Prefetches past the last step
-    // re-read the last step (in bounds) and are never written to LDS.
-    uint4 ra0[A_LOADS], rb0[B_LOADS], ra1[A_LOADS], rb1[B_LOADS];
-    const int klast = kbeg + (nk - 1) * G_BK;
-    auto kat = [&](int j) { return min(kbeg + j * G_BK, klast); };
-    if (nk > 0) {
-      gload_to(ra0, rb0, kat(0));
-      gload_to(ra1, rb1, kat(1));
-      swrite_from(ra0, rb0, 0);
-      gload_to(ra0, rb0, kat(2));
-    }
+  uint4 ra[A_LOADS], rb[B_LOADS];
+  if (nk > 0) {
+    gload_to(ra, rb, kbeg);
+    swrite_from(ra, rb, 0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < nk;
+    if (more) gload_to(ra, rb, kbeg + (it + 1) * G_BK);
+    mma(smem[buf], smem[buf] + A_ELEMS);
+    if (more) swrite_from(ra, rb, buf ^ 1);
     __syncthreads();
-    for (int it = 0; it < nk; it += 2) {
-      mma(smem[0], smem[0] + A_ELEMS);
-      if (it + 1 < nk) swrite_from(ra1, rb1, 1);
-      gload_to(ra1, rb1, kat(it + 3));
-      __syncthreads();
-      if (it + 1 >= nk) break;
-      mma(smem[1], smem[1] + A_ELEMS);
-      if (it + 2 < nk) swrite_from(ra0, rb0, 0);
-      gload_to(ra0, rb0, kat(it + 4));
-      __syncthreads();
-    }
-  } else {
-    uint4 ra[A_LOADS], rb[B_LOADS];
-    if (nk > 0) {
-      gload_to(ra, rb, kbeg);
-      swrite_from(ra, rb, 0);
-    }
-    __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-      const int buf = it & 1;
-      const bool more = it + 1 < nk;
-      if (more) gload_to(ra, rb, kbeg + (it + 1) * G_BK);
-      mma(smem[buf], smem[buf] + A_ELEMS);
-      if (more) swrite_from(ra, rb, buf ^ 1);
-      __syncthreads();
-    }
   }
   if constexpr (EPI == EPI_F32_STORE || EPI == EPI_F32_ATOMIC || EPI == EPI_F32_PLANES) {
     float* planeC = (float*)ep.C + (EPI == EPI_F32_PLANES ? (int64_t)split * ep.plane : 0);
