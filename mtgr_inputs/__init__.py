@@ -20,5 +20,7 @@ from .synth import (  # noqa: F401
     make_activations,
     make_probe_head,
     config_inputs,
+    make_user_pool,
+    make_uniform_draws,
     NUM_GROUPS,
 )

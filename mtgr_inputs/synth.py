@@ -297,3 +297,29 @@ def config_inputs(cfg_id: int, seed: int = 0, K: Optional[int] = None):
     batch = make_batch(cfg_id, seed, K=K)
     x = make_activations(batch.T, cfg["d"], xrng, cfg["x_init"])
     return batch, params, x
+
+
+def make_user_pool(cfg_id: int, min_tokens: int, seed: int = 0) -> Batch:
+    """Users drawn one after another with a workload's length distributions
+    (no trimming) until they hold at least ``min_tokens`` tokens: the pool a
+    training batch is cut from after Stochastic Length sampling shortens its
+    histories (paper-daily "计算量涨了 65 倍" section)."""
+    cfg = CONFIGS[cfg_id]
+    rng = np.random.default_rng([seed, cfg_id, 7])
+    users: List[List[int]] = []
+    total = 0
+    while total < min_tokens:
+        n_s = _draw_len(rng, cfg["n_s"])
+        n_r = _draw_len(rng, cfg["n_r"])
+        n_c = _draw_len(rng, cfg["n_c"])
+        users.append([cfg["n_u"], n_s, n_r, n_c])
+        total += cfg["n_u"] + n_s + n_r + n_c
+    batch = make_batch_from_lengths(users, rng, cfg["ts_max"], cfg.get("cand_after_rt"))
+    batch.meta = dict(cfg_id=cfg_id, seed=seed, name=cfg["name"] + "_pool")
+    return batch
+
+
+def make_uniform_draws(n: int, seed: int = 0) -> np.ndarray:
+    """``n`` float32 uniforms in [0, 1): the per-user random numbers of
+    Stochastic Length sampling, drawn here and passed to both sides."""
+    return np.random.default_rng([seed, 11]).random(n, dtype=np.float32)
