@@ -43,6 +43,10 @@ def parse():
                     help="time the 22-layer fp16 one-request serving forward per candidate count instead "
                          "(eager layer calls, one stack call, graph replay)")
     ap.add_argument("--requests", type=int, default=200, help="timed requests per K and mode (--serving)")
+    ap.add_argument("--stochastic-length", type=int, default=0, metavar="S_KEEP",
+                    help="time Stochastic Length sampling (histories cut to S_KEEP tokens) of a long-tail user "
+                         "pool and the layer step on the 65,536-token batch cut from it, against the batch "
+                         "without sampling")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed steps, copy MIB MiB device-to-device 3 times (a plain copy kernel "
                          "of known size, the calibration for HBM byte counters)")
@@ -262,6 +266,9 @@ def main():
         sys.exit(2)
     if args.serving:
         serving_bench(args)
+        return
+    if args.stochastic_length > 0:
+        sl_bench(args)
         return
     import numpy as np
     import torch
@@ -512,6 +519,132 @@ def serving_bench(args):
                                "candidates), 22 layers, d_model 1024, 8 heads of 128",
                    "K_sweep": list(results)},
         "per_K": results,
+    }
+    print(json.dumps(out))
+
+
+def sl_bench(args):
+    """Stochastic Length: a pool of long-tail users (four times the budget)
+    has each history cut to a random window of S_KEEP tokens and the longest
+    prefix within 65,536 tokens becomes the training batch.  Reports the
+    sampling kernels' time (HIP events, median of repeated calls) and
+    bandwidth, and the layer forward + backward on that batch against the
+    token-balanced batch of the same budget without sampling."""
+    import numpy as np
+    import torch
+
+    import generative_recommendation_ranking_grouplayernorm_amd.binding as mb
+    from generative_recommendation_ranking_grouplayernorm_amd import flops as fl
+    from mtgr_inputs import CONFIGS, config_inputs, make_uniform_draws, make_user_pool
+
+    cfg_id, budget, s_keep = 4, 65536, args.stochastic_length
+    cfg = CONFIGS[cfg_id]
+    dev = torch.device("cuda:0")
+    lib = mb.load_library()
+    dt = torch.bfloat16
+    d, H = cfg["d"], cfg["H"]
+    pool = make_user_pool(cfg_id, 4 * budget, seed=args.seed)
+    u = torch.from_numpy(make_uniform_draws(pool.B, seed=args.seed)).to(dev)
+    gen = torch.Generator(device="cpu").manual_seed(args.seed)
+    x = torch.randn(pool.T, d, generator=gen).to(dt).to(dev)
+    off = torch.from_numpy(pool.offsets).to(dev)
+    g = torch.from_numpy(pool.group_ids).to(dev)
+    ts = torch.from_numpy(pool.timestamps).to(dev)
+    off_o = torch.empty(pool.B + 1, dtype=torch.int32, device=dev)
+    g_o = torch.empty(pool.T, dtype=torch.uint8, device=dev)
+    ts_o = torch.empty(pool.T, dtype=torch.int64, device=dev)
+    x_o = torch.empty_like(x)
+    fit = torch.empty(2, dtype=torch.int64, device=dev)
+    ws = mb.workspace(mb.OP_STOCHASTIC_LENGTH, pool.B, pool.T, d, H, dt, dev)
+    stream = torch.cuda.current_stream()
+
+    def sample():
+        mb.mtgr_stochastic_length(off, g, ts, x, u, s_keep, budget, off_o, g_o, ts_o, x_o, fit, ws, stream)
+
+    for _ in range(3):
+        sample()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(args.steps, 10)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sample()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    sl_ms = float(np.median(times))
+    Bf, Tf = (int(v) for v in fit.cpu())
+    T_all = int(off_o[-1].item())
+    # algorithmic bytes: every row of the cut batch read and written
+    # (features, group id, timestamp), plus offsets and draws
+    sl_bytes = Tf * (2 * d * 2 + 2 * 1 + 2 * 8) + pool.B * (4 + 4 + 4)
+    sl_gbs = sl_bytes / (sl_ms / 1e3) / 1e9
+
+    def layer_step_ms(offsets_t, g_t, ts_t, xin, B, T, max_len, params):
+        p = params[0]
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(dev)
+        dev_p = {k: to(getattr(p, k)) for k in ("W_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o")}
+        prm = mb.make_params(dev_p, H)
+        saved = mb.alloc_saved(T, d, dt, dev)
+        sv = mb.make_saved(saved)
+        y = torch.empty(T, d, dtype=dt, device=dev)
+        dx = torch.empty_like(y)
+        R = torch.randn(T, d, generator=gen).to(dt).to(dev)
+        grads = mb.alloc_grads(d, 4, False, dev)
+        ws_f = mb.workspace(mb.OP_LAYER_FWD, B, T, d, H, dt, dev)
+        ws_b = mb.workspace(mb.OP_LAYER_BWD, B, T, d, H, dt, dev, max_len=max_len)
+        scale = 1.0 / max_len
+
+        def step():
+            mb.mtgr_hstu_layer_fwd(prm, xin, y, sv, offsets_t, g_t, ts_t, scale, ws_f, stream)
+            mb.mtgr_hstu_layer_bwd(prm, xin, sv, R, dx, grads, offsets_t, g_t, ts_t, scale, ws_b, max_len=max_len,
+                                   stream=stream)
+
+        for _ in range(max(args.warmup, 2)):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    _, params, _ = config_inputs(cfg_id, seed=args.seed)
+    off_h = off_o[:Bf + 1].cpu().numpy()
+    max_len_sl = int(np.max(np.diff(off_h)))
+    ms_sl = layer_step_ms(off_o[:Bf + 1].clone(), g_o[:Tf], ts_o[:Tf], x_o[:Tf], Bf, Tf, max_len_sl, params)
+    P_sl = fl.visible_pairs(off_h, g_o[:Tf].cpu().numpy(), ts_o[:Tf].cpu().numpy())
+    base, _, xb = config_inputs(cfg_id, seed=args.seed)
+    xbd = torch.from_numpy(np.ascontiguousarray(xb, dtype=np.float32)).to(dt).to(dev)
+    ms_base = layer_step_ms(torch.from_numpy(base.offsets).to(dev), torch.from_numpy(base.group_ids).to(dev),
+                            torch.from_numpy(base.timestamps).to(dev), xbd, base.B, base.T, int(base.max_len),
+                            params)
+    P_base = fl.visible_pairs(base.offsets, base.group_ids, base.timestamps)
+    ups_sl = Bf / (ms_sl / 1e3)
+    ups_base = base.B / (ms_base / 1e3)
+    out = {
+        "metric": "users/sec of the layer fwd+bwd at a 65,536-token budget with Stochastic Length sampling",
+        "value": round(ups_sl, 1),
+        "unit": "users/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded long-tail user pool, random-init weights)",
+        "config": {"workload": "Stochastic Length on a long-tail user pool, then MTGR HSTU layer fwd+bwd",
+                   "s_keep": s_keep, "token_budget": budget, "pool_users": pool.B, "pool_tokens": pool.T,
+                   "d_model": d, "heads": H},
+        "sampled": {"users": Bf, "tokens": Tf, "max_len": max_len_sl, "visible_pairs": P_sl,
+                    "ms_per_step": round(ms_sl, 4), "users_per_sec": round(ups_sl, 1)},
+        "unsampled": {"users": base.B, "tokens": base.T, "max_len": int(base.max_len), "visible_pairs": P_base,
+                      "ms_per_step": round(ms_base, 4), "users_per_sec": round(ups_base, 1)},
+        "users_per_sec_ratio": round(ups_sl / ups_base, 3),
+        "sampling": {"ms": round(sl_ms, 4), "kept_tokens_of_pool": T_all, "bytes": sl_bytes,
+                     "roofline": {"bound": "hbm", "achieved": round(sl_gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(sl_gbs / HBM_PEAK_GBS, 4)}},
     }
     print(json.dumps(out))
 

@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmtgr.so")
 
 MTGR_F32, MTGR_BF16, MTGR_F16 = 0, 1, 2
-OP_PREP, OP_GLN_FWD, OP_GLN_BWD, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_STACK_FWD = range(8)
+(OP_PREP, OP_GLN_FWD, OP_GLN_BWD, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_STACK_FWD,
+ OP_STOCHASTIC_LENGTH) = range(9)
 
 _DT = {torch.float32: MTGR_F32, torch.bfloat16: MTGR_BF16, torch.float16: MTGR_F16}
 
@@ -26,7 +27,7 @@ EXPORTED = (
     "mtgr_version", "mtgr_status_string", "mtgr_workspace_size", "mtgr_jagged_prep",
     "mtgr_group_layernorm", "mtgr_group_layernorm_bwd", "mtgr_hstu_attn_fwd", "mtgr_hstu_attn_bwd",
     "mtgr_hstu_layer_fwd", "mtgr_hstu_layer_bwd", "mtgr_hstu_stack_fwd", "mtgr_stack_graph_create",
-    "mtgr_stack_graph_launch", "mtgr_stack_graph_destroy",
+    "mtgr_stack_graph_launch", "mtgr_stack_graph_destroy", "mtgr_stochastic_length",
 )
 
 
@@ -97,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      P, SZ, ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
         "mtgr_stack_graph_launch": ([P, P], ctypes.c_int),
         "mtgr_stack_graph_destroy": ([P], ctypes.c_int),
+        "mtgr_stochastic_length": ([P, P, P, P, I64, I32, I64, I32, ctypes.c_int, P, I32, I64, P, P, P, P, I64, P,
+                                    P, SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -318,3 +321,13 @@ def mtgr_stack_graph_launch(graph: StackGraph, stream=None) -> None:
 
 def mtgr_stack_graph_destroy(graph: StackGraph) -> None:
     graph.close()
+
+
+def mtgr_stochastic_length(offsets, group_ids, timestamps, x, u, s_keep: int, token_budget: int, offsets_out,
+                           group_ids_out, timestamps_out, x_out, fit_out, ws, stream=None) -> None:
+    B = offsets.numel() - 1
+    T = x.shape[0]
+    _check("mtgr_stochastic_length", load_library().mtgr_stochastic_length(
+        _p(offsets), _p(group_ids), _p(timestamps), _p(x), _ld(x), B, T, x.shape[1], dtype_code(x.dtype), _p(u),
+        s_keep, token_budget, _p(offsets_out), _p(group_ids_out), _p(timestamps_out), _p(x_out), _ld(x_out),
+        _p(fit_out), _p(ws), ws.numel(), _stream(stream)))

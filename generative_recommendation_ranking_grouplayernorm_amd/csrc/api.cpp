@@ -167,6 +167,7 @@ size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t max_len, int32_
     case MTGR_OP_LAYER_FWD: return layer_fwd_ws(B, T, d, H, dt);
     case MTGR_OP_LAYER_BWD: return layer_bwd_ws(B, T, max_len, d, H, dt);
     case MTGR_OP_STACK_FWD: return stack_fwd_ws(B, T, d, H, dt);
+    case MTGR_OP_STOCHASTIC_LENGTH: return sl_workspace_bytes(B, T);
     default: return 0;
   }
 }
@@ -179,6 +180,27 @@ int mtgr_jagged_prep(const int32_t* offsets, const uint8_t* group_ids, int32_t B
   if (B == 0) return MTGR_OK;
   if (!offsets || !seg || (T > 0 && !group_ids)) return MTGR_ERR_INVALID_ARG;
   return launch_seg_only(offsets, group_ids, B, seg, S(stream));
+}
+
+int mtgr_stochastic_length(const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
+                           const void* x, int64_t ld_x, int32_t B, int64_t T, int32_t d, int dt, const float* u,
+                           int32_t s_keep, int64_t token_budget, int32_t* offsets_out, uint8_t* group_ids_out,
+                           int64_t* timestamps_out, void* x_out, int64_t ld_out, int64_t* fit_out, void* workspace,
+                           size_t ws_bytes, mtgr_stream_t stream) {
+  if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
+  if (!jagged_ok(offsets, group_ids, timestamps, B, T) || d < 1 || s_keep < 0 || token_budget < 0)
+    return MTGR_ERR_INVALID_ARG;
+  if (!offsets_out || !fit_out) return MTGR_ERR_INVALID_ARG;
+  if (B > 0 && !u) return MTGR_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !x_out || !group_ids_out || !timestamps_out)) return MTGR_ERR_INVALID_ARG;
+  const int64_t row_bytes = (int64_t)d * elt(dt);
+  if (ld_x < d || ld_out < d || row_bytes % 16) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(x, ld_x, dt) || !vec_ok(x_out, ld_out, dt)) return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < sl_workspace_bytes(B, T) || !workspace) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  // an empty batch still gets its offsets and budget cut written
+  return launch_stochastic_length(offsets, group_ids, timestamps, x, ld_x * (int64_t)elt(dt), (int)row_bytes, B, T, u,
+                                  s_keep, token_budget, offsets_out, group_ids_out, timestamps_out, x_out,
+                                  ld_out * (int64_t)elt(dt), fit_out, workspace, S(stream));
 }
 
 int mtgr_group_layernorm(const void* x, void* y, const void* gamma, const void* beta,

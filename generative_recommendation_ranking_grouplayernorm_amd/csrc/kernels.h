@@ -53,6 +53,14 @@ int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t
 int launch_seg_only(const int32_t* offsets, const uint8_t* group_ids, int B, int32_t* seg,
                     hipStream_t stream);
 
+// ---- Stochastic Length sampling and the token-budget cut -----------------
+int64_t sl_max_blocks(int B, int64_t T);
+size_t sl_workspace_bytes(int B, int64_t T);
+int launch_stochastic_length(const int32_t* offsets, const uint8_t* g, const int64_t* ts, const void* x,
+                             int64_t ldx_bytes, int row_bytes, int B, int64_t T, const float* u, int s_keep,
+                             int64_t budget, int32_t* offsets_out, uint8_t* g_out, int64_t* ts_out, void* x_out,
+                             int64_t ldo_bytes, int64_t* fit_out, void* ws, hipStream_t stream);
+
 // ---- a2/a5: group norm rows ---------------------------------------------
 // y = GLN(x) (mode plain) or y = GLN(x) * u (mode gate).
 int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,

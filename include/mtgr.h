@@ -18,6 +18,7 @@
  *          训练数据怎么组织 (jagged rows, timestamps kept for the mask).
  *   [fr]   "MTGR：混合范式建模" (fun-rec 7.3): 7.3.3 (GLN formula),
  *          7.3.4 (the three mask rules).
+ *   [blog] also 11.3 (batches sized by token count).
  *   [dr]   paper-daily deep reading of the Meituan blog post: 2 方法详解
  *          (extra norm on every layer's input), 3 核心技术贡献 and
  *          4 实验结果分析 / 工程指标 (fp16 serving, graph replay, P99).
@@ -75,7 +76,8 @@ typedef enum {
   MTGR_OP_ATTN_BWD = 4,
   MTGR_OP_LAYER_FWD = 5,
   MTGR_OP_LAYER_BWD = 6,
-  MTGR_OP_STACK_FWD = 7
+  MTGR_OP_STACK_FWD = 7,
+  MTGR_OP_STOCHASTIC_LENGTH = 8
 } mtgr_op;
 
 typedef void* mtgr_stream_t; /* hipStream_t */
@@ -108,6 +110,41 @@ size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t max_len, int32_
  */
 int mtgr_jagged_prep(const int32_t* offsets, const uint8_t* group_ids, int32_t B, int64_t T,
                      int32_t* seg, void* workspace, size_t ws_bytes, mtgr_stream_t stream);
+
+/*
+ * Stochastic Length sampling in front of the training path, and the cut of
+ * the shortened users to a token budget.  [pd] 计算量涨了 65 倍，训练成本怎么压住:
+ * training replaces a long user sequence by a randomly drawn segment of it
+ * (scoring keeps the full sequence); [blog] 11.3: batches are sized by token
+ * count.  Reading: each user's history S keeps a contiguous window of
+ * min(n_s, s_keep) tokens, in order, starting (within S) at
+ *   min(floor(u_b * (n_s - s_keep + 1)), n_s - s_keep)
+ * (u_b * (n_s - s_keep + 1) one float32 product; draws outside [0, 1) are
+ * clamped to the first / last window); U, R and C tokens are kept, in order.
+ *   offsets, group_ids, timestamps : the input batch (B users, T tokens)
+ *   x          : [T, d] features, row stride ld_x elements, dtype dt; each
+ *                row d * sizeof(dt) bytes, a multiple of 16
+ *   u          : [B] float32 draws in [0, 1) (device), one per user
+ *   s_keep     : >= 0, history tokens kept per user
+ *   token_budget : >= 0
+ * Written (device):
+ *   offsets_out    : [B + 1] offsets of all B shortened users, input order
+ *   fit_out        : int64 [2]: the number of leading shortened users whose
+ *                    tokens fit token_budget (users of zero length included
+ *                    while they fit), and those tokens
+ *   group_ids_out, timestamps_out, x_out (row stride ld_out elements):
+ *                    capacity T rows; only the rows of the fitting users,
+ *                    [0, fit_out[1]), are written (pass token_budget >= T
+ *                    to materialise every shortened user).
+ *   The training batch is offsets_out[0 .. fit_out[0]] over those rows; the
+ *   caller reads fit_out when it needs B and T on the host.
+ *   workspace      : MTGR_OP_STOCHASTIC_LENGTH bytes for B and T
+ */
+int mtgr_stochastic_length(const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
+                           const void* x, int64_t ld_x, int32_t B, int64_t T, int32_t d, int dt,
+                           const float* u, int32_t s_keep, int64_t token_budget, int32_t* offsets_out,
+                           uint8_t* group_ids_out, int64_t* timestamps_out, void* x_out, int64_t ld_out,
+                           int64_t* fit_out, void* workspace, size_t ws_bytes, mtgr_stream_t stream);
 
 /*
  * a2/a5 - Group LayerNorm ([fr] 7.3.3; [pd] 模型怎么搭; [blog] 8).
