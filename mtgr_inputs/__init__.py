@@ -22,5 +22,8 @@ from .synth import (  # noqa: F401
     config_inputs,
     make_user_pool,
     make_uniform_draws,
+    HeadParams,
+    make_head_params,
+    make_labels,
     NUM_GROUPS,
 )

@@ -323,3 +323,34 @@ def make_uniform_draws(n: int, seed: int = 0) -> np.ndarray:
     """``n`` float32 uniforms in [0, 1): the per-user random numbers of
     Stochastic Length sampling, drawn here and passed to both sides."""
     return np.random.default_rng([seed, 11]).random(n, dtype=np.float32)
+
+
+@dataclass
+class HeadParams:
+    """Candidate head: Linear(d -> h) + bias, then Linear(h -> n_tasks) + bias."""
+    W1: np.ndarray
+    b1: Optional[np.ndarray]
+    W2: np.ndarray
+    b2: Optional[np.ndarray]
+
+
+def make_head_params(d: int, h: int, n_tasks: int, rng: np.random.Generator, bias: bool = True) -> HeadParams:
+    """Xavier-uniform weights, biases N(0, 0.02) (random init: no trained head)."""
+    def lin(out_f, in_f):
+        bound = np.sqrt(6.0 / (in_f + out_f))
+        return rng.uniform(-bound, bound, size=(out_f, in_f)).astype(np.float32)
+
+    W1 = lin(h, d)
+    b1 = rng.normal(0.0, 0.02, size=h).astype(np.float32) if bias else None
+    W2 = lin(n_tasks, h)
+    b2 = rng.normal(0.0, 0.02, size=n_tasks).astype(np.float32) if bias else None
+    return HeadParams(W1, b1, W2, b2)
+
+
+def make_labels(n_cand: int, rng: np.random.Generator, p_click: float = 0.1,
+                p_order: float = 0.3) -> np.ndarray:
+    """[n_cand, 2] float32 labels: click ~ Bernoulli(p_click), and click-then-
+    order (a subset of clicks) ~ click * Bernoulli(p_order)."""
+    click = (rng.random(n_cand) < p_click).astype(np.float32)
+    order = click * (rng.random(n_cand) < p_order).astype(np.float32)
+    return np.stack([click, order], axis=1)
