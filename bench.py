@@ -43,6 +43,8 @@ def parse():
                     help="time the 22-layer fp16 one-request serving forward per candidate count instead "
                          "(eager layer calls, one stack call, graph replay)")
     ap.add_argument("--requests", type=int, default=200, help="timed requests per K and mode (--serving)")
+    ap.add_argument("--head", action="store_true",
+                    help="time the candidate head with its loss and backward on the 65,536-token batch")
     ap.add_argument("--stochastic-length", type=int, default=0, metavar="S_KEEP",
                     help="time Stochastic Length sampling (histories cut to S_KEEP tokens) of a long-tail user "
                          "pool and the layer step on the 65,536-token batch cut from it, against the batch "
@@ -269,6 +271,9 @@ def main():
         return
     if args.stochastic_length > 0:
         sl_bench(args)
+        return
+    if args.head:
+        head_bench(args)
         return
     import numpy as np
     import torch
@@ -645,6 +650,104 @@ def sl_bench(args):
         "sampling": {"ms": round(sl_ms, 4), "kept_tokens_of_pool": T_all, "bytes": sl_bytes,
                      "roofline": {"bound": "hbm", "achieved": round(sl_gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(sl_gbs / HBM_PEAK_GBS, 4)}},
+    }
+    print(json.dumps(out))
+
+
+def head_bench(args):
+    """Candidate head (Linear 1024 -> 512, SiLU, Linear 512 -> 2 tasks) with
+    its binary cross-entropy loss and backward on the last-layer output of
+    the 65,536-token bf16 batch (2,220 candidates).  Per kernel step: HIP
+    events on the stream (library instrumentation) over the timed calls."""
+    import numpy as np
+    import torch
+
+    import generative_recommendation_ranking_grouplayernorm_amd.binding as mb
+    from mtgr_inputs import config_inputs, make_head_params, make_labels
+
+    dev = torch.device("cuda:0")
+    lib = mb.load_library()
+    dt = torch.bfloat16
+    batch, _, x = config_inputs(4, seed=args.seed)
+    d, h, nt = 1024, 512, 2
+    rng = np.random.default_rng([args.seed, 4, 9])
+    hp = make_head_params(d, h, nt, rng, True)
+    n_cand = int(np.sum(batch.group_ids == 3))
+    y = torch.from_numpy(make_labels(n_cand, rng)).to(dev)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(dev)
+    dev_p = {"W1": to(hp.W1), "b1": to(hp.b1), "W2": to(hp.W2), "b2": to(hp.b2)}
+    prm = mb.make_head_params(dev_p)
+    xd = to(x)
+    off = torch.from_numpy(batch.offsets).to(dev)
+    g = torch.from_numpy(batch.group_ids).to(dev)
+    ws = mb.head_workspace(batch.B, n_cand, d, h, nt, dt, dev)
+    loss = torch.empty(1, device=dev)
+    logits = torch.empty(n_cand, nt, device=dev)
+    dx = torch.empty(batch.T, d, dtype=dt, device=dev)
+    grads = {"W1": torch.empty(h, d, device=dev), "b1": torch.empty(h, device=dev),
+             "W2": torch.empty(nt, h, device=dev), "b2": torch.empty(nt, device=dev)}
+    stream = torch.cuda.current_stream()
+
+    def call():
+        mb.mtgr_candidate_head_loss(prm, xd, off, g, n_cand, y, loss, logits, dx, grads, ws, stream)
+
+    for _ in range(max(args.warmup, 3)):
+        call()
+    torch.cuda.synchronize()
+    lib.mtgr_profile_enable(1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prof = profile_summary(lib)
+    lib.mtgr_profile_enable(0)
+    for _ in range(3):
+        call()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e2.record(stream)
+    for _ in range(args.steps):
+        call()
+    e3.record(stream)
+    torch.cuda.synchronize()
+    ms = e2.elapsed_time(e3) / args.steps
+    T = batch.T
+    work = {  # algorithmic work per call
+        "head_hidden": ("mfma", 2 * n_cand * d * h),
+        "head_dW1": ("mfma", 2 * n_cand * d * h),
+        "head_dX": ("mfma", 2 * n_cand * d * h),
+        "head_expand": ("hbm", T * d * 2 + n_cand * d * 2),
+        "head_gather": ("hbm", 2 * n_cand * d * 2),
+    }
+    kernels = {}
+    for name, (tot, n) in prof.items():
+        avg = tot / max(n, 1)
+        ent = {"avg_ms": round(avg, 5), "ms_per_call": round(tot / args.steps, 5)}
+        if name in work:
+            bound, amount = work[name]
+            if bound == "mfma":
+                ach = amount / (avg / 1e3) / 1e12
+                ent.update(bound="mfma", achieved=round(ach, 2), unit="TFLOP/s", frac=round(ach / BF16_PEAK_TFLOPS, 4))
+            else:
+                ach = amount / (avg / 1e3) / 1e9
+                ent.update(bound="hbm", achieved=round(ach, 1), unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4))
+        kernels[name] = ent
+    out = {
+        "metric": "candidate head + loss + backward time per training batch",
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": False,
+        "dtype": "bf16",
+        "data": "synthetic (seeded 65,536-token batch, random-init head, Bernoulli labels)",
+        "config": {"workload": "candidate head (d 1024 -> 512 -> 2 tasks) with BCE loss and backward",
+                   "tokens": T, "users": batch.B, "candidates": n_cand, "d_model": d, "hidden": h, "tasks": nt},
+        "loss": float(loss.item()),
+        "kernels": kernels,
     }
     print(json.dumps(out))
 

@@ -28,6 +28,7 @@ EXPORTED = (
     "mtgr_group_layernorm", "mtgr_group_layernorm_bwd", "mtgr_hstu_attn_fwd", "mtgr_hstu_attn_bwd",
     "mtgr_hstu_layer_fwd", "mtgr_hstu_layer_bwd", "mtgr_hstu_stack_fwd", "mtgr_stack_graph_create",
     "mtgr_stack_graph_launch", "mtgr_stack_graph_destroy", "mtgr_stochastic_length",
+    "mtgr_head_workspace_size", "mtgr_candidate_head_fwd", "mtgr_candidate_head_loss",
 )
 
 
@@ -57,6 +58,15 @@ class LayerGrads(ctypes.Structure):
                 ("gamma1", ctypes.c_void_p), ("beta1", ctypes.c_void_p),
                 ("gamma2", ctypes.c_void_p), ("beta2", ctypes.c_void_p),
                 ("W_o", ctypes.c_void_p), ("b_o", ctypes.c_void_p)]
+
+
+class HeadParams(ctypes.Structure):
+    _fields_ = [("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("W2", ctypes.c_void_p), ("b2", ctypes.c_void_p),
+                ("d", ctypes.c_int32), ("h", ctypes.c_int32), ("n_tasks", ctypes.c_int32)]
+
+
+class HeadGrads(ctypes.Structure):
+    _fields_ = [("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("W2", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
 
 
 class LayerBwdExtras(ctypes.Structure):
@@ -100,6 +110,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mtgr_stack_graph_destroy": ([P], ctypes.c_int),
         "mtgr_stochastic_length": ([P, P, P, P, I64, I32, I64, I32, ctypes.c_int, P, I32, I64, P, P, P, P, I64, P,
                                     P, SZ, P], ctypes.c_int),
+        "mtgr_head_workspace_size": ([I32, I64, I32, I32, I32, ctypes.c_int], SZ),
+        "mtgr_candidate_head_fwd": ([ctypes.POINTER(HeadParams), P, I64, P, P, I32, I64, I64, P, ctypes.c_int, P, SZ,
+                                     P], ctypes.c_int),
+        "mtgr_candidate_head_loss": ([ctypes.POINTER(HeadParams), P, I64, P, P, I32, I64, I64, P, P, P, P, I64,
+                                      ctypes.POINTER(HeadGrads), ctypes.c_int, P, SZ, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -331,3 +346,28 @@ def mtgr_stochastic_length(offsets, group_ids, timestamps, x, u, s_keep: int, to
         _p(offsets), _p(group_ids), _p(timestamps), _p(x), _ld(x), B, T, x.shape[1], dtype_code(x.dtype), _p(u),
         s_keep, token_budget, _p(offsets_out), _p(group_ids_out), _p(timestamps_out), _p(x_out), _ld(x_out),
         _p(fit_out), _p(ws), ws.numel(), _stream(stream)))
+
+
+def make_head_params(p: Dict[str, torch.Tensor]) -> HeadParams:
+    h, d = p["W1"].shape
+    return HeadParams(_p(p["W1"]), _p(p.get("b1")), _p(p["W2"]), _p(p.get("b2")), d, h, p["W2"].shape[0])
+
+
+def head_workspace(B: int, n_cand: int, d: int, h: int, n_tasks: int, dtype: torch.dtype, device="cuda"):
+    n = int(load_library().mtgr_head_workspace_size(B, n_cand, d, h, n_tasks, dtype_code(dtype)))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mtgr_candidate_head_fwd(params: HeadParams, x, offsets, group_ids, n_cand: int, logits, ws, stream=None) -> None:
+    _check("mtgr_candidate_head_fwd", load_library().mtgr_candidate_head_fwd(
+        ctypes.byref(params), _p(x), _ld(x), _p(offsets), _p(group_ids), offsets.numel() - 1, x.shape[0], n_cand,
+        _p(logits), dtype_code(x.dtype), _p(ws), ws.numel(), _stream(stream)))
+
+
+def mtgr_candidate_head_loss(params: HeadParams, x, offsets, group_ids, n_cand: int, labels, loss, logits, dx,
+                             grads: Dict[str, torch.Tensor], ws, stream=None) -> None:
+    g = HeadGrads(_p(grads["W1"]), _p(grads.get("b1")), _p(grads["W2"]), _p(grads.get("b2")))
+    _check("mtgr_candidate_head_loss", load_library().mtgr_candidate_head_loss(
+        ctypes.byref(params), _p(x), _ld(x), _p(offsets), _p(group_ids), offsets.numel() - 1, x.shape[0], n_cand,
+        _p(labels), _p(loss), _p(logits), _p(dx), _ld(dx), ctypes.byref(g), dtype_code(x.dtype), _p(ws), ws.numel(),
+        _stream(stream)))

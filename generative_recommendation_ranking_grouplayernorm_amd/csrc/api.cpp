@@ -203,6 +203,68 @@ int mtgr_stochastic_length(const int32_t* offsets, const uint8_t* group_ids, con
                                   ld_out * (int64_t)elt(dt), fit_out, workspace, S(stream));
 }
 
+static int head_checks(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                       const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, int dt) {
+  if (!p) return MTGR_ERR_INVALID_ARG;
+  if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
+  if (p->n_tasks < 1 || p->n_tasks > 4) return MTGR_ERR_UNSUPPORTED;
+  if (p->d < 8 || p->h < 8 || p->d % 8 || p->h % 8) return MTGR_ERR_UNSUPPORTED;
+  if (!p->W1 || !p->W2) return MTGR_ERR_INVALID_ARG;
+  if (!vec_ok(p->W1, p->d, dt) || !aligned16(p->W2) || (p->b1 && !aligned16(p->b1)) || (p->b2 && !aligned16(p->b2)))
+    return MTGR_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || n_cand < 0 || n_cand > T || T > INT32_MAX) return MTGR_ERR_INVALID_ARG;
+  if (B > 0 && (!offsets || !group_ids)) return MTGR_ERR_INVALID_ARG;
+  if (T > 0 && !x) return MTGR_ERR_INVALID_ARG;
+  if (ld_x < p->d || !vec_ok(x, ld_x, dt)) return MTGR_ERR_INVALID_ARG;
+  return MTGR_OK;
+}
+
+size_t mtgr_head_workspace_size(int32_t B, int64_t n_cand, int32_t d, int32_t h, int32_t n_tasks, int dt) {
+  if (B < 0 || n_cand < 0 || d < 1 || h < 1 || n_tasks < 1 || !dt_ok(dt)) return 0;
+  return head_workspace_bytes(B, n_cand, d, h, n_tasks, dt);
+}
+
+int mtgr_candidate_head_fwd(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                            const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, float* logits, int dt,
+                            void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
+  int r = head_checks(p, x, ld_x, offsets, group_ids, B, T, n_cand, dt);
+  if (r) return r;
+  if (n_cand > 0 && !logits) return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < head_workspace_bytes(B, n_cand, p->d, p->h, p->n_tasks, dt) || !workspace)
+    return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  if (n_cand == 0 || B == 0) return MTGR_OK;
+  HeadArgs a = {};
+  a.offsets = offsets; a.group_ids = group_ids; a.B = B; a.T = T; a.n_cand = n_cand;
+  a.x = x; a.ldx = ld_x; a.d = p->d; a.h = p->h; a.nt = p->n_tasks;
+  a.W1 = p->W1; a.b1 = p->b1; a.W2 = p->W2; a.b2 = p->b2;
+  a.logits = logits;
+  return launch_head(dt, a, workspace, S(stream));
+}
+
+int mtgr_candidate_head_loss(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                             const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, const float* labels,
+                             float* loss, float* logits, void* dx, int64_t ld_dx, const mtgr_head_grads* grads, int dt,
+                             void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
+  int r = head_checks(p, x, ld_x, offsets, group_ids, B, T, n_cand, dt);
+  if (r) return r;
+  if (!loss || !grads || !grads->W1 || !grads->W2) return MTGR_ERR_INVALID_ARG;
+  if ((p->b1 != nullptr) != (grads->b1 != nullptr) || (p->b2 != nullptr) != (grads->b2 != nullptr))
+    return MTGR_ERR_INVALID_ARG;
+  if (n_cand > 0 && !labels) return MTGR_ERR_INVALID_ARG;
+  if (T > 0 && (!dx || ld_dx < p->d || !vec_ok(dx, ld_dx, dt))) return MTGR_ERR_INVALID_ARG;
+  if (dx && dx == x) return MTGR_ERR_INVALID_ARG;
+  if (ws_bytes < head_workspace_bytes(B, n_cand, p->d, p->h, p->n_tasks, dt) || !workspace)
+    return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  HeadArgs a = {};
+  a.offsets = offsets; a.group_ids = group_ids; a.B = B; a.T = T; a.n_cand = B > 0 ? n_cand : 0;
+  a.x = x; a.ldx = ld_x; a.d = p->d; a.h = p->h; a.nt = p->n_tasks;
+  a.W1 = p->W1; a.b1 = p->b1; a.W2 = p->W2; a.b2 = p->b2;
+  a.train = true; a.labels = labels; a.logits = logits; a.loss = loss;
+  a.dx = dx; a.lddx = ld_dx;
+  a.dW1 = grads->W1; a.db1 = grads->b1; a.dW2 = grads->W2; a.db2 = grads->b2;
+  return launch_head(dt, a, workspace, S(stream));
+}
+
 int mtgr_group_layernorm(const void* x, void* y, const void* gamma, const void* beta,
                          const uint8_t* group_ids, int64_t T, int32_t d, int32_t G, float eps, int dt,
                          float* mean_out, float* rstd_out, mtgr_stream_t stream) {

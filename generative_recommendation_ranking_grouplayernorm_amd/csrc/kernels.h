@@ -61,6 +61,31 @@ int launch_stochastic_length(const int32_t* offsets, const uint8_t* g, const int
                              int64_t budget, int32_t* offsets_out, uint8_t* g_out, int64_t* ts_out, void* x_out,
                              int64_t ldo_bytes, int64_t* fit_out, void* ws, hipStream_t stream);
 
+// ---- candidate head and loss ----------------------------------------------
+struct HeadArgs {
+  const int32_t* offsets; const uint8_t* group_ids; int B; int64_t T; int64_t n_cand;
+  const void* x; int64_t ldx;
+  int d, h, nt;
+  const void* W1; const void* b1; const void* W2; const void* b2;
+  bool train;           // loss and backward too
+  const float* labels;  // [n_cand, nt] when train
+  float* logits;        // [n_cand, nt] or NULL
+  float* loss;          // [1]
+  void* dx; int64_t lddx;
+  float* dW1; float* db1; float* dW2; float* db2;
+};
+struct HeadWs {
+  int32_t* seg; int32_t* cand_off;
+  char* xc; char* z1; char* hc; char* dz1;
+  float* dz; float* loss_k;
+  char* dxc; char* red;
+  size_t bytes;
+};
+HeadWs head_carve(void* ws, int B, int64_t n_cand, int d, int h, int nt, int dt);
+size_t head_workspace_bytes(int B, int64_t n_cand, int d, int h, int nt, int dt);
+int head_split(int M, int N, int K);
+int launch_head(int dt, const HeadArgs& a, void* ws, hipStream_t stream);
+
 // ---- a2/a5: group norm rows ---------------------------------------------
 // y = GLN(x) (mode plain) or y = GLN(x) * u (mode gate).
 int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,

@@ -16,9 +16,10 @@
  *          order: linear+SiLU gives U,Q,K,V; SiLU(QK^T) without softmax;
  *          normalise the aggregate, gate by U, one linear layer),
  *          训练数据怎么组织 (jagged rows, timestamps kept for the mask).
- *   [fr]   "MTGR：混合范式建模" (fun-rec 7.3): 7.3.3 (GLN formula),
- *          7.3.4 (the three mask rules).
- *   [blog] also 11.3 (batches sized by token count).
+ *   [fr]   "MTGR：混合范式建模" (fun-rec 7.3): 7.3.1 (loss at candidate
+ *          positions), 7.3.3 (GLN formula), 7.3.4 (the three mask rules).
+ *   [blog] also 5.4, 6, 7 (candidate head and loss) and 11.3 (batches
+ *          sized by token count).
  *   [dr]   paper-daily deep reading of the Meituan blog post: 2 方法详解
  *          (extra norm on every layer's input), 3 核心技术贡献 and
  *          4 实验结果分析 / 工程指标 (fp16 serving, graph replay, P99).
@@ -110,6 +111,64 @@ size_t mtgr_workspace_size(int op, int32_t B, int64_t T, int32_t max_len, int32_
  */
 int mtgr_jagged_prep(const int32_t* offsets, const uint8_t* group_ids, int32_t B, int64_t T,
                      int32_t* seg, void* workspace, size_t ws_bytes, mtgr_stream_t stream);
+
+/* Candidate head weights (device, dtype dt): W1 [h, d], b1 [h] or NULL,
+ * W2 [n_tasks, h], b2 [n_tasks] or NULL; d and h multiples of 8, 1 <= n_tasks
+ * <= 4. */
+typedef struct {
+  const void* W1;
+  const void* b1;
+  const void* W2;
+  const void* b2;
+  int32_t d, h, n_tasks;
+} mtgr_head_params;
+
+/* fp32 head gradients, OVERWRITTEN; b1 / b2 non-NULL exactly when the
+ * params have them. */
+typedef struct {
+  float* W1; /* [h, d] */
+  float* b1; /* [h] */
+  float* W2; /* [n_tasks, h] */
+  float* b2; /* [n_tasks] */
+} mtgr_head_grads;
+
+/* Workspace bytes of the two head calls below. */
+size_t mtgr_head_workspace_size(int32_t B, int64_t n_cand, int32_t d, int32_t h, int32_t n_tasks, int dt);
+
+/*
+ * Candidate head after the last layer ([blog] 5.4 and 7: the candidate
+ * tokens' outputs pass through an MLP to logits; [pd] 它解决什么问题: a click
+ * rate and a conversion rate for every exposed candidate).  Reading: for the
+ * candidate (group C) tokens in batch order,
+ *   logits = SiLU(x_c W1^T + b1) W2^T + b2      [n_cand, n_tasks] fp32.
+ *   x       : [T, d] the last layer's output, row stride ld_x, dtype dt
+ *   n_cand  : the number of group-C tokens in the batch (the caller's data
+ *             loader knows it); a wrong count gives undefined logits but no
+ *             access outside the stated buffers
+ *   workspace : mtgr_head_workspace_size bytes
+ */
+int mtgr_candidate_head_fwd(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                            const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, float* logits, int dt,
+                            void* workspace, size_t ws_bytes, mtgr_stream_t stream);
+
+/*
+ * Forward, discriminative loss and backward of the candidate head ([blog] 6
+ * and [fr] 7.3.1: a ranking loss at candidate positions only, not next-token
+ * prediction).  Reading: loss = (1 / n_cand) sum over candidates and tasks
+ * of the binary cross-entropy of the task's logit against its label.
+ *   labels : [n_cand, n_tasks] fp32 in [0, 1] (device)
+ *   loss   : [1] fp32 (device), written
+ *   logits : [n_cand, n_tasks] fp32 or NULL
+ *   dx     : [T, d] dtype dt, row stride ld_dx: d loss / d x, zero on every
+ *            non-candidate row (the upstream gradient of the last layer's
+ *            backward); must not alias x
+ *   grads  : head weight gradients, fp32, overwritten
+ *   workspace : mtgr_head_workspace_size bytes
+ */
+int mtgr_candidate_head_loss(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                             const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, const float* labels,
+                             float* loss, float* logits, void* dx, int64_t ld_dx, const mtgr_head_grads* grads,
+                             int dt, void* workspace, size_t ws_bytes, mtgr_stream_t stream);
 
 /*
  * Stochastic Length sampling in front of the training path, and the cut of
