@@ -417,7 +417,8 @@ def serving_bench(args):
     """One request (one user, 1000 history tokens, 32 real-time tokens, K
     candidates) through 22 fp16 layers of d_model 1024, per K in the sweep.
     Three ways to issue it: 22 single-layer calls from Python, one stack
-    call, one graph launch.  Latency = host clock from the first call to the
+    call, one graph launch; and the graph of the whole request (layers and
+    the candidate head's logits, 1024 -> 512 -> 2 tasks).  Latency = host clock from the first call to the
     end of a stream synchronisation, one request at a time; throughput =
     requests issued back to back on one stream, then one synchronisation.
     GPU time = the summed kernel durations of one request (HIP events around
@@ -443,6 +444,11 @@ def serving_bench(args):
     keep = [{k: to(getattr(p, k)) for k in ("W_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o")}
             for p in params]
     lps = [mb.make_params(t, H) for t in keep]
+    from mtgr_inputs import make_head_params
+
+    hp = make_head_params(d, 512, 2, np.random.default_rng([args.seed, 5, 77]), True)
+    hdev = {k: to(getattr(hp, k)) for k in ("W1", "b1", "W2", "b2")}
+    hprm = mb.make_head_params(hdev)
     stream = torch.cuda.current_stream()
     n = max(args.requests, 10)
     results = {}
@@ -459,6 +465,11 @@ def serving_bench(args):
         ws_s = mb.workspace(mb.OP_STACK_FWD, 1, T, d, H, dt, dev)
         h2 = torch.empty_like(xd)
         graph = mb.mtgr_stack_graph_create(lps, xd, y, off, g, ts, scale, ws_s)
+        logits = torch.empty(K, 2, device=dev)
+        ws_h = mb.head_workspace(1, K, d, 512, 2, dt, dev)
+        ws_s2 = mb.workspace(mb.OP_STACK_FWD, 1, T, d, H, dt, dev)
+        y2 = torch.empty_like(xd)
+        graph_h = mb.mtgr_serving_graph_create(lps, hprm, xd, y2, logits, K, off, g, ts, scale, ws_s2, ws_h)
 
         def layers():
             src, dst = xd, (y if L % 2 == 1 else h2)
@@ -472,7 +483,10 @@ def serving_bench(args):
         def replay():
             graph.launch(stream)
 
-        modes = {"layer_calls": layers, "stack_call": stack, "graph": replay}
+        def replay_head():
+            graph_h.launch(stream)
+
+        modes = {"layer_calls": layers, "stack_call": stack, "graph": replay, "graph_with_head": replay_head}
         res = {}
         for name, fn in modes.items():
             for _ in range(max(args.warmup, 3)):
@@ -507,6 +521,7 @@ def serving_bench(args):
         res["tokens"] = T
         res["fwd_gflop"] = round(L * (4 * d * P + fl.layer_gemm_flops(T, d, backward=False)) / 1e9, 2)
         graph.close()
+        graph_h.close()
         results[K] = res
         print(f"[bench] K={K}: " + ", ".join(f"{m} p50 {res[m]['p50_ms']} ms" for m in modes),
               file=sys.stderr, flush=True)

@@ -28,7 +28,7 @@ EXPORTED = (
     "mtgr_group_layernorm", "mtgr_group_layernorm_bwd", "mtgr_hstu_attn_fwd", "mtgr_hstu_attn_bwd",
     "mtgr_hstu_layer_fwd", "mtgr_hstu_layer_bwd", "mtgr_hstu_stack_fwd", "mtgr_stack_graph_create",
     "mtgr_stack_graph_launch", "mtgr_stack_graph_destroy", "mtgr_stochastic_length",
-    "mtgr_head_workspace_size", "mtgr_candidate_head_fwd", "mtgr_candidate_head_loss",
+    "mtgr_head_workspace_size", "mtgr_candidate_head_fwd", "mtgr_candidate_head_loss", "mtgr_serving_graph_create",
 )
 
 
@@ -115,6 +115,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      P], ctypes.c_int),
         "mtgr_candidate_head_loss": ([ctypes.POINTER(HeadParams), P, I64, P, P, I32, I64, I64, P, P, P, P, I64,
                                       ctypes.POINTER(HeadGrads), ctypes.c_int, P, SZ, P], ctypes.c_int),
+        "mtgr_serving_graph_create": ([ctypes.POINTER(LayerParams), I32, ctypes.POINTER(HeadParams), P, P, P, I64, P,
+                                       P, P, I32, I64, F, ctypes.c_int, P, SZ, P, SZ,
+                                       ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -371,3 +374,16 @@ def mtgr_candidate_head_loss(params: HeadParams, x, offsets, group_ids, n_cand: 
         ctypes.byref(params), _p(x), _ld(x), _p(offsets), _p(group_ids), offsets.numel() - 1, x.shape[0], n_cand,
         _p(labels), _p(loss), _p(logits), _p(dx), _ld(dx), ctypes.byref(g), dtype_code(x.dtype), _p(ws), ws.numel(),
         _stream(stream)))
+
+
+def mtgr_serving_graph_create(layers: Sequence[LayerParams], head: HeadParams, x_in, x_out, logits, n_cand: int,
+                              offsets, group_ids, timestamps, attn_scale, ws, head_ws) -> StackGraph:
+    arr, L = _layer_array(layers)
+    B = offsets.numel() - 1
+    T = x_in.shape[0]
+    h = ctypes.c_void_p()
+    _check("mtgr_serving_graph_create", load_library().mtgr_serving_graph_create(
+        arr, L, ctypes.byref(head), _p(x_in), _p(x_out), _p(logits), n_cand, _p(offsets), _p(group_ids),
+        _p(timestamps), B, T, attn_scale, dtype_code(x_in.dtype), _p(ws), ws.numel(), _p(head_ws), head_ws.numel(),
+        ctypes.byref(h)))
+    return StackGraph(h.value, (x_in, x_out, logits, offsets, group_ids, timestamps, ws, head_ws))

@@ -203,8 +203,10 @@ int mtgr_stochastic_length(const int32_t* offsets, const uint8_t* group_ids, con
                                   ld_out * (int64_t)elt(dt), fit_out, workspace, S(stream));
 }
 
-static int head_checks(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
-                       const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, int dt) {
+}  // extern "C"
+
+int mtgr::head_validate(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                        const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, int dt) {
   if (!p) return MTGR_ERR_INVALID_ARG;
   if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
   if (p->n_tasks < 1 || p->n_tasks > 4) return MTGR_ERR_UNSUPPORTED;
@@ -219,6 +221,8 @@ static int head_checks(const mtgr_head_params* p, const void* x, int64_t ld_x, c
   return MTGR_OK;
 }
 
+extern "C" {
+
 size_t mtgr_head_workspace_size(int32_t B, int64_t n_cand, int32_t d, int32_t h, int32_t n_tasks, int dt) {
   if (B < 0 || n_cand < 0 || d < 1 || h < 1 || n_tasks < 1 || !dt_ok(dt)) return 0;
   return head_workspace_bytes(B, n_cand, d, h, n_tasks, dt);
@@ -227,7 +231,7 @@ size_t mtgr_head_workspace_size(int32_t B, int64_t n_cand, int32_t d, int32_t h,
 int mtgr_candidate_head_fwd(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
                             const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, float* logits, int dt,
                             void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
-  int r = head_checks(p, x, ld_x, offsets, group_ids, B, T, n_cand, dt);
+  int r = head_validate(p, x, ld_x, offsets, group_ids, B, T, n_cand, dt);
   if (r) return r;
   if (n_cand > 0 && !logits) return MTGR_ERR_INVALID_ARG;
   if (ws_bytes < head_workspace_bytes(B, n_cand, p->d, p->h, p->n_tasks, dt) || !workspace)
@@ -245,7 +249,7 @@ int mtgr_candidate_head_loss(const mtgr_head_params* p, const void* x, int64_t l
                              const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, const float* labels,
                              float* loss, float* logits, void* dx, int64_t ld_dx, const mtgr_head_grads* grads, int dt,
                              void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
-  int r = head_checks(p, x, ld_x, offsets, group_ids, B, T, n_cand, dt);
+  int r = head_validate(p, x, ld_x, offsets, group_ids, B, T, n_cand, dt);
   if (r) return r;
   if (!loss || !grads || !grads->W1 || !grads->W2) return MTGR_ERR_INVALID_ARG;
   if ((p->b1 != nullptr) != (grads->b1 != nullptr) || (p->b2 != nullptr) != (grads->b2 != nullptr))

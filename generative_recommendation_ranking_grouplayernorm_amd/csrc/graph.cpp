@@ -1,5 +1,6 @@
-// Captured stack forwards: one mtgr_hstu_stack_fwd call recorded as a HIP
-// graph on a private stream, then replayed with a single launch.
+// Captured serving forwards: one mtgr_hstu_stack_fwd call (and, for a
+// serving graph, the candidate head after it) recorded as a HIP graph on a
+// private stream, then replayed with a single launch.
 #include <new>
 
 #include "kernels.h"
@@ -20,23 +21,9 @@ void release(mtgr_graph_s* g) {
   delete g;
 }
 
-}  // namespace
-
-extern "C" {
-
-int mtgr_stack_graph_create(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
-                            const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
-                            int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
-                            mtgr_graph* out) {
-  if (!out) return MTGR_ERR_INVALID_ARG;
-  *out = nullptr;
-  // Timing events recorded during capture would become graph nodes.
-  if (profiling_enabled()) return MTGR_ERR_INVALID_ARG;
-  // Empty batches launch nothing; refuse them here so that every handle
-  // holds a graph with work in it.
-  if (T <= 0 || B <= 0) return MTGR_ERR_INVALID_ARG;
-  int r = stack_fwd_validate(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, dt, workspace, ws_bytes);
-  if (r) return r;
+// Records fn(stream) on a private stream and instantiates the graph.
+template <typename F>
+int capture(F fn, mtgr_graph* out) {
   hipStream_t cs = nullptr;
   if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MTGR_ERR_HIP;
   mtgr_graph_s* g = new (std::nothrow) mtgr_graph_s;
@@ -44,11 +31,11 @@ int mtgr_stack_graph_create(const mtgr_layer_params* layers, int32_t L, const vo
     (void)hipStreamDestroy(cs);
     return MTGR_ERR_HIP;
   }
+  int r;
   if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
     r = MTGR_ERR_HIP;
   } else {
-    r = mtgr_hstu_stack_fwd(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt,
-                            workspace, ws_bytes, (mtgr_stream_t)cs);
+    r = fn((mtgr_stream_t)cs);
     // End the capture whatever happened, so the stream is usable again.
     hipGraph_t graph = nullptr;
     const hipError_t e = hipStreamEndCapture(cs, &graph);
@@ -68,6 +55,58 @@ int mtgr_stack_graph_create(const mtgr_layer_params* layers, int32_t L, const vo
   }
   *out = g;
   return MTGR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtgr_stack_graph_create(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                            const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                            int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                            mtgr_graph* out) {
+  if (!out) return MTGR_ERR_INVALID_ARG;
+  *out = nullptr;
+  // Timing events recorded during capture would become graph nodes.
+  if (profiling_enabled()) return MTGR_ERR_INVALID_ARG;
+  // Empty batches launch nothing; refuse them here so that every handle
+  // holds a graph with work in it.
+  if (T <= 0 || B <= 0) return MTGR_ERR_INVALID_ARG;
+  int r = stack_fwd_validate(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, dt, workspace, ws_bytes);
+  if (r) return r;
+  return capture(
+      [&](mtgr_stream_t s) {
+        return mtgr_hstu_stack_fwd(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt,
+                                   workspace, ws_bytes, s);
+      },
+      out);
+}
+
+int mtgr_serving_graph_create(const mtgr_layer_params* layers, int32_t L, const mtgr_head_params* head,
+                              const void* x_in, void* x_out, float* logits, int64_t n_cand,
+                              const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
+                              int32_t B, int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                              void* head_ws, size_t head_ws_bytes, mtgr_graph* out) {
+  if (!out) return MTGR_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (profiling_enabled()) return MTGR_ERR_INVALID_ARG;
+  if (T <= 0 || B <= 0 || n_cand < 1 || !logits) return MTGR_ERR_INVALID_ARG;
+  int r = stack_fwd_validate(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, dt, workspace, ws_bytes);
+  if (r) return r;
+  r = head_validate(head, x_out, layers[0].d, offsets, group_ids, B, T, n_cand, dt);
+  if (r) return r;
+  if (head->d != layers[0].d) return MTGR_ERR_INVALID_ARG;
+  if (head_ws_bytes < head_workspace_bytes(B, n_cand, head->d, head->h, head->n_tasks, dt) || !head_ws)
+    return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  return capture(
+      [&](mtgr_stream_t s) {
+        int rr = mtgr_hstu_stack_fwd(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt,
+                                     workspace, ws_bytes, s);
+        if (rr) return rr;
+        return mtgr_candidate_head_fwd(head, x_out, layers[0].d, offsets, group_ids, B, T, n_cand, logits, dt,
+                                       head_ws, head_ws_bytes, s);
+      },
+      out);
 }
 
 int mtgr_stack_graph_launch(mtgr_graph g, mtgr_stream_t stream) {

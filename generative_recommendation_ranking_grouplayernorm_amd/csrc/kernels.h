@@ -85,6 +85,9 @@ HeadWs head_carve(void* ws, int B, int64_t n_cand, int d, int h, int nt, int dt)
 size_t head_workspace_bytes(int B, int64_t n_cand, int d, int h, int nt, int dt);
 int head_split(int M, int N, int K);
 int launch_head(int dt, const HeadArgs& a, void* ws, hipStream_t stream);
+// Host-side argument checks shared by the head entry points.
+int head_validate(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                  const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, int dt);
 
 // ---- a2/a5: group norm rows ---------------------------------------------
 // y = GLN(x) (mode plain) or y = GLN(x) * u (mode gate).

@@ -82,6 +82,7 @@ typedef enum {
 } mtgr_op;
 
 typedef void* mtgr_stream_t; /* hipStream_t */
+typedef struct mtgr_graph_s* mtgr_graph; /* a captured launch sequence (see mtgr_stack_graph_create) */
 
 /* Library version string, e.g. "mtgr-hstu 0.1.0 gfx950". Host memory, static. */
 const char* mtgr_version(void);
@@ -169,6 +170,7 @@ int mtgr_candidate_head_loss(const mtgr_head_params* p, const void* x, int64_t l
                              const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, const float* labels,
                              float* loss, float* logits, void* dx, int64_t ld_dx, const mtgr_head_grads* grads,
                              int dt, void* workspace, size_t ws_bytes, mtgr_stream_t stream);
+
 
 /*
  * Stochastic Length sampling in front of the training path, and the cut of
@@ -392,13 +394,28 @@ int mtgr_hstu_stack_fwd(const mtgr_layer_params* layers, int32_t L, const void* 
  *   mtgr_stack_graph_destroy: releases the handle (NULL is accepted); the
  *     caller ensures no launch of it is still pending.
  */
-typedef struct mtgr_graph_s* mtgr_graph;
 int mtgr_stack_graph_create(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
                             const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
                             int32_t B, int64_t T, float attn_scale, int dt, void* workspace,
                             size_t ws_bytes, mtgr_graph* out);
 int mtgr_stack_graph_launch(mtgr_graph g, mtgr_stream_t stream);
 int mtgr_stack_graph_destroy(mtgr_graph g);
+
+/*
+ * A whole serving request as one graph: mtgr_hstu_stack_fwd and then
+ * mtgr_candidate_head_fwd on its output, recorded once and replayed with
+ * mtgr_stack_graph_launch (released with mtgr_stack_graph_destroy).  The
+ * scores of [pd] 计算量涨了 65 倍 (one pass per request, all candidates) come
+ * out as logits [n_cand, n_tasks] fp32.  Same rules as
+ * mtgr_stack_graph_create; n_cand >= 1; head->d equals the layers' d;
+ * workspace: MTGR_OP_STACK_FWD bytes, head_ws: mtgr_head_workspace_size
+ * bytes (distinct buffers).
+ */
+int mtgr_serving_graph_create(const mtgr_layer_params* layers, int32_t L, const mtgr_head_params* head,
+                              const void* x_in, void* x_out, float* logits, int64_t n_cand,
+                              const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
+                              int32_t B, int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
+                              void* head_ws, size_t head_ws_bytes, mtgr_graph* out);
 
 /*
  * a6..a2 backward (a8 plus the attention backward a7): from dx_out computes

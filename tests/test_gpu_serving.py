@@ -8,7 +8,8 @@ import pytest
 import torch
 
 from mtgr_inputs import CONFIGS, config_inputs, make_activations, make_batch_from_lengths
-from mtgr_inputs import make_layer_params, make_probe_head
+from mtgr_inputs import make_head_params, make_layer_params, make_probe_head
+from oracle import candidate_head as chd
 from oracle import mtgr_oracle as orc
 from tests.gpu_util import TOL, f64, meta, params_to, rel_l2, rounded, say
 
@@ -218,3 +219,61 @@ def test_serving_graph_replay_matches_eager(mb):
     assert torch.equal(buf_y[:T], e_y)
     for gr in graphs.values():
         gr.close()
+
+
+def test_serving_graph_with_candidate_head(mb):
+    """One request = 22 fp16 layers and the candidate head (1024 -> 512 -> 2
+    tasks) in one graph.  Replays give the eager logits bit for bit; at K=20
+    the scores sigmoid(logit) of both tasks are within the pages' 6e-3 of the
+    fp64 oracle run on the same rounded inputs and weights."""
+    cfg = CONFIGS[5]
+    dtype = torch.float16
+    d, H = cfg["d"], cfg["H"]
+    _, params, _ = config_inputs(5)
+    lps, keep, qs = device_layers(mb, params, dtype)
+    hp = make_head_params(d, 512, 2, np.random.default_rng([0, 5, 77]), True)
+    hdev = {k: rounded(getattr(hp, k), dtype).to(DEV) for k in ("W1", "b1", "W2", "b2")}
+    hprm = mb.make_head_params(hdev)
+
+    class HQ:
+        pass
+
+    hq = HQ()
+    for k in ("W1", "b1", "W2", "b2"):
+        setattr(hq, k, f64(hdev[k]))
+    for K in (20, 1000):
+        batch, _, x = config_inputs(5, K=K)
+        T = batch.T
+        scale = 1.0 / batch.max_len
+        off, g, ts = meta(batch, DEV)
+        xs = rounded(x, dtype).to(DEV)
+        ys = torch.empty_like(xs)
+        logits = torch.full((K, 2), float("nan"), device=DEV)
+        ws = mb.workspace(mb.OP_STACK_FWD, 1, T, d, H, dtype, DEV)
+        hws = mb.head_workspace(1, K, d, 512, 2, dtype, DEV)
+        gr = mb.mtgr_serving_graph_create(lps, hprm, xs, ys, logits, K, off, g, ts, scale, ws, hws)
+        # eager reference on its own buffers
+        e_y = torch.empty_like(xs)
+        e_logits = torch.empty(K, 2, device=DEV)
+        e_ws = mb.workspace(mb.OP_STACK_FWD, 1, T, d, H, dtype, DEV)
+        e_hws = mb.head_workspace(1, K, d, 512, 2, dtype, DEV)
+        mb.mtgr_hstu_stack_fwd(lps, xs, e_y, off, g, ts, scale, e_ws)
+        mb.mtgr_candidate_head_fwd(hprm, e_y, off, g, K, e_logits, e_hws)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            logits.fill_(float("nan"))
+            gr.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(logits, e_logits), f"K={K}: replay {rep} logits differ from the eager call"
+            mb.mtgr_hstu_stack_fwd(lps[:1], xs, torch.empty_like(xs), off, g, ts, scale, e_ws)
+            torch.cuda.synchronize()
+        if K == 20:
+            ref = orc.stack_fwd(qs, f64(xs), batch.offsets, batch.group_ids, batch.timestamps, 1.0, scale)
+            lg_ref, _ = chd.head_fwd(hq, ref, batch.group_ids)
+            s_gpu = 1.0 / (1.0 + np.exp(-logits.cpu().numpy().astype(np.float64)))
+            s_ref = 1.0 / (1.0 + np.exp(-lg_ref))
+            dmax = float(np.max(np.abs(s_gpu - s_ref)))
+            say(f"  K=20 head scores vs oracle: max |diff| {dmax:.2e} over {s_ref.size} scores")
+            assert dmax <= SCORE_BOUND
+        gr.close()
+        say(f"  K={K}: serving graph with head, replays equal the eager call")
