@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--requests", type=int, default=200, help="timed requests per K and mode (--serving)")
     ap.add_argument("--head", action="store_true",
                     help="time the candidate head with its loss and backward on the 65,536-token batch")
+    ap.add_argument("--forward-batches", action="store_true",
+                    help="users/s of the forward-only workloads: one bf16 d_model 512 layer over 32 users, and the "
+                         "22-layer fp16 d_model 1024 stack over 64 users (one graph)")
     ap.add_argument("--stochastic-length", type=int, default=0, metavar="S_KEEP",
                     help="time Stochastic Length sampling (histories cut to S_KEEP tokens) of a long-tail user "
                          "pool and the layer step on the 65,536-token batch cut from it, against the batch "
@@ -274,6 +277,9 @@ def main():
         return
     if args.head:
         head_bench(args)
+        return
+    if args.forward_batches:
+        forward_batches_bench(args)
         return
     import numpy as np
     import torch
@@ -764,6 +770,64 @@ def head_bench(args):
         "loss": float(loss.item()),
         "kernels": kernels,
     }
+    print(json.dumps(out))
+
+
+def forward_batches_bench(args):
+    """Forward-only throughput of two batch workloads: a bf16 layer of
+    d_model 512 (4 heads of 128) over 32 long-tail users, users/s =
+    B / t_layer_fwd; and 22 fp16 layers of d_model 1024 (8 heads of 128) over
+    64 users, users/s = B / t_22-layer fwd, with the forward GFLOP per user
+    (context: the pages print 137.87 GFLOPs per sample for their 22-layer,
+    d_model 1024 model, counted their own way).  HIP events around timed
+    repeats after warm-up; inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import generative_recommendation_ranking_grouplayernorm_amd.binding as mb
+    from generative_recommendation_ranking_grouplayernorm_amd import flops as fl
+    from mtgr_inputs import CONFIGS, config_inputs
+
+    dev = torch.device("cuda:0")
+    mb.load_library()
+    stream = torch.cuda.current_stream()
+    out = {"metric": "users/sec of forward-only batch workloads", "n_gpus": 1, "data": "synthetic",
+           "higher_is_better": True, "workloads": {}}
+    for cfg_id, dt in ((2, torch.bfloat16), (3, torch.float16)):
+        cfg = CONFIGS[cfg_id]
+        batch, params, x = config_inputs(cfg_id, seed=args.seed)
+        d, H, L = cfg["d"], cfg["H"], cfg["layers"]
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dt).to(dev)
+        keep = [{k: to(getattr(p, k)) for k in ("W_uqkv", "gamma1", "beta1", "gamma2", "beta2", "W_o")}
+                for p in params]
+        lps = [mb.make_params(t, H) for t in keep]
+        xd = to(x)
+        y = torch.empty_like(xd)
+        off = torch.from_numpy(batch.offsets).to(dev)
+        g = torch.from_numpy(batch.group_ids).to(dev)
+        ts = torch.from_numpy(batch.timestamps).to(dev)
+        scale = 1.0 / batch.max_len
+        ws = mb.workspace(mb.OP_STACK_FWD, batch.B, batch.T, d, H, dt, dev)
+        graph = mb.mtgr_stack_graph_create(lps, xd, y, off, g, ts, scale, ws)
+        for _ in range(max(args.warmup, 3)):
+            graph.launch(stream)
+        torch.cuda.synchronize()
+        reps = max(args.steps, 5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.launch(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        graph.close()
+        P = fl.visible_pairs(batch.offsets, batch.group_ids, batch.timestamps)
+        gflop = L * (4 * d * P + fl.layer_gemm_flops(batch.T, d, backward=False)) / 1e9
+        out["workloads"][cfg["name"]] = {
+            "dtype": "bf16" if dt == torch.bfloat16 else "f16", "layers": L, "users": batch.B, "tokens": batch.T,
+            "d_model": d, "heads": H, "ms_per_batch": round(ms, 4), "users_per_sec": round(batch.B / (ms / 1e3), 1),
+            "fwd_gflop_per_user": round(gflop / batch.B, 2), "tflops": round(gflop / ms, 1)}
+        print(f"[bench] {cfg['name']}: {ms:.3f} ms, {batch.B / (ms / 1e3):.0f} users/s", file=sys.stderr, flush=True)
     print(json.dumps(out))
 
 
