@@ -129,6 +129,19 @@ __device__ __forceinline__ op8 pack_kstep(const float (&v)[2][16], int u) {
 // Scheduling hint for a run of N MFMAs each fed by one LDS read: keep AHEAD
 // reads in flight ahead of the MFMA that consumes them, so that a wave does
 // not stall on LDS latency before every MFMA.  Only orders instructions.
+// As pipeline_lds_mfma for NM MFMAs fed by two LDS reads each (transposed
+// operands): AHEAD reads first, then one MFMA per two reads.
+template <int NM, int AHEAD>
+__device__ __forceinline__ void pipeline_lds2_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < NM - AHEAD / 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD / 2, 0);
+}
+
 template <int N, int AHEAD>
 __device__ __forceinline__ void pipeline_lds_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
@@ -548,6 +561,47 @@ __device__ __forceinline__ op8 row_operand_swz(const uint16_t* s, int r0, int ks
   return o;
 }
 
+// B operand from a QuadRows tile read transposed (gfx950 LDS transpose
+// load): column 32 c + l32 of the tile over contraction rows 16 u + 4 g +
+// (j % 4) + 8 (j / 4) (g = lane / 32, j = 0..7: the permuted k order of
+// pack_kstep), as two 4-row x 16-column quarter-wave blocks.  A lane's 8-byte
+// piece never straddles a 16-byte chunk, so the row swizzle only moves whole
+// chunks.  Lane i of quarter G reads row 16 u + 4 g + i / 4 + 8 h (h = 0, 1)
+// at column 32 c + 16 (G % 2) + 4 (i % 4); with DH = 128 the swizzled chunk
+// is 4 ((c ^ u ^ i / 4) % 4) + ((2 (G % 2) + (i % 4) / 2) ^ (g + 2 h)), so a
+// lane needs only 8 base addresses, picked by (c ^ u) % 4 and h; u adds 16
+// rows, an immediate offset.
+template <int DH>
+struct TrAddr {
+  int a[4][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int G = lane >> 4, i = lane & 15, q = i >> 2, g = G >> 1;
+    const int chl = 2 * (G & 1) + ((i & 3) >> 1), sub = (i & 1) * 4;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 4 * g + q + 8 * h;
+        if (DH == 128) {
+          a[v][h] = row * 128 + 8 * (4 * ((v ^ q) & 3) + (chl ^ (g + 2 * h))) + sub;
+        } else {
+          // padded rows: column 32 c + 16 (G % 2) + 4 (i % 4), no swizzle
+          a[v][h] = row * QuadRows<DH>::PITCH + 16 * (G & 1) + 4 * (i & 3);
+        }
+      }
+  }
+  // operand (u, c) of tile s
+  __device__ __forceinline__ op8 get(const uint16_t* s, int u, int c) const {
+    const int v = DH == 128 ? ((c ^ u) & 3) : 0;
+    const int imm = DH == 128 ? u * 16 * 128 : u * 16 * QuadRows<DH>::PITCH + 32 * c;
+    const uint2 lo = lds_read_tr16(s + a[v][0] + imm);
+    const uint2 hi = lds_read_tr16(s + a[v][1] + imm);
+    op8 o;
+    o.v[0] = lo.x; o.v[1] = lo.y; o.v[2] = hi.x; o.v[3] = hi.y;
+    return o;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Elementwise SiLU terms of a 64 x 32 score tile (two 32 x 32 accumulators),
 // with or without the mask test.  Kept as straight-line code per variant so
@@ -789,8 +843,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   struct Smem {
     uint16_t Qs[2][QuadRows<DH>::SIZE];
     uint16_t Ds[2][QuadRows<DH>::SIZE];
-    uint16_t Qt[2][DH * VT_PITCH];
-    uint16_t Dt[2][DH * VT_PITCH];
     uint32_t Fx[4][32 * 16 * 2];  // per group: 2 x 16 x 32 lanes
     int64_t Tq[2][KV_BQ];         // query timestamps of the stage
   };
@@ -800,8 +852,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   } sm;
   auto& Qs = sm.m.Qs;
   auto& Ds = sm.m.Ds;
-  auto& Qt = sm.m.Qt;
-  auto& Dt = sm.m.Dt;
   auto& Fx = sm.m.Fx;
   auto& Tq = sm.m.Tq;
   int tile, h;
@@ -865,13 +915,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     if (!full && wave == 0) rt = ts_load(ts, q0, qhi, lane);
   };
   auto swrite = [&](int buf) {
-    if (producer) {
-      quad_swrite_swz<DH>(Qs[buf], ld);
-      vt_swrite<DH>(Qt[buf], ld);
-    } else {
-      quad_swrite_swz<DH>(Ds[buf], ld);
-      vt_swrite<DH>(Dt[buf], ld);
-    }
+    quad_swrite_swz<DH>(producer ? Qs[buf] : Ds[buf], ld);
     if (!full && wave == 0) Tq[buf][lane] = rt;
   };
   const int nqt = (qhi - qlo + KV_BQ - 1) / KV_BQ;
@@ -881,6 +925,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   }
   __syncthreads();
   uint32_t* fx = Fx[grp];
+  TrAddr<DH> tra;
+  tra.init(lane);
   for (int it = 0; it < nqt; ++it) {
     const int buf = it & 1, q0 = qlo + it * KV_BQ;
     gload(q0 + KV_BQ);  // past the query range: zeros, never used
@@ -921,13 +967,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
         for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(w[u].v, (u32x4_t*)(dp + u * 1024));
       }
     }
-    // phase 2: dV += P^T dO (producer) or dK += dS^T Q (consumer)
-    const uint16_t* Bt = producer ? Dt[buf] : Qt[buf];
+    // phase 2: dV += P^T dO (producer) or dK += dS^T Q (consumer), the B
+    // operand read transposed from the other role's row-major tile
+    const uint16_t* Bt = producer ? Ds[buf] : Qs[buf];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], vt_operand(Bt, u, c * 32, lane), acc[c]);
-    pipeline_lds_mfma<4 * NC, 8>();
+      for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], tra.get(Bt, u, c), acc[c]);
+    pipeline_lds2_mfma<4 * NC, 8>();
     swrite(buf ^ 1);
     __syncthreads();
   }
