@@ -553,6 +553,18 @@ __device__ __forceinline__ void quad_swrite_swz(uint16_t* s, const VtLoad<DH>& L
 #pragma unroll
   for (int r = 0; r < 4; ++r) *(uint4*)(s + QuadRows<DH>::off(4 * L.kq + r, L.c)) = L.x[r];
 }
+// Rows of a tile loaded by tile_gload_rows (thread chunks c = tid + 256 i,
+// row c / (DH/8)) written to a QuadRows tile.
+template <int DH, int ROWS>
+__device__ __forceinline__ void tile_swrite_swz(uint16_t* s, const uint4* r, int tid) {
+  constexpr int CPR = DH / 8;
+  constexpr int CH = ROWS * CPR / 256;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + 256 * i;
+    *(uint4*)(s + QuadRows<DH>::off(c / CPR, c % CPR)) = r[i];
+  }
+}
 // A operand from a QuadRows tile: row r0 + l32, 8 columns at 16 ks + 8 g.
 template <int DH>
 __device__ __forceinline__ op8 row_operand_swz(const uint16_t* s, int r0, int ks, int lane) {
@@ -878,16 +890,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   const int64_t tk = ts[kr];
   const int hc = h * DH;
   const bool full = k0 + KV_BK <= s_end;  // every query sees these keys
-  // dS store target of this (dA-side) wave: see attn_bwd_dq_stream for the layout
-  uint8_t* dsw = nullptr;
+  // dS store target of this (dA-side) wave: see attn_bwd_dq_stream for the
+  // layout.  dsb is the wave's block at query stage 0 (same on every lane).
+  const uint8_t* dsb = dS;
   int64_t ds_qt_stride = 0;
+  bool ds_on = false;
   if (STORE && !producer) {
     const int nt = (hi - lo + 127) >> 7;
     const int64_t pb = tprefix[b];
     if (pb + (int64_t)nt * nt <= ds_cap) {
       ds_qt_stride = (int64_t)nt * DS_TILE_BYTES;
-      dsw = dS + (pb * H + (int64_t)h * nt * nt) * (int64_t)DS_TILE_BYTES +
-            (int64_t)((k0 - lo) >> 7) * DS_TILE_BYTES + (grp >> 1) * 16384 + (grp & 1) * 4096 + lane * 16;
+      dsb = dS + (pb * H + (int64_t)h * nt * nt) * (int64_t)DS_TILE_BYTES +
+            (int64_t)((k0 - lo) >> 7) * DS_TILE_BYTES + (grp >> 1) * 16384 + (grp & 1) * 4096;
+      ds_on = true;
     }
   }
 
@@ -907,15 +922,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
 
-  VtLoad<DH> ld;  // producers load Q quads, consumers dO quads
+  // producers load Q rows, consumers dO rows; each wave-wide load covers
+  // whole rows (for DH = 128 four rows of 256 bytes), the fewest cache lines
+  // per instruction
+  constexpr int LCH = DH / 32;
+  uint4 ldx[LCH];
   int64_t rt = 0;
   auto gload = [&](int q0) {
-    if (producer) vt_gload<DH>(ld, Q, ldqkv, q0, qhi, hc, ltid);
-    else vt_gload<DH>(ld, dO, lddo, q0, qhi, hc, ltid);
+    tile_gload_rows<DH, KV_BQ>(ldx, producer ? Q : dO, producer ? ldqkv : lddo, q0, qhi, hc, ltid);
     if (!full && wave == 0) rt = ts_load(ts, q0, qhi, lane);
   };
   auto swrite = [&](int buf) {
-    quad_swrite_swz<DH>(producer ? Qs[buf] : Ds[buf], ld);
+    tile_swrite_swz<DH, KV_BQ>(producer ? Qs[buf] : Ds[buf], ldx, ltid);
     if (!full && wave == 0) Tq[buf][lane] = rt;
   };
   const int nqt = (qhi - qlo + KV_BQ - 1) / KV_BQ;
@@ -930,6 +948,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   for (int it = 0; it < nqt; ++it) {
     const int buf = it & 1, q0 = qlo + it * KV_BQ;
     gload(q0 + KV_BQ);  // past the query range: zeros, never used
+    // A second use of the loaded values here, under a condition that never
+    // holds (q0 is a row index, never negative) but that the compiler cannot
+    // fold, keeps the loads at the top of the stage: their real use follows
+    // the mid-stage barrier, and code sinking would otherwise move them
+    // there, a whole stage of latency hiding lost.
+    if (q0 < 0) {
+      uint32_t any = 0;
+#pragma unroll
+      for (int r = 0; r < LCH; ++r) any |= ldx[r].x | ldx[r].y | ldx[r].z | ldx[r].w;
+      Tq[buf][lane] = any;
+    }
     // phase 1: S (producer) or dA (consumer) for 64 queries x 32 keys
     const uint16_t* A = producer ? Qs[buf] : Ds[buf];
     f32x16_t x[2];
@@ -960,12 +989,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
         }
 #pragma unroll
       for (int u = 0; u < 4; ++u) w[u] = pack_kstep<T>(d, u);
-      if (STORE && dsw) {
-        const int qs = (q0 - lo) >> 6;
-        uint8_t* dp = dsw + (qs >> 1) * ds_qt_stride + (qs & 1) * 8192;
+    }
+    if (STORE) {
+      // Every wave issues the (non-temporal) dS stores, through a resource
+      // of size zero where nothing is kept (the S side, rows beyond the dS
+      // buffer), so that they sit in straight-line code: the wait before the
+      // next stage's LDS writes then covers only that stage's loads.  Under
+      // a branch, the wait counts merged at its join would make it cover
+      // the stores as well, whose completion takes far longer.
+      const int qs = (q0 - lo) >> 6;
+      const __amdgpu_buffer_rsrc_t drs =
+          make_rsrc(ds_on ? dsb + (qs >> 1) * ds_qt_stride + (qs & 1) * 8192 : dS, ds_on ? 4096 : 0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(w[u].v, (u32x4_t*)(dp + u * 1024));
-      }
+      for (int u = 0; u < 4; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, w[u].v), drs, lane * 16 + u * 1024, 0,
+                                               2 /* non-temporal */);
     }
     // phase 2: dV += P^T dO (producer) or dK += dS^T Q (consumer), the B
     // operand read transposed from the other role's row-major tile
