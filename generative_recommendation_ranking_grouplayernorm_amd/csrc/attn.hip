@@ -1056,14 +1056,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
   constexpr int NC = DH / 32;
   struct Smem {
     uint8_t Ss[2][16384];
-    uint16_t Kt[2][DH * VT_PITCH];
+    uint16_t Ks[2][QuadRows<DH>::SIZE];
   };
   __shared__ __attribute__((aligned(16))) union {
     Smem m;
     float ep[4 * EP_FLOATS];
   } sm;
   auto& Ss = sm.m.Ss;
-  auto& Kt = sm.m.Kt;
+  auto& Ks = sm.m.Ks;
   int tile, h;
   xcd_tile_head(blockIdx.x, H, tile, h);
   if (tile >= *ntiles) return;
@@ -1104,27 +1104,39 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
   // lanes 0-1 of every quad still read one full 64-byte global segment.
   const int cidx = (lane & 3) | (((lane >> 4) & 3) << 2) | ((wave & 1) << 4) | (((lane >> 2) & 3) << 5) |
                    ((wave >> 1) << 7);
-  u32x4_t rs[4];
-  VtLoad<DH> rk;
-  auto gload = [&](int it) {
+  // Loads of one 64-key step: the 16 KB dS piece (two 8 KB query stages)
+  // and the 64 K rows.  Both go through range-checked buffer resources, so
+  // that a stage the dK/dV pass never wrote, or a step past the last, reads
+  // nothing and costs no branch: the loads stay straight-line code, and the
+  // wait before a step's LDS writes covers only that step's loads.
+  constexpr int LCH = DH / 32;
+  struct StepRegs {
+    u32x4_t s[4];
+    uint4 k[LCH];
+  };
+  auto gload = [&](StepRegs& R, int it) {
+    const bool live = it < nsteps;
     const int kpos = it < na ? lo + 64 * it : q0 + 64 * (it - na);
     const int kt = (kpos - lo) >> 7, half = ((kpos - lo) >> 6) & 1;
     const int k0 = lo + 128 * kt;
     const uint8_t* src = dsq + (int64_t)kt * DS_TILE_BYTES + half * 16384;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int st = 2 * qt + (i >> 1);
-      const bool avail = lo + 64 * st < hi && (k0 < s_end || k0 >= r_end || st >= rt_stage0);
-      rs[i] = avail ? __builtin_nontemporal_load((const u32x4_t*)(src + 16 * (cidx + 256 * i)))
-                    : u32x4_t{0, 0, 0, 0};
+    for (int p = 0; p < 2; ++p) {
+      const int st = 2 * qt + p;
+      const bool avail = live && lo + 64 * st < hi && (k0 < s_end || k0 >= r_end || st >= rt_stage0);
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(avail ? src + 8192 * p : dS, avail ? 8192 : 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        R.s[2 * p + i] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (cidx + 256 * i), 0, 2 /* non-temporal */));
     }
-    vt_gload<DH>(rk, K, ldqkv, kpos, hi, hc, tid);
+    tile_gload_rows<DH, 64>(R.k, K, ldqkv, live ? kpos : hi, hi, hc, tid);
   };
   const int wsw = ds_lds_pos(16 * cidx);
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, const StepRegs& R) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4_t*)(Ss[buf] + wsw + 4096 * i) = rs[i];
-    vt_swrite<DH>(Kt[buf], rk);
+    for (int i = 0; i < 4; ++i) *(u32x4_t*)(Ss[buf] + wsw + 4096 * i) = R.s[i];
+    tile_swrite_swz<DH, 64>(Ks[buf], R.k, tid);
   };
 
   // transposed dS reads: lane 4r + c of quarter G supplies (key 4g + r of
@@ -1137,17 +1149,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
+  TrAddr<DH> tra;
+  tra.init(lane);
 
-  if (nsteps > 0) {
-    gload(0);
-    swrite(0);
-  }
+  // Two register sets alternate, so that a step's loads are issued two
+  // steps ahead of the step that reads them: step it loads step it + 2 and
+  // writes step it + 1 (loaded during step it - 1) to LDS.
+  StepRegs R0, R1;
+  gload(R0, 0);
+  swrite(0, R0);
+  gload(R1, 1);
   __syncthreads();
-  for (int it = 0; it < nsteps; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < nsteps;
-    if (more) gload(it + 1);
-    const uint8_t* sb = Ss[buf] + rd_base;
+  auto step = [&](int it, StepRegs& Rl, const StepRegs& Rw) {
+    gload(Rl, it + 2);
+    const uint8_t* sb = Ss[it & 1] + rd_base;
+    const uint16_t* kb = Ks[it & 1];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       // key 16 ks + 8 rd + 4 g + r: stored byte bits 12 (ks / 2), 8 (ks % 2)
@@ -1158,10 +1174,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
       op8 a;
       a.v[0] = lo2.x; a.v[1] = lo2.y; a.v[2] = hi2.x; a.v[3] = hi2.y;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(a, vt_operand(Kt[buf], ks, c * 32, lane), acc[c]);
+      for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(a, tra.get(kb, ks, c), acc[c]);
     }
-    if (more) swrite(buf ^ 1);
+    swrite((it + 1) & 1, Rw);
     __syncthreads();
+  };
+  // Steps in pairs, with no branch between them (a branch there would make
+  // the wait counts merged at the loop head wait for loads a step early);
+  // for an odd count the last step of the last pair reads nothing (sizes
+  // zero) and adds zero.
+  for (int it = 0; it < nsteps; it += 2) {
+    step(it, R0, R1);
+    step(it + 1, R1, R0);
   }
   wave_store_rows<T, NC>(sm.ep + wave * EP_FLOATS, acc, 0, lane, q0 + wave * 32, hi, out_scale, dQ, lddq, hc, zq,
                          ldz);
