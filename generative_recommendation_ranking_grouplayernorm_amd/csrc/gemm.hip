@@ -129,16 +129,25 @@ struct GemmCfg {
 using GemmLarge = GemmCfg<256, 256, 2, 4, 1, true>;
 using GemmSmall = GemmCfg<128, 128, 2, 2, 2, false>;
 
-// LDS tile of one operand with ROWS rows (its M or N extent).  K-contiguous:
-// [ROWS][72]; M/N-contiguous: [64][ROWS + 16].  Both layouts get the larger
-// of the two sizes so that A and B sit at fixed offsets.
+// LDS tile of one operand with ROWS rows (its M or N extent), unpadded rows
+// of 16-byte chunks under an XOR swizzle.  K-contiguous: [ROWS][64], chunk c
+// (of 8) of row r at c ^ kc_swz(r), so that the 16 rows of a quarter-wave's
+// operand read (one chunk each) and the 2 rows x 8 chunks of a quarter-wave's
+// write land on distinct bank groups.  M/N-contiguous: [64][ROWS], chunk c of
+// K row r at c ^ mn_swz(r), so that a half-wave's transpose read (4 K rows x
+// 4 chunks, 8 bytes per lane) covers 16 distinct chunk positions and each of
+// its quarter-waves (4 rows x 2 chunks) 8 distinct positions modulo 8.  With
+// padded pitches (72 / ROWS + 16 elements) both kinds of reads collided, the
+// transposed ones on most accesses.  The allocation keeps the padded size,
+// which the epilogue's fp32 staging needs.
 template <int ROWS>
 struct GTile {
   static constexpr int KC_ELEMS = ROWS * G_KC_PITCH;
-  static constexpr int MN_PITCH = ROWS + 16;
-  static constexpr int MN_ELEMS = G_BK * MN_PITCH;
+  static constexpr int MN_ELEMS = G_BK * (ROWS + 16);
   static constexpr int ELEMS = KC_ELEMS > MN_ELEMS ? KC_ELEMS : MN_ELEMS;
 };
+__device__ __forceinline__ int kc_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int mn_swz(int r) { return (4 * (r & 3)) ^ (r & 2); }
 
 // Buffer resource over one operand's K step.  K-contiguous: rows r0.. (the
 // M or N index), columns k0..; M/N-contiguous: rows k0.. (the K index),
@@ -160,9 +169,14 @@ __device__ __forceinline__ int gemm_voff(int64_t ld, int c) {
 
 template <bool KC, int ROWS>
 __device__ __forceinline__ void gemm_swrite(uint16_t* s, int c, uint4 v) {
-  constexpr int CPR = KC ? 8 : ROWS / 8;
-  constexpr int PITCH = KC ? G_KC_PITCH : GTile<ROWS>::MN_PITCH;
-  *(uint4*)(s + (c / CPR) * PITCH + (c % CPR) * 8) = v;
+  if (KC) {
+    const int row = c / 8, ch = c % 8;
+    *(uint4*)(s + row * G_BK + 8 * (ch ^ kc_swz(row))) = v;
+  } else {
+    constexpr int CPR = ROWS / 8;
+    const int row = c / CPR, ch = c % CPR;
+    *(uint4*)(s + row * ROWS + 8 * (ch ^ mn_swz(row))) = v;
+  }
 }
 
 // MFMA operand for 32 rows starting at r0 (within the tile), k-step ks.
@@ -170,15 +184,16 @@ template <bool KC, int ROWS>
 __device__ __forceinline__ op8 gemm_operand(const uint16_t* s, int r0, int ks, int lane) {
   op8 o;
   if (KC) {
-    const int row = r0 + (lane & 31), kk = ks * 16 + 8 * (lane >> 5);
-    o.v = *(const u32x4_t*)(s + row * G_KC_PITCH + kk);
+    const int row = r0 + (lane & 31), ch = 2 * ks + (lane >> 5);
+    o.v = *(const u32x4_t*)(s + row * G_BK + 8 * (ch ^ kc_swz(row)));
   } else {
-    constexpr int PITCH = GTile<ROWS>::MN_PITCH;
     const int G = lane >> 4, i = lane & 15;
     const int kr = ks * 16 + 8 * (G >> 1) + (i >> 2);
     const int col = r0 + 16 * (G & 1) + 4 * (i & 3);
-    uint2 lo = lds_read_tr16(s + kr * PITCH + col);
-    uint2 hi = lds_read_tr16(s + (kr + 4) * PITCH + col);
+    // rows kr and kr + 4 share kr % 4, so both reads use one swizzle
+    const uint16_t* p = s + kr * ROWS + 8 * ((col >> 3) ^ mn_swz(kr)) + (col & 7);
+    uint2 lo = lds_read_tr16(p);
+    uint2 hi = lds_read_tr16(p + 4 * ROWS);
     o.v[0] = lo.x; o.v[1] = lo.y; o.v[2] = hi.x; o.v[3] = hi.y;
   }
   return o;
