@@ -30,7 +30,11 @@ __global__ void seg_kernel(const int32_t* __restrict__ offsets, const uint8_t* _
 // Everything the attention launches need, in one workgroup: segments of
 // every user, the 128-row tile list (longest users first) and the
 // exclusive prefix of n_t^2.  Per-user values are recomputed where needed
-// rather than kept, so any B works with fixed shared memory.
+// rather than kept, so any B works with fixed shared memory.  Group ids of
+// batches up to PREP_G_LDS tokens are first copied to LDS, so that the
+// binary searches for the group starts wait on LDS rather than on a chain
+// of dependent global loads.
+constexpr int PREP_G_LDS = 128 * 1024;
 static_assert(ATTN_QTILE == 128 && ATTN_KTILE == 128, "query and key tile lists are one list");
 
 __global__ __launch_bounds__(1024) void prep_all_kernel(const int32_t* __restrict__ offsets,
@@ -38,36 +42,60 @@ __global__ __launch_bounds__(1024) void prep_all_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ seg,
                                                         int32_t* __restrict__ order_scratch,
                                                         int2* __restrict__ tiles, int32_t* __restrict__ ntiles,
-                                                        int64_t* __restrict__ tprefix) {
+                                                        int64_t* __restrict__ tprefix, int64_t T) {
   __shared__ int hist[1024];
   __shared__ int warp_i[16];
   __shared__ long long warp_l[16];
   __shared__ int carry_i;
   __shared__ long long carry_l;
+  __shared__ __attribute__((aligned(16))) uint8_t gs[PREP_G_LDS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // segments and the histogram of tile counts
-  for (int i = tid; i < 1024; i += 1024) hist[i] = 0;
+  const bool in_lds = T <= PREP_G_LDS;
+  hist[tid] = 0;
+  if (in_lds) {
+    if (((uintptr_t)g & 15) == 0) {
+      for (int i = 16 * tid; i < T; i += 16 * 1024) {
+        if (i + 16 <= T) *(uint4*)(gs + i) = *(const uint4*)(g + i);
+        else for (int j = i; j < T; ++j) gs[j] = g[j];
+      }
+    } else {
+      for (int i = tid; i < T; i += 1024) gs[i] = g[i];
+    }
+  }
   __syncthreads();
+  // segments and the histogram of tile counts
+  const uint8_t* gsrc = in_lds ? (const uint8_t*)gs : g;
   for (int b = tid; b < B; b += 1024) {
     const int lo = offsets[b], hi = offsets[b + 1];
     seg[b * 5 + 0] = lo;
-    seg[b * 5 + 1] = lower_bound_u8(g, lo, hi, 1);
-    seg[b * 5 + 2] = lower_bound_u8(g, lo, hi, 2);
-    seg[b * 5 + 3] = lower_bound_u8(g, lo, hi, 3);
+    seg[b * 5 + 1] = lower_bound_u8(gsrc, lo, hi, 1);
+    seg[b * 5 + 2] = lower_bound_u8(gsrc, lo, hi, 2);
+    seg[b * 5 + 3] = lower_bound_u8(gsrc, lo, hi, 3);
     seg[b * 5 + 4] = hi;
     const int c = (hi - lo + 127) / 128;
     atomicAdd(&hist[min(c, 1023)], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;  // exclusive prefix over buckets from the largest count down
-    for (int c = 1023; c >= 0; --c) {
-      const int h = hist[c];
-      hist[c] = run;
-      run += h;
+  {
+    // exclusive prefix over the buckets from the largest count down: thread
+    // t holds bucket 1023 - t
+    const int c = 1023 - tid;
+    const int h = hist[c];
+    int v = h;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
     }
-    carry_i = 0;
-    carry_l = 0;
+    if (lane == 63) warp_i[w] = v;
+    __syncthreads();
+    int before = 0;
+    for (int k = 0; k < w; ++k) before += warp_i[k];
+    hist[c] = before + v - h;
+    if (tid == 0) {
+      carry_i = 0;
+      carry_l = 0;
+    }
   }
   __syncthreads();
   for (int b = tid; b < B; b += 1024) {
@@ -164,7 +192,7 @@ int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t
   out->k.tiles = out->q.tiles;
   out->k.ntiles = out->q.ntiles;
   hipLaunchKernelGGL(prep_all_kernel, dim3(1), dim3(1024), 0, stream, offsets, group_ids, B, out->seg, order,
-                     out->q.tiles, out->q.ntiles, out->tprefix);
+                     out->q.tiles, out->q.ntiles, out->tprefix, T);
   MTGR_LAUNCH_CHECK();
   return MTGR_OK;
 }
