@@ -45,15 +45,15 @@ __device__ __forceinline__ void store8_t(T* p, const float* v) {
   else *(u32x4_t*)p = r;
 }
 
+// bb: the 8 bias values of columns n..n+7 (zeros without a bias); rr: the
+// raw residual row segment (EPI_BIAS_RESID), both loaded by the caller ahead
+// of the stores.
 template <typename T, int EPI, bool NT>
-__device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, float* v) {
-  if (EPI == EPI_BIAS_SILU || EPI == EPI_BIAS_RESID) {
-    if (ep.bias) {
-      float bb[8];
-      load8_t<T>((const T*)ep.bias + n, bb);
+__device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, float* v, const float* bb,
+                                         const uint4& rr) {
+  if ((EPI == EPI_BIAS_SILU || EPI == EPI_BIAS_RESID) && ep.bias) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += bb[e];
-    }
+    for (int e = 0; e < 8; ++e) v[e] += bb[e];
   }
   if (EPI == EPI_BIAS_SILU) {
     float z[8];
@@ -65,10 +65,12 @@ __device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, fl
     for (int e = 0; e < 8; ++e) z[e] = silu_fast(z[e]);
     store8_t<T, NT>((T*)ep.C + (int64_t)m * ep.ldc + n, z);
   } else if (EPI == EPI_BIAS_RESID) {
-    float r[8];
-    load8_t<T>((const T*)ep.R + (int64_t)m * ep.ldr + n, r);
+    const uint32_t w[4] = {rr.x, rr.y, rr.z, rr.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] += r[e];
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] += from_bits16<T>((uint16_t)(w[e] & 0xffff));
+      v[2 * e + 1] += from_bits16<T>((uint16_t)(w[e] >> 16));
+    }
     store8_t<T, NT>((T*)ep.C + (int64_t)m * ep.ldc + n, v);
   } else {
     store8_t<T, NT>((T*)ep.C + (int64_t)m * ep.ldc + n, v);
@@ -323,11 +325,29 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
         }
   } else {
     // 16-bit outputs: stage each wave's tile through its own LDS region (64
-    // rows at a time, fp32) and write whole 128-byte row segments.
+    // rows at a time, fp32) and write whole 128-byte row segments.  The bias
+    // and residual values a lane needs are loaded before any store: the
+    // compiler cannot move a load past a store that may alias it, so loads
+    // inside the store loop would each wait a full memory round trip.
     float* st = (float*)&smem[0][0] + wave * (64 * G_EPI_PITCH);
     const int wr0 = m0 + wm * (TM * 32), wc0 = n0 + wn * (TN * 32);
+    const int cc = (lane & 7) * 8;
+    const int n = wc0 + cc;
+    float bb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bb[e] = 0.f;
+    if ((EPI == EPI_BIAS_SILU || EPI == EPI_BIAS_RESID) && ep.bias && n < N) load8_t<T>((const T*)ep.bias + n, bb);
 #pragma unroll
     for (int half = 0; half < TM / 2; ++half) {
+      uint4 rr[8];
+#pragma unroll
+      for (int pass = 0; pass < 8; ++pass) {
+        rr[pass] = make_uint4(0, 0, 0, 0);
+        if (EPI == EPI_BIAS_RESID) {
+          const int m = wr0 + half * 64 + pass * 8 + (lane >> 3);
+          if (m < M && n < N) rr[pass] = *(const uint4*)((const T*)ep.R + (int64_t)m * ep.ldr + n);
+        }
+      }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -338,8 +358,6 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
             st[r * G_EPI_PITCH + u * 32 + (lane & 31)] = acc[2 * half + tt][u][j];
           }
       // lane -> 8 consecutive columns of one row; 8 rows per pass
-      const int cc = (lane & 7) * 8;
-      const int n = wc0 + cc;
 #pragma unroll
       for (int pass = 0; pass < 8; ++pass) {
         const int r = pass * 8 + (lane >> 3);
@@ -349,7 +367,7 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
           const float4 a = *(const float4*)&st[r * G_EPI_PITCH + cc];
           const float4 b = *(const float4*)&st[r * G_EPI_PITCH + cc + 4];
           v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-          epi_row8<T, EPI, C::STREAM_OUT>(ep, m, n, v);
+          epi_row8<T, EPI, C::STREAM_OUT>(ep, m, n, v, bb, rr[pass]);
         }
       }
     }
