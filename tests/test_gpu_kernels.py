@@ -145,6 +145,51 @@ def test_attention_parity(mb, dtype, d, H, which, ds):
         assert err <= TOL[dtype], (name, err)
 
 
+@pytest.mark.parametrize("case", ["beyond_lds", "unaligned_ids"])
+def test_prep_group_id_paths(mb, case):
+    """The attention prep copies group ids to LDS for batches of up to 128K
+    tokens, 16 bytes at a time when the pointer allows: a longer batch (the
+    binary searches then read global memory) and a group-id pointer one byte
+    past an aligned address (byte-wise copy), bf16 forward and backward
+    against the oracle."""
+    rng = np.random.default_rng(31)
+    if case == "beyond_lds":
+        lengths = [[2, 60, 10, 8]] * 1700 + [[8, 300, 30, 20]] * 10   # 139,580 tokens
+    else:
+        lengths = EDGE_LENGTHS
+    batch = make_batch_from_lengths(lengths, rng, ts_max=50)
+    assert (batch.T > 128 * 1024) == (case == "beyond_lds")
+    d, H, dtype = 64, 1, torch.bfloat16
+    say("prep paths", case, batch.B, batch.T)
+    uqkv, d_o = _attn_case(batch, d, H, dtype, seed=7)
+    scale = 1.0 / batch.max_len
+    off, g, ts = meta(batch, DEV)
+    if case == "unaligned_ids":
+        buf = torch.zeros(batch.T + 16, dtype=torch.uint8, device=DEV)
+        buf[1:1 + batch.T] = g
+        g = buf[1:1 + batch.T]
+        assert g.data_ptr() % 16 == 1
+    U = uqkv.to(DEV)
+    q, k, v = U[:, d:2 * d], U[:, 2 * d:3 * d], U[:, 3 * d:]
+    o = torch.full((batch.T, d), float("nan"), dtype=dtype, device=DEV)
+    ws_f = mb.workspace(mb.OP_ATTN_FWD, batch.B, batch.T, d, H, dtype, DEV)
+    mb.mtgr_hstu_attn_fwd(q, k, v, o, off, g, ts, H, d // H, 1.0, scale, ws_f)
+    dqkv = torch.full((batch.T, 3 * d), float("nan"), dtype=dtype, device=DEV)
+    dq, dk, dv = dqkv[:, :d], dqkv[:, d:2 * d], dqkv[:, 2 * d:]
+    ws = mb.workspace(mb.OP_ATTN_BWD, batch.B, batch.T, d, H, dtype, DEV, max_len=int(batch.max_len))
+    mb.mtgr_hstu_attn_bwd(q, k, v, d_o.to(DEV), dq, dk, dv, off, g, ts, H, d // H, 1.0, scale, ws,
+                          max_len=int(batch.max_len))
+    torch.cuda.synchronize()
+    qn, kn, vn = (f64(t) for t in (uqkv[:, d:2 * d], uqkv[:, 2 * d:3 * d], uqkv[:, 3 * d:]))
+    ro = orc.hstu_attention(qn, kn, vn, batch.offsets, batch.group_ids, batch.timestamps, H, 1.0, scale)
+    rq, rk, rv = orc.hstu_attention_bwd(qn, kn, vn, f64(d_o), batch.offsets, batch.group_ids, batch.timestamps,
+                                        H, 1.0, scale)
+    for name, got, ref in (("o", o, ro), ("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        err = rel_l2(f64(got), ref)
+        say(f"  {name}: rel-L2 {err:.3e}")
+        assert err <= TOL[dtype], (name, err)
+
+
 @pytest.mark.parametrize("ds", ["stored", "recomputed"])
 def test_attention_bf16_long_users(mb, ds):
     """Several 128-row tiles per user, mixed tails, alpha != 1."""
