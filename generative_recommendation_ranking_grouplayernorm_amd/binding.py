@@ -29,6 +29,7 @@ EXPORTED = (
     "mtgr_hstu_layer_fwd", "mtgr_hstu_layer_bwd", "mtgr_hstu_stack_fwd", "mtgr_stack_graph_create",
     "mtgr_stack_graph_launch", "mtgr_stack_graph_destroy", "mtgr_stochastic_length",
     "mtgr_head_workspace_size", "mtgr_candidate_head_fwd", "mtgr_candidate_head_loss", "mtgr_serving_graph_create",
+    "mtgr_set_validate",
 )
 
 
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "mtgr_version": ([], ctypes.c_char_p),
         "mtgr_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "mtgr_set_validate": ([ctypes.c_int], ctypes.c_int),
         "mtgr_workspace_size": ([ctypes.c_int, I32, I64, I32, I32, I32, ctypes.c_int], SZ),
         "mtgr_jagged_prep": ([P, P, I32, I64, P, P, SZ, P], ctypes.c_int),
         "mtgr_group_layernorm": ([P, P, P, P, P, I64, I32, I32, F, ctypes.c_int, P, P, P], ctypes.c_int),
@@ -167,6 +169,11 @@ def mtgr_version() -> str:
 
 def mtgr_status_string(status: int) -> str:
     return load_library().mtgr_status_string(status).decode()
+
+
+def mtgr_set_validate(on: int) -> int:
+    """Validation mode on (1) / off (0), or query (-1); returns the previous state."""
+    return int(load_library().mtgr_set_validate(on))
 
 
 def mtgr_workspace_size(op: int, B: int, T: int, max_len: int, d: int, H: int, dtype: torch.dtype) -> int:

@@ -10,6 +10,12 @@ using namespace mtgr;
 namespace {
 
 constexpr int kMaxG = 8;
+// Largest row stride (elements) of any row-major operand: tile offsets
+// inside a kernel are 32-bit byte offsets over at most 256 rows.
+constexpr int64_t kMaxLd = (int64_t)1 << 22;
+// The layer's token groups U, S, R, C: its group norms need G >= 4 rows of
+// gamma / beta.
+constexpr int kLayerGroups = 4;
 
 inline hipStream_t S(mtgr_stream_t s) { return (hipStream_t)s; }
 
@@ -22,7 +28,7 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // Row strides and base pointers must allow 16-byte vector access.
 inline bool vec_ok(const void* p, int64_t ld, int dt) {
   if (!p) return true;
-  return aligned16(p) && (ld * (int64_t)elt(dt)) % 16 == 0;
+  return aligned16(p) && ld <= kMaxLd && (ld * (int64_t)elt(dt)) % 16 == 0;
 }
 
 bool attn_shape_ok(int dt, int dh) {
@@ -142,7 +148,13 @@ int splits_for(int M, int N, int K) {
 
 extern "C" {
 
-const char* mtgr_version(void) { return "mtgr-hstu 0.1.0 gfx950"; }
+const char* mtgr_version(void) { return "mtgr-hstu 0.2.0 gfx950"; }
+
+int mtgr_set_validate(int on) {
+  const int prev = validation_enabled() ? 1 : 0;
+  if (on >= 0) set_validation(on);
+  return prev;
+}
 
 const char* mtgr_status_string(int status) {
   switch (status) {
@@ -179,7 +191,9 @@ int mtgr_jagged_prep(const int32_t* offsets, const uint8_t* group_ids, int32_t B
   if (B < 0 || T < 0) return MTGR_ERR_INVALID_ARG;
   if (B == 0) return MTGR_OK;
   if (!offsets || !seg || (T > 0 && !group_ids)) return MTGR_ERR_INVALID_ARG;
-  return launch_seg_only(offsets, group_ids, B, seg, S(stream));
+  const int vr = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, 0, S(stream));
+  if (vr) return vr;
+  return launch_seg_only(offsets, group_ids, B, T, seg, S(stream));
 }
 
 int mtgr_stochastic_length(const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,
@@ -197,6 +211,8 @@ int mtgr_stochastic_length(const int32_t* offsets, const uint8_t* group_ids, con
   if (ld_x < d || ld_out < d || row_bytes % 16) return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(x, ld_x, dt) || !vec_ok(x_out, ld_out, dt)) return MTGR_ERR_INVALID_ARG;
   if (ws_bytes < sl_workspace_bytes(B, T) || !workspace) return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  const int vr = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, 0, S(stream));
+  if (vr) return vr;
   // an empty batch still gets its offsets and budget cut written
   return launch_stochastic_length(offsets, group_ids, timestamps, x, ld_x * (int64_t)elt(dt), (int)row_bytes, B, T, u,
                                   s_keep, token_budget, offsets_out, group_ids_out, timestamps_out, x_out,
@@ -231,19 +247,34 @@ size_t mtgr_head_workspace_size(int32_t B, int64_t n_cand, int32_t d, int32_t h,
 int mtgr_candidate_head_fwd(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
                             const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, float* logits, int dt,
                             void* workspace, size_t ws_bytes, mtgr_stream_t stream) {
+  return head_fwd_run(p, x, ld_x, offsets, group_ids, B, T, n_cand, logits, dt, workspace, ws_bytes,
+                      S(stream), true);
+}
+
+}  // extern "C"
+
+int mtgr::head_fwd_run(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                       const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, float* logits, int dt,
+                       void* workspace, size_t ws_bytes, hipStream_t stream, bool check_meta) {
   int r = head_validate(p, x, ld_x, offsets, group_ids, B, T, n_cand, dt);
   if (r) return r;
   if (n_cand > 0 && !logits) return MTGR_ERR_INVALID_ARG;
   if (ws_bytes < head_workspace_bytes(B, n_cand, p->d, p->h, p->n_tasks, dt) || !workspace)
     return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  if (check_meta) {
+    r = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, 0, stream);
+    if (r) return r;
+  }
   if (n_cand == 0 || B == 0) return MTGR_OK;
   HeadArgs a = {};
   a.offsets = offsets; a.group_ids = group_ids; a.B = B; a.T = T; a.n_cand = n_cand;
   a.x = x; a.ldx = ld_x; a.d = p->d; a.h = p->h; a.nt = p->n_tasks;
   a.W1 = p->W1; a.b1 = p->b1; a.W2 = p->W2; a.b2 = p->b2;
   a.logits = logits;
-  return launch_head(dt, a, workspace, S(stream));
+  return launch_head(dt, a, workspace, stream);
 }
+
+extern "C" {
 
 int mtgr_candidate_head_loss(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
                              const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, const float* labels,
@@ -259,6 +290,8 @@ int mtgr_candidate_head_loss(const mtgr_head_params* p, const void* x, int64_t l
   if (dx && dx == x) return MTGR_ERR_INVALID_ARG;
   if (ws_bytes < head_workspace_bytes(B, n_cand, p->d, p->h, p->n_tasks, dt) || !workspace)
     return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  r = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, 0, S(stream));
+  if (r) return r;
   HeadArgs a = {};
   a.offsets = offsets; a.group_ids = group_ids; a.B = B; a.T = T; a.n_cand = B > 0 ? n_cand : 0;
   a.x = x; a.ldx = ld_x; a.d = p->d; a.h = p->h; a.nt = p->n_tasks;
@@ -279,7 +312,9 @@ int mtgr_group_layernorm(const void* x, void* y, const void* gamma, const void* 
   if ((mean_out == nullptr) != (rstd_out == nullptr)) return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(x, d, dt) || !vec_ok(y, d, dt) || !vec_ok(gamma, d, dt) || !vec_ok(beta, d, dt))
     return MTGR_ERR_INVALID_ARG;
-  return launch_gln_fwd(dt, x, d, y, d, gamma, beta, group_ids, T, d, eps, mean_out, rstd_out, nullptr, 0,
+  const int vr = validate_jagged(nullptr, group_ids, 0, T, G, false, 0, S(stream));
+  if (vr) return vr;
+  return launch_gln_fwd(dt, x, d, y, d, gamma, beta, group_ids, T, d, G, eps, mean_out, rstd_out, nullptr, 0,
                         S(stream));
 }
 
@@ -296,6 +331,8 @@ int mtgr_group_layernorm_bwd(const void* dy, const void* x, const float* mean, c
     return MTGR_ERR_INVALID_ARG;
   if (ws_bytes < gln_bwd_workspace_bytes(T, d, G) || (T > 0 && !workspace))
     return MTGR_ERR_WORKSPACE_TOO_SMALL;
+  const int vr = validate_jagged(nullptr, group_ids, 0, T, G, false, 0, S(stream));
+  if (vr) return vr;
   return launch_gln_bwd(dt, dy, d, x, d, mean, rstd, gamma, nullptr, group_ids, T, d, G, dx, d, nullptr, 0,
                         nullptr, 0, nullptr, 0, nullptr, 0, dgamma, dbeta, workspace, S(stream));
 }
@@ -323,6 +360,8 @@ int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_q
   if (ld_o < (int64_t)H * dh || (T > 0 && !o) || !vec_ok(o, ld_o, dt)) return MTGR_ERR_INVALID_ARG;
   if (ws_bytes < attn_fwd_ws(B, T, H, dh, dt)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   if (B == 0 || T == 0) return MTGR_OK;
+  r = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, 0, S(stream));
+  if (r) return r;
   Carver cv{(char*)workspace, ws_bytes};
   void* ws_prep = cv.take(attn_ws(B, T));
   const size_t pb = attn_fwd_part_bytes(dt, B, T, H, dh);
@@ -361,6 +400,8 @@ int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_q
       !vec_ok(dv, ld_dqkv, dt))
     return MTGR_ERR_INVALID_ARG;
   if (B == 0 || T == 0) return MTGR_OK;
+  r = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, max_len, S(stream));
+  if (r) return r;
   PrepView pv;
   r = launch_prep(offsets, group_ids, B, T, workspace, S(stream), &pv);
   if (r) return r;
@@ -377,6 +418,9 @@ static int layer_param_checks(const mtgr_layer_params* p, int dt) {
   if (!p) return MTGR_ERR_INVALID_ARG;
   if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
   if (p->H < 1 || p->dh < 1 || p->d != p->H * p->dh || p->G < 1 || p->G > kMaxG) return MTGR_ERR_INVALID_ARG;
+  // group ids of a layer run over U, S, R, C: fewer parameter rows cannot
+  // serve them
+  if (p->G < kLayerGroups) return MTGR_ERR_UNSUPPORTED;
   if (!attn_shape_ok(dt, p->dh)) return MTGR_ERR_UNSUPPORTED;
   if (p->d % 8 != 0 || p->d > 8192 || p->G * p->d > 8192) return MTGR_ERR_UNSUPPORTED;
   if (dt != MTGR_F32 && p->d % 64 != 0) return MTGR_ERR_UNSUPPORTED;
@@ -408,10 +452,10 @@ static int layer_fwd_body(const mtgr_layer_params* p, const void* x_in, void* x_
   {
     ProfScope ps("gln1_fwd", st);
     if (in_planes)
-      r = launch_gln_fwd_part(dt, *in_planes, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->eps,
+      r = launch_gln_fwd_part(dt, *in_planes, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->G, p->eps,
                               saved ? saved->mean1 : nullptr, saved ? saved->rstd1 : nullptr, nullptr, 0, st);
     else
-      r = launch_gln_fwd(dt, x_in, d, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->eps,
+      r = launch_gln_fwd(dt, x_in, d, xhat, d, p->gamma1, p->beta1, group_ids, T, d, p->G, p->eps,
                          saved ? saved->mean1 : nullptr, saved ? saved->rstd1 : nullptr, nullptr, 0, st);
   }
   if (r) return r;
@@ -443,10 +487,10 @@ static int layer_fwd_body(const mtgr_layer_params* p, const void* x_in, void* x_
       PartialRows pr = {};
       pr.part = (const float*)part; pr.n = a.nsplit; pr.plane = T * d; pr.ldp = d;
       pr.xs = saved ? saved->o : nullptr; pr.ldxs = d;
-      r = launch_gln_fwd_part(dt, pr, y, d, p->gamma2, p->beta2, group_ids, T, d, p->eps,
+      r = launch_gln_fwd_part(dt, pr, y, d, p->gamma2, p->beta2, group_ids, T, d, p->G, p->eps,
                               saved ? saved->mean2 : nullptr, saved ? saved->rstd2 : nullptr, uqkv, 4 * d, st);
     } else {
-      r = launch_gln_fwd(dt, o, d, y, d, p->gamma2, p->beta2, group_ids, T, d, p->eps,
+      r = launch_gln_fwd(dt, o, d, y, d, p->gamma2, p->beta2, group_ids, T, d, p->G, p->eps,
                          saved ? saved->mean2 : nullptr, saved ? saved->rstd2 : nullptr, uqkv, 4 * d, st);
     }
   }
@@ -480,6 +524,8 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
     return MTGR_ERR_INVALID_ARG;
   if (ws_bytes < layer_fwd_ws(B, T, d, p->H, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   if (T == 0 || B == 0) return MTGR_OK;
+  r = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, 0, S(stream));
+  if (r) return r;
   hipStream_t st = S(stream);
   const size_t e = elt(dt);
   Carver cv{(char*)workspace, ws_bytes};
@@ -536,11 +582,24 @@ int mtgr_hstu_stack_fwd(const mtgr_layer_params* layers, int32_t L, const void* 
                         const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
                         int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes,
                         mtgr_stream_t stream) {
+  return stack_fwd_run(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt, workspace,
+                       ws_bytes, S(stream), true);
+}
+
+}  // extern "C"
+
+int mtgr::stack_fwd_run(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                        int64_t T, float attn_scale, int dt, void* workspace, size_t ws_bytes, hipStream_t st,
+                        bool check_meta) {
   int r = stack_fwd_validate(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, dt, workspace, ws_bytes);
   if (r) return r;
   if (T == 0 || B == 0) return MTGR_OK;
+  if (check_meta) {
+    r = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, 0, st);
+    if (r) return r;
+  }
   const int d = layers[0].d;
-  hipStream_t st = S(stream);
   const size_t e = elt(dt);
   const int H = layers[0].H;
   Carver cv{(char*)workspace, ws_bytes};
@@ -594,6 +653,8 @@ int mtgr_hstu_stack_fwd(const mtgr_layer_params* layers, int32_t L, const void* 
   return MTGR_OK;
 }
 
+extern "C" {
+
 int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr_layer_saved* saved,
                         const void* dx_out, void* dx_in, const mtgr_layer_grads* grads,
                         const mtgr_layer_bwd_extras* extras, const int32_t* offsets, const uint8_t* group_ids,
@@ -614,6 +675,10 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
     return MTGR_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = S(stream);
   const int G = p->G;
+  if (T > 0 && B > 0) {
+    r = validate_jagged(offsets, group_ids, B, T, kLayerGroups, true, max_len, st);
+    if (r) return r;
+  }
   if (T == 0 || B == 0) {
     r = launch_fill_f32(grads->W_uqkv, (int64_t)4 * d * d, 0.f, st);
     if (!r) r = launch_fill_f32(grads->W_o, (int64_t)d * d, 0.f, st);

@@ -55,6 +55,23 @@ __device__ __forceinline__ int key_end_for(int q_last, int s_end, int r_end) {
   return q_last + 1;
 }
 
+// The 64-key tiles (counted from the row start lo) that a query tile
+// [q0, q_last] visits: every tile up to the end of R, then, for a tile of
+// candidates, only the tiles of its own rows: a candidate key is visible
+// only to itself, so candidate x candidate blocks off the diagonal are
+// skipped.  Visit it (0 <= it < n) is tile tile(it).
+struct KeyRuns {
+  int na, b0, n;
+  __device__ __forceinline__ int tile(int it) const { return it < na ? it : b0 + (it - na); }
+};
+__device__ __forceinline__ KeyRuns key_runs(int lo, int q0, int q_last, int s_end, int r_end) {
+  const int kv_end = key_end_for(q_last, s_end, r_end);
+  const int nall = (kv_end - lo + 63) >> 6;
+  const int na = min(nall, (min(r_end, kv_end) - lo + 63) >> 6);
+  const int b0 = max(na, (max(q0, r_end) - lo) >> 6);
+  return {na, b0, na + max(0, nall - b0)};
+}
+
 constexpr int A_BQ = 128;  // queries per forward / dQ workgroup (4 waves x 32)
 constexpr int A_BK = 64;   // keys per LDS tile (forward / dQ)
 constexpr int A_BKW = 128; // keys per dK/dV workgroup (4 waves x 32)
@@ -187,16 +204,18 @@ inline unsigned xcd_grid(int64_t max_tiles, int H) {
 // Buffer resource over rows [r0, rlim) of a row-major [.., ld] 16-bit array,
 // starting at column col0: rows at or beyond rlim read as zero.  The row
 // range is wave-uniform, so advancing a tile changes only scalar registers.
+// No caller reads more than 128 rows from one resource, so the range stops
+// there: its byte size stays a small 32-bit value for any row length.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* P, int64_t ld, int r0, int rlim,
                                                          int col0) {
-  return make_rsrc(P + (int64_t)r0 * ld + col0, (int)((int64_t)max(rlim - r0, 0) * ld * 2));
+  return make_rsrc(P + (int64_t)r0 * ld + col0, (int)((int64_t)min(max(rlim - r0, 0), 128) * ld * 2));
 }
 
 // Timestamp of token r0 + lane, or 0 at or beyond rlim, as a range-checked
 // buffer load: no select on the loaded value, so the load stays in flight
 // until the value is used.
 __device__ __forceinline__ int64_t ts_load(const int64_t* ts, int r0, int rlim, int lane) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(ts + r0, max(rlim - r0, 0) * 8);
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(ts + r0, min(max(rlim - r0, 0), 64) * 8);
   return __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, 0));
 }
 
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), l32 = lane & 31, g = lane >> 5;
   const int q_last = min(q0 + F_BQ, hi) - 1;
-  const int kv_end = key_end_for(q_last, s_end, r_end);
+  const KeyRuns kr = key_runs(lo, q0, q_last, s_end, r_end);
   const int qi = q0 + wave * 32 + l32;
   const bool qv = qi < hi;
   const int qr = qv ? qi : lo;
@@ -458,8 +477,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   uint4 rk[CH];
   VtLoad<DH> rv;
   int64_t rt = 0;
-  const int nkt = (kv_end - lo + F_BK - 1) / F_BK;
-  // this workgroup's run of key tiles [it0, it1)
+  const int nkt = kr.n;
+  // this workgroup's run of key-tile visits [it0, it1)
   int it0 = 0, it1 = nkt;
   if (nsplit > 1) {
     const int per = (nkt + nsplit - 1) / nsplit;
@@ -479,23 +498,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
     if (wave == 0) Tk[buf][lane] = rt;
   };
   if (it0 < it1) {
-    gload(lo + it0 * F_BK);
+    gload(lo + kr.tile(it0) * F_BK);
     swrite(0);
   }
   __syncthreads();
+  // the full tiles come first (tile(it) == it there)
   const int mid = max(it0, min(it1, nfull));
   for (int it = it0; it < mid; ++it) {
     const int buf = (it - it0) & 1, k0 = lo + it * F_BK;
     const bool more = it + 1 < it1;
-    if (more) gload(k0 + F_BK);
+    if (more) gload(lo + kr.tile(it + 1) * F_BK);
     fwd_tile<T, DH, false>(Ks[buf], Vt[buf], Tk[buf], qop, oacc, k0, qi, tq, s_end, r_end, kexp, lane);
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
   for (int it = mid; it < it1; ++it) {
-    const int buf = (it - it0) & 1, k0 = lo + it * F_BK;
+    const int buf = (it - it0) & 1, k0 = lo + kr.tile(it) * F_BK;
     const bool more = it + 1 < it1;
-    if (more) gload(k0 + F_BK);
+    if (more) gload(lo + kr.tile(it + 1) * F_BK);
     fwd_tile<T, DH, true>(Ks[buf], Vt[buf], Tk[buf], qop, oacc, k0, qi, tq, s_end, r_end, kexp, lane);
     if (more) swrite(buf ^ 1);
     __syncthreads();
@@ -725,7 +745,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   const int grp = wave & 3;
   const int ltid = tid & 255;
   const int q_last = min(q0 + A_BQ, hi) - 1;
-  const int kv_end = key_end_for(q_last, s_end, r_end);
+  const KeyRuns kr = key_runs(lo, q0, q_last, s_end, r_end);
   const int qi = q0 + grp * 32 + l32;
   const bool qv = qi < hi;
   const int qr = qv ? qi : lo;
@@ -765,18 +785,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
     }
     if (wave == 0) Tk[buf][lane] = rt;
   };
-  const int nkt = (kv_end - lo + A_BK - 1) / A_BK;
+  static_assert(A_BK == 64, "key runs count 64-key tiles");
+  const int nkt = kr.n;
   const int nfull = min(nkt, max(0, (s_end - lo) / A_BK));
   if (nkt > 0) {
-    gload(lo);
+    gload(lo + kr.tile(0) * A_BK);
     swrite(0);
   }
   __syncthreads();
   uint32_t* fx = Fx[grp];
   for (int it = 0; it < nkt; ++it) {
-    const int buf = it & 1, k0 = lo + it * A_BK;
+    const int buf = it & 1, k0 = lo + kr.tile(it) * A_BK;
     const bool more = it + 1 < nkt;
-    if (more) gload(k0 + A_BK);
+    if (more) gload(lo + kr.tile(it + 1) * A_BK);
     // phase 1: S^T (producer) or dA^T (consumer) for 64 keys x 32 queries
     const uint16_t* A = producer ? Ks[buf] : Vs[buf];
     f32x16_t x[2];

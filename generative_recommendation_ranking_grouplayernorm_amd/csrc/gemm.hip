@@ -153,12 +153,15 @@ __device__ __forceinline__ int mn_swz(int r) { return (4 * (r & 3)) ^ (r & 2); }
 
 // Buffer resource over one operand's K step.  K-contiguous: rows r0.. (the
 // M or N index), columns k0..; M/N-contiguous: rows k0.. (the K index),
-// columns r0...  Reads beyond the valid rows return zeros.
-template <bool KC>
+// columns r0...  Reads beyond the valid rows return zeros.  A step reads at
+// most ROWS (K-contiguous) or G_BK (M/N-contiguous) rows, so the range ends
+// there: its byte size fits 32 bits for any number of tokens.
+template <bool KC, int ROWS>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const uint16_t* P, int64_t ld, int r0, int R, int k0,
                                                          int kend) {
-  if (KC) return make_rsrc(P + (int64_t)r0 * ld + k0, (int)((int64_t)(R - r0) * ld * 2 - (int64_t)k0 * 2));
-  return make_rsrc(P + (int64_t)k0 * ld + r0, (int)((int64_t)(kend - k0) * ld * 2 - (int64_t)r0 * 2));
+  if (KC)
+    return make_rsrc(P + (int64_t)r0 * ld + k0, (int)((int64_t)min(R - r0, ROWS) * ld * 2 - (int64_t)k0 * 2));
+  return make_rsrc(P + (int64_t)k0 * ld + r0, (int)((int64_t)min(kend - k0, G_BK) * ld * 2 - (int64_t)r0 * 2));
 }
 
 // 16-byte chunk c of a K step: K-contiguous, 8 chunks per row of 64;
@@ -281,8 +284,8 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
     gemm_pipeline<TM * (AK ? 1 : 2) + TN * (BKC ? 1 : 2), TM * TN>();
   };
   auto gload_to = [&](uint4 (&ra)[A_LOADS], uint4 (&rb)[B_LOADS], int k0) {
-    const __amdgpu_buffer_rsrc_t sa = gemm_rsrc<AK>(A, lda, m0, M, k0, kend);
-    const __amdgpu_buffer_rsrc_t sb = gemm_rsrc<BKC>(B, ldb, n0, N, k0, kend);
+    const __amdgpu_buffer_rsrc_t sa = gemm_rsrc<AK, BM>(A, lda, m0, M, k0, kend);
+    const __amdgpu_buffer_rsrc_t sb = gemm_rsrc<BKC, BN>(B, ldb, n0, N, k0, kend);
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) ra[i] = buf_load16(sa, va[i]);
 #pragma unroll

@@ -10,6 +10,12 @@ using namespace mtgr;
 struct mtgr_graph_s {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  // the captured batch's metadata, checked before each replay in validation
+  // mode
+  const int32_t* offsets = nullptr;
+  const uint8_t* group_ids = nullptr;
+  int32_t B = 0;
+  int64_t T = 0;
 };
 
 namespace {
@@ -21,9 +27,15 @@ void release(mtgr_graph_s* g) {
   delete g;
 }
 
-// Records fn(stream) on a private stream and instantiates the graph.
+// Records fn(stream) on a private stream and instantiates the graph.  In
+// validation mode the metadata is checked first (on the null stream: no
+// kernel can be recorded while it runs).
 template <typename F>
-int capture(F fn, mtgr_graph* out) {
+int capture(F fn, const int32_t* offsets, const uint8_t* group_ids, int32_t B, int64_t T, mtgr_graph* out) {
+  if (validation_enabled()) {
+    const int vr = validate_jagged(offsets, group_ids, B, T, 4, true, 0, nullptr);
+    if (vr) return vr;
+  }
   hipStream_t cs = nullptr;
   if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MTGR_ERR_HIP;
   mtgr_graph_s* g = new (std::nothrow) mtgr_graph_s;
@@ -53,6 +65,10 @@ int capture(F fn, mtgr_graph* out) {
     (void)hipGetLastError();
     return r;
   }
+  g->offsets = offsets;
+  g->group_ids = group_ids;
+  g->B = B;
+  g->T = T;
   *out = g;
   return MTGR_OK;
 }
@@ -76,10 +92,10 @@ int mtgr_stack_graph_create(const mtgr_layer_params* layers, int32_t L, const vo
   if (r) return r;
   return capture(
       [&](mtgr_stream_t s) {
-        return mtgr_hstu_stack_fwd(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt,
-                                   workspace, ws_bytes, s);
+        return stack_fwd_run(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt,
+                             workspace, ws_bytes, (hipStream_t)s, false);
       },
-      out);
+      offsets, group_ids, B, T, out);
 }
 
 int mtgr_serving_graph_create(const mtgr_layer_params* layers, int32_t L, const mtgr_head_params* head,
@@ -100,17 +116,21 @@ int mtgr_serving_graph_create(const mtgr_layer_params* layers, int32_t L, const 
     return MTGR_ERR_WORKSPACE_TOO_SMALL;
   return capture(
       [&](mtgr_stream_t s) {
-        int rr = mtgr_hstu_stack_fwd(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt,
-                                     workspace, ws_bytes, s);
+        int rr = stack_fwd_run(layers, L, x_in, x_out, offsets, group_ids, timestamps, B, T, attn_scale, dt,
+                               workspace, ws_bytes, (hipStream_t)s, false);
         if (rr) return rr;
-        return mtgr_candidate_head_fwd(head, x_out, layers[0].d, offsets, group_ids, B, T, n_cand, logits, dt,
-                                       head_ws, head_ws_bytes, s);
+        return head_fwd_run(head, x_out, layers[0].d, offsets, group_ids, B, T, n_cand, logits, dt, head_ws,
+                            head_ws_bytes, (hipStream_t)s, false);
       },
-      out);
+      offsets, group_ids, B, T, out);
 }
 
 int mtgr_stack_graph_launch(mtgr_graph g, mtgr_stream_t stream) {
   if (!g || !g->exec) return MTGR_ERR_INVALID_ARG;
+  if (validation_enabled()) {
+    const int vr = validate_jagged(g->offsets, g->group_ids, g->B, g->T, 4, true, 0, (hipStream_t)stream);
+    if (vr) return vr;
+  }
   return hipGraphLaunch(g->exec, (hipStream_t)stream) == hipSuccess ? MTGR_OK : MTGR_ERR_HIP;
 }
 

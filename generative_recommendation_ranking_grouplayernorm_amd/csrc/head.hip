@@ -299,7 +299,7 @@ static int head_sums(int nt, const HeadWs& w, int h, int64_t n_cand, float* dW2,
 int launch_head(int dt, const HeadArgs& a, void* ws, hipStream_t st) {
   const size_t e = dt == MTGR_F32 ? 4 : 2;
   const HeadWs w = head_carve(ws, a.B, a.n_cand, a.d, a.h, a.nt, dt);
-  int r = launch_seg_only(a.offsets, a.group_ids, a.B, w.seg, st);
+  int r = launch_seg_only(a.offsets, a.group_ids, a.B, a.T, w.seg, st);
   if (r) return r;
   {
     ProfScope ps("head_gather", st);

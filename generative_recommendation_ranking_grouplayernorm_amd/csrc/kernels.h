@@ -24,6 +24,16 @@ class ProfScope {
 // True while mtgr_profile_enable(1) is in effect.
 bool profiling_enabled();
 
+// mtgr_hstu_stack_fwd / mtgr_candidate_head_fwd on a HIP stream; with
+// check_meta false the validation-mode device check is skipped (the graph
+// entry points run it before capture and before every replay instead).
+int stack_fwd_run(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
+                  const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B, int64_t T,
+                  float attn_scale, int dt, void* workspace, size_t ws_bytes, hipStream_t st, bool check_meta);
+int head_fwd_run(const mtgr_head_params* p, const void* x, int64_t ld_x, const int32_t* offsets,
+                 const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, float* logits, int dt,
+                 void* workspace, size_t ws_bytes, hipStream_t stream, bool check_meta);
+
 // Host-side argument checks of mtgr_hstu_stack_fwd (MTGR_OK or a status).
 int stack_fwd_validate(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
@@ -50,8 +60,18 @@ int64_t max_tiles(int B, int64_t T, int rows_per_tile);
 size_t prep_workspace_bytes(int B, int64_t T);
 int launch_prep(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t T, void* ws,
                 hipStream_t stream, PrepView* out);
-int launch_seg_only(const int32_t* offsets, const uint8_t* group_ids, int B, int32_t* seg,
+int launch_seg_only(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t T, int32_t* seg,
                     hipStream_t stream);
+// Device check of jagged metadata (validation mode): offsets[0] = 0,
+// non-decreasing, offsets[B] = T; every group id < G; with `ordered`, group
+// ids non-decreasing inside each user; with max_len > 0, no row longer than
+// max_len.  Reads offsets[0..B] (when B > 0) and group_ids[0..T) only.
+// MTGR_OK when validation is off or the metadata passes, MTGR_ERR_VALIDATION
+// when it fails; synchronises `stream` when on.
+int validate_jagged(const int32_t* offsets, const uint8_t* group_ids, int B, int64_t T, int G, bool ordered,
+                    int max_len, hipStream_t stream);
+bool validation_enabled();
+void set_validation(int on);
 
 // ---- Stochastic Length sampling and the token-budget cut -----------------
 int64_t sl_max_blocks(int B, int64_t T);
@@ -91,8 +111,9 @@ int head_validate(const mtgr_head_params* p, const void* x, int64_t ld_x, const 
 
 // ---- a2/a5: group norm rows ---------------------------------------------
 // y = GLN(x) (mode plain) or y = GLN(x) * u (mode gate).
+// Group ids at or above G read the last parameter row (G - 1).
 int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,
-                   const void* beta, const uint8_t* g, int64_t T, int d, float eps, float* mean,
+                   const void* beta, const uint8_t* g, int64_t T, int d, int G, float eps, float* mean,
                    float* rstd, const void* u, int64_t ldu, hipStream_t stream);
 // Row inputs given as fp32 partial sums (split-K products, split-key
 // attention): x[row, col] = round_T(sum_{s < n} part[s * plane + row * ldp +
@@ -107,8 +128,8 @@ struct PartialRows {
 };
 // launch_gln_fwd with x taken from partial sums.
 int launch_gln_fwd_part(int dt, const PartialRows& in, void* y, int64_t ldy, const void* gamma, const void* beta,
-                        const uint8_t* g, int64_t T, int d, float eps, float* mean, float* rstd, const void* u,
-                        int64_t ldu, hipStream_t stream);
+                        const uint8_t* g, int64_t T, int d, int G, float eps, float* mean, float* rstd,
+                        const void* u, int64_t ldu, hipStream_t stream);
 // Only the sum: xs = x (in.xs must be set).
 int launch_partial_reduce(int dt, const PartialRows& in, int64_t T, int d, hipStream_t stream);
 // Backward.  Plain: dx = GLN'(dy) [+ resid].  Gate (u != NULL): the forward

@@ -108,7 +108,7 @@ __device__ __forceinline__ void partial_row8(const PartialRows& pr, int64_t row,
 template <typename T, int NCH, bool GATE, bool PART>
 __global__ __launch_bounds__(256) void gln_fwd_kernel(
     const T* x, int64_t ldx, T* y, int64_t ldy, const T* __restrict__ gamma,
-    const T* __restrict__ beta, const uint8_t* __restrict__ g, int64_t nrows, int d, float eps,
+    const T* __restrict__ beta, const uint8_t* __restrict__ g, int64_t nrows, int d, int G, float eps,
     float* __restrict__ mean_out, float* __restrict__ rstd_out, const T* __restrict__ u, int64_t ldu,
     PartialRows pr) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -145,7 +145,9 @@ __global__ __launch_bounds__(256) void gln_fwd_kernel(
   }
   const float var = warp_sum(q) * inv_d;
   const float rstd = 1.0f / sqrtf(var + eps);
-  const int grp = g[row];
+  // a group id beyond the parameter rows (metadata outside the contract)
+  // takes the last row: never a read past gamma / beta
+  const int grp = min((int)g[row], G - 1);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int c = lane * 8 + i * 512;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) void gln_fwd_kernel(
 
 template <typename T, bool GATE, bool PART>
 static int gln_fwd_dispatch(const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,
-                            const void* beta, const uint8_t* g, int64_t T_, int d, float eps,
+                            const void* beta, const uint8_t* g, int64_t T_, int d, int G, float eps,
                             float* mean, float* rstd, const void* u, int64_t ldu, const PartialRows& pr,
                             hipStream_t st) {
   dim3 grid((unsigned)((T_ + 3) / 4)), block(256);
@@ -181,7 +183,7 @@ static int gln_fwd_dispatch(const void* x, int64_t ldx, void* y, int64_t ldy, co
 #define GLN_FWD_CASE(N)                                                                                 \
   case N:                                                                                               \
     hipLaunchKernelGGL((gln_fwd_kernel<T, N, GATE, PART>), grid, block, 0, st, (const T*)x, ldx, (T*)y, \
-                       ldy, (const T*)gamma, (const T*)beta, g, T_, d, eps, mean, rstd, (const T*)u, ldu, \
+                       ldy, (const T*)gamma, (const T*)beta, g, T_, d, G, eps, mean, rstd, (const T*)u, ldu, \
                        pr);                                                                             \
     break;
   switch (n) {
@@ -221,16 +223,16 @@ int launch_partial_reduce(int dt, const PartialRows& in, int64_t T_, int d, hipS
 }
 
 int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, const void* gamma,
-                   const void* beta, const uint8_t* g, int64_t T_, int d, float eps, float* mean,
+                   const void* beta, const uint8_t* g, int64_t T_, int d, int G, float eps, float* mean,
                    float* rstd, const void* u, int64_t ldu, hipStream_t stream) {
   if (T_ <= 0) return MTGR_OK;
   const bool gate = u != nullptr;
   const PartialRows none = {};
 #define GLN_FWD_DT(TY)                                                                                        \
-  return gate ? gln_fwd_dispatch<TY, true, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, \
-                                                  ldu, none, stream)                                         \
-              : gln_fwd_dispatch<TY, false, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, \
-                                                   ldu, none, stream);
+  return gate ? gln_fwd_dispatch<TY, true, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, G, eps, mean, rstd, \
+                                                  u, ldu, none, stream)                                      \
+              : gln_fwd_dispatch<TY, false, false>(x, ldx, y, ldy, gamma, beta, g, T_, d, G, eps, mean, rstd, \
+                                                   u, ldu, none, stream);
   switch (dt) {
     case MTGR_F32: GLN_FWD_DT(float)
     case MTGR_BF16: GLN_FWD_DT(bf16_t)
@@ -241,15 +243,15 @@ int launch_gln_fwd(int dt, const void* x, int64_t ldx, void* y, int64_t ldy, con
 }
 
 int launch_gln_fwd_part(int dt, const PartialRows& in, void* y, int64_t ldy, const void* gamma, const void* beta,
-                        const uint8_t* g, int64_t T_, int d, float eps, float* mean, float* rstd, const void* u,
-                        int64_t ldu, hipStream_t stream) {
+                        const uint8_t* g, int64_t T_, int d, int G, float eps, float* mean, float* rstd,
+                        const void* u, int64_t ldu, hipStream_t stream) {
   if (T_ <= 0) return MTGR_OK;
   if (!in.part || in.n < 1) return MTGR_ERR_INVALID_ARG;
   const bool gate = u != nullptr;
 #define GLN_FWD_DT(TY)                                                                                             \
-  return gate ? gln_fwd_dispatch<TY, true, true>(nullptr, 0, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u, ldu, \
-                                                 in, stream)                                                       \
-              : gln_fwd_dispatch<TY, false, true>(nullptr, 0, y, ldy, gamma, beta, g, T_, d, eps, mean, rstd, u,    \
+  return gate ? gln_fwd_dispatch<TY, true, true>(nullptr, 0, y, ldy, gamma, beta, g, T_, d, G, eps, mean, rstd, u, \
+                                                 ldu, in, stream)                                                     \
+              : gln_fwd_dispatch<TY, false, true>(nullptr, 0, y, ldy, gamma, beta, g, T_, d, G, eps, mean, rstd, u, \
                                                   ldu, in, stream);
   switch (dt) {
     case MTGR_F32: GLN_FWD_DT(float)
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
   auto load_raw = [&](Raw& R, int64_t row) {
     R.mu = mean[row];
     R.rs = rstd[row];
-    R.grp = g[row];
+    R.grp = min((int)g[row], G - 1);  // never an LDS slot past the G groups
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane * 8 + i * 512;

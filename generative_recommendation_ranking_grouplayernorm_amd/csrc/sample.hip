@@ -205,9 +205,11 @@ int launch_stochastic_length(const int32_t* offsets, const uint8_t* g, const int
   int32_t* nblocks = (int32_t*)w;
   w += 256;
   int4* blocks = (int4*)w;
-  int r = launch_seg_only(offsets, g, B, seg, st);
+  int r = launch_seg_only(offsets, g, B, T, seg, st);
   if (r) return r;
-  hipLaunchKernelGGL(sl_plan_kernel, dim3(1), dim3(SL_PLAN_THREADS), 0, st, seg, u, B, s_keep, budget, starts,
+  // never more than T rows fit, whatever the metadata (the output capacity)
+  const int64_t cut = budget < T ? budget : T;
+  hipLaunchKernelGGL(sl_plan_kernel, dim3(1), dim3(SL_PLAN_THREADS), 0, st, seg, u, B, s_keep, cut, starts,
                      offsets_out, fit_out, blocks, nblocks);
   MTGR_LAUNCH_CHECK();
   if (T <= 0 || B <= 0) return MTGR_OK;

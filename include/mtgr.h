@@ -40,6 +40,21 @@
  *   - Return value: MTGR_OK or a negative mtgr_status.  Argument errors are
  *     detected on the host before anything is launched, so no output is
  *     written; MTGR_ERR_HIP reports a failed launch.
+ *   - Sizes: T <= INT32_MAX; every row stride (ld_*) at most 2^22 elements.
+ *   - Validation mode (environment MTGR_VALIDATE=1 at the first call, or
+ *     mtgr_set_validate(1)): every call that takes jagged metadata first runs
+ *     a device check of it, which reads only offsets[0..B] and
+ *     group_ids[0..T), synchronises the stream and returns
+ *     MTGR_ERR_VALIDATION, with nothing else launched and no output written,
+ *     when offsets[0] != 0, offsets decrease, offsets[B] != T, a group id is
+ *     >= 4 (>= G for the stand-alone group norms), group ids decrease inside
+ *     a user, or (backward calls with max_len > 0) a row is longer than
+ *     max_len.  It is a debugging aid: it synchronises, so a call under
+ *     stream capture returns MTGR_ERR_UNSUPPORTED, and validated calls of one
+ *     process run one at a time.  Without it, metadata outside these rules
+ *     gives undefined results; the kernels clamp offsets into [0, T] and
+ *     group ids below G, so they do not read or write outside the stated
+ *     buffers.
  *   - Calls that share a workspace must not overlap; calls with distinct
  *     workspaces may run concurrently on different streams.
  */
@@ -89,6 +104,10 @@ const char* mtgr_version(void);
 
 /* Human-readable text of a status code. Host memory, static. */
 const char* mtgr_status_string(int status);
+
+/* Switches validation mode (see the conventions above) on (1) or off (0) for
+ * the whole process; on < 0 only queries.  Returns the previous state. */
+int mtgr_set_validate(int on);
 
 /* Bytes of workspace `op` needs for these sizes (0 = none).  d = model width,
  * H = heads, max_len = an upper bound on every row's length (tokens), used
@@ -295,7 +314,7 @@ typedef struct {
   int32_t d;          /* model width, = H * dh */
   int32_t H;
   int32_t dh;
-  int32_t G;          /* number of token groups (4: U, S, R, C) */
+  int32_t G;          /* rows of gamma/beta, 4 <= G <= 8 (groups U, S, R, C use rows 0..3) */
   float eps;          /* Group LayerNorm epsilon (1e-5) */
   float alpha;        /* factor inside the SiLU of the attention scores (1) */
 } mtgr_layer_params;

@@ -59,3 +59,22 @@ def params_to(p, dtype: torch.dtype, dev):
         setattr(q, k, f64(t))
     q.H = p.H
     return dev_p, q
+
+
+GROUP_SETS = {"U/S": (0, 1), "R": (2,), "C": (3,)}
+
+
+def group_errors(got, ref, group_ids):
+    """rel-L2 over the rows of each token group (U/S, R, C) and the largest
+    absolute error of any row, so that an error confined to a few rows of one
+    group is not diluted by the rest."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    g = np.asarray(group_ids)
+    out = {}
+    for name, grp in GROUP_SETS.items():
+        sel = np.isin(g, grp)
+        if sel.any():
+            out[name] = rel_l2(got[sel], ref[sel])
+    out["max_abs"] = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    return out

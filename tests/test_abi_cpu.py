@@ -162,6 +162,11 @@ def test_argument_errors_are_reported_before_launch(lib):
     assert _call_attn_fwd(lib, ws_bytes=16) == -3     # workspace too small
     assert _call_attn_fwd(lib, H=0) == -1
     assert _call_attn_fwd(lib, B=-1) == -1
+    # row strides beyond 2^22 elements: 32-bit tile offsets inside the kernels
+    assert _call_attn_fwd(lib, ldqkv=(1 << 22) + 8) == -1
+    assert _call_attn_fwd(lib, ldo=(1 << 22) + 8) == -1
+    assert _call_attn_fwd(lib, ldqkv=1 << 22, ldo=1 << 22, ws_bytes=16) == -3  # the largest stride passes
+    assert _call_attn_fwd(lib, T=(1 << 31)) == -1                           # T beyond int32
     P = ctypes.c_void_p
     # group norm: d not a multiple of 8, too many groups
     assert lib.mtgr_group_layernorm(P(8192), P(8192), P(8192), P(8192), P(4096), 10, 60, 4, 1e-5, 1,
@@ -191,6 +196,11 @@ def test_layer_param_errors(lib):
     assert call(H=4, dh=64, d=256, G=9) == -1
     assert call(W_o=None) == -1
     assert call(H=2, dh=96, d=192) == -2
+    # the layer's rows hold groups U, S, R, C: fewer gamma/beta rows cannot
+    # serve them
+    for G in (1, 2, 3):
+        assert call(G=G) == -2, G
+    assert call(G=0) == -1
 
 
 def test_stack_and_graph_argument_errors(lib):
@@ -283,3 +293,22 @@ def test_flop_counter_matches_oracle_mask(cfg):
     else:
         off, g, t = batch.offsets, batch.group_ids, batch.timestamps
     assert flops.visible_pairs(off, g, t) == int(orc.visible_pairs(off, g, t).sum())
+
+
+def test_validation_switch(lib):
+    """mtgr_set_validate switches the process-wide validation mode and
+    reports the previous state; -1 only queries.  Host argument errors still
+    come first with validation on (nothing reaches the device check)."""
+    from generative_recommendation_ranking_grouplayernorm_amd import binding as b
+
+    prev = b.mtgr_set_validate(-1)
+    try:
+        assert b.mtgr_set_validate(1) == prev
+        assert b.mtgr_set_validate(-1) == 1
+        assert _call_attn_fwd(lib, dt=7) == -2
+        assert _call_attn_fwd(lib, q=0) == -1
+        assert _call_attn_fwd(lib, ws_bytes=16) == -3
+        assert b.mtgr_set_validate(0) == 1
+        assert b.mtgr_set_validate(-1) == 0
+    finally:
+        b.mtgr_set_validate(prev)

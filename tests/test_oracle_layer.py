@@ -40,6 +40,72 @@ def test_projection_steps_match_torch_functional():
     np.testing.assert_allclose(saved["uqkv"], F.silu(z).numpy(), rtol=1e-12, atol=1e-13)
 
 
+def _a5_a6_by_torch(p, x, saved, group_ids, d):
+    """The layer's last two steps composed from torch library routines, from
+    the oracle's attention output o and gate u: per token a
+    ``torch.nn.functional.layer_norm`` with gamma2/beta2 of the token's
+    group (paper-daily 模型怎么搭: normalise the aggregated output), times u
+    (gated by U), then ``F.linear`` with W_o and b_o plus the input
+    (marovi Métodos, the X-update: one linear layer and the residual)."""
+    o = torch.from_numpy(np.asarray(saved["o"], np.float64))
+    u = torch.from_numpy(np.asarray(saved["uqkv"], np.float64)[:, :d])
+    g = torch.from_numpy(np.asarray(group_ids, np.int64))
+    g2 = torch.from_numpy(np.asarray(p.gamma2, np.float64))
+    b2 = torch.from_numpy(np.asarray(p.beta2, np.float64))
+    n2 = torch.stack([F.layer_norm(o[i], (d,), g2[g[i]], b2[g[i]], eps=EPS) for i in range(o.shape[0])])
+    y = n2 * u
+    bias = None if p.b_o is None else torch.from_numpy(np.asarray(p.b_o, np.float64))
+    x_out = F.linear(y, torch.from_numpy(np.asarray(p.W_o, np.float64)), bias) + torch.from_numpy(x)
+    return n2.numpy(), y.numpy(), x_out.numpy()
+
+
+def _a5_a6_agrees(layer_fwd, p, x, batch):
+    d = x.shape[1]
+    x_out, saved = layer_fwd(p, x, batch.offsets, batch.group_ids, batch.timestamps, 1.0, 0.1, EPS)
+    n2, y, want = _a5_a6_by_torch(p, x, saved, batch.group_ids, d)
+    return (np.allclose(saved["n2"], n2, rtol=1e-12, atol=1e-13) and np.allclose(saved["y"], y, rtol=1e-12, atol=1e-13)
+            and np.allclose(x_out, want, rtol=1e-12, atol=1e-13))
+
+
+def _slipped(kind):
+    """The oracle's layer with one plausible slip in its last two steps (a
+    planted mistake, for the test below): the pin must reject each."""
+    def fwd(p, x, offsets, group_ids, timestamps, alpha, attn_scale, eps):
+        x_out, saved = orc.layer_fwd(p, x, offsets, group_ids, timestamps, alpha, attn_scale, eps)
+        d = x.shape[1]
+        u = saved["uqkv"][:, :d]
+        W = np.asarray(p.W_o, np.float64)
+        b = 0.0 if p.b_o is None else np.asarray(p.b_o, np.float64)[None, :]
+        if kind == "norm_after_gate":
+            n2, _, _ = orc.group_layernorm(saved["o"] * u, p.gamma2, p.beta2, group_ids, eps)
+            y = n2
+        else:
+            n2, y = saved["n2"], saved["y"]
+        if kind == "wo_untransposed":
+            out = x + y @ W + b
+        elif kind == "no_residual":
+            out = y @ W.T + b
+        elif kind == "no_bias":
+            out = x + y @ W.T
+        else:
+            out = x + y @ W.T + b
+        saved = dict(saved, n2=n2, y=y)
+        return out, saved
+    return fwd
+
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_gate_and_output_projection_match_torch_functional(bias):
+    """a5-a6 pinned on their own: GLN2 of the attention output, times U, then
+    the output projection and the residual, against torch's layer_norm and
+    linear; and each slip (norm after the gate, W_o untransposed, residual
+    dropped, bias dropped) fails that pin."""
+    batch, p, x = _tiny(seed=6, bias=bias)
+    assert _a5_a6_agrees(orc.layer_fwd, p, x, batch)
+    for kind in ("norm_after_gate", "wo_untransposed", "no_residual") + (("no_bias",) if bias else ()):
+        assert not _a5_a6_agrees(_slipped(kind), p, x, batch), kind
+
+
 def test_layer_bwd_matches_finite_differences():
     batch, p, x = _tiny(seed=1)
     args = (batch.offsets, batch.group_ids, batch.timestamps, 1.0, 0.1)
