@@ -219,6 +219,15 @@ def cpu_baseline(batch, params, x, R, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     p = params[0]
     scale = 1.0 / batch.max_len
     attn_t = layer_t = 0.0
@@ -248,7 +257,10 @@ def cpu_baseline(batch, params, x, R, budget_s):
     return {
         "value": attn_f / attn_t / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": int(min(threads, cores)),
+        "cores_available": int(cores),
+        "blas_threads": int(threads),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"first {users} users ({toks} tokens) of the same 65,536-token batch, fp64 NumPy: "
                   f"attention fwd+bwd timed alone ({attn_t:.2f} s), then the whole layer fwd+bwd "
@@ -330,15 +342,15 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
     lib.mtgr_profile_enable(1)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
+    ms_total = ev[0].elapsed_time(ev[-1])
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     prof = profile_summary(lib)
     lib.mtgr_profile_enable(0)
     ms_step = ms_total / args.steps
@@ -387,6 +399,8 @@ def main():
                 "peak": BF16_PEAK_TFLOPS if dk["bound"] == "mfma" else HBM_PEAK_GBS,
                 "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
 
+    gln = gln_rotated(mb, T, d, G, dt, dev, stream)
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
@@ -400,6 +414,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": {"min": round(step_ms[0], 4), "median": round(step_ms[len(step_ms) // 2], 4),
+                    "p90": round(step_ms[min(len(step_ms) - 1, (9 * len(step_ms)) // 10)], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -414,9 +430,57 @@ def main():
         "layer_tflops": round(layer_flops / (ms_step / 1e3) / 1e12, 2),
         "roofline": roofline,
         "kernels": kernels,
+        "gln_hbm_rotated": gln,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def gln_rotated(mb, T, d, G, dt, dev, stream, sets=4, reps=3):
+    """Group LayerNorm forward and backward through the C ABI on the layer's
+    [T, d] shape, each launch on the next of ``sets`` distinct buffer sets
+    (together larger than the 256 MB last-level cache, so every launch reads
+    from HBM), HIP events around each launch on the stream it runs on.
+    Bytes per launch: forward x in, y out, mean/rstd out (+ group id);
+    backward dy and x in, dx out, mean/rstd and group id in (the per-group
+    gamma/beta sums are a few KB)."""
+    import torch
+
+    e = 2
+    gen = torch.Generator(device=dev).manual_seed(0)
+    g = torch.randint(0, G, (T,), generator=gen, device=dev, dtype=torch.int64).sort().values.to(torch.uint8)
+    gam = torch.ones(G, d, dtype=dt, device=dev)
+    bet = torch.zeros(G, d, dtype=dt, device=dev)
+    bufs = []
+    for _ in range(sets):
+        x = torch.randn(T, d, generator=gen, device=dev).to(dt)
+        bufs.append(dict(x=x, y=torch.empty_like(x), dy=torch.randn(T, d, generator=gen, device=dev).to(dt),
+                         dx=torch.empty_like(x), mean=torch.empty(T, device=dev), rstd=torch.empty(T, device=dev)))
+    dg = torch.empty(G, d, device=dev)
+    db = torch.empty(G, d, device=dev)
+    ws = mb.workspace(mb.OP_GLN_BWD, 0, T, d, 1, dt, dev)
+    times = {"fwd": [], "bwd": []}
+    for r in range(reps + 1):
+        for b in bufs:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            mb.mtgr_group_layernorm(b["x"], b["y"], gam, bet, g, 1e-5, b["mean"], b["rstd"], stream=stream)
+            ev[1].record(stream)
+            mb.mtgr_group_layernorm_bwd(b["dy"], b["x"], b["mean"], b["rstd"], gam, g, b["dx"], dg, db, ws,
+                                        stream=stream)
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            if r > 0:  # the first round warms up
+                times["fwd"].append(ev[0].elapsed_time(ev[1]))
+                times["bwd"].append(ev[1].elapsed_time(ev[2]))
+    nbytes = {"fwd": T * (2 * e * d + 8 + 1), "bwd": T * (3 * e * d + 8 + 1)}
+    out = {"buffer_sets": sets, "set_bytes": int(sets and 4 * T * d * e + 8 * T), "launches": reps * sets}
+    for k in ("fwd", "bwd"):
+        ms = sorted(times[k])[len(times[k]) // 2]
+        gbs = nbytes[k] / (ms / 1e3) / 1e9
+        out[k] = {"median_ms": round(ms, 5), "bytes": nbytes[k], "GB/s": round(gbs, 1),
+                  "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def serving_bench(args):
