@@ -29,7 +29,7 @@ EXPORTED = (
     "mtgr_hstu_layer_fwd", "mtgr_hstu_layer_bwd", "mtgr_hstu_stack_fwd", "mtgr_stack_graph_create",
     "mtgr_stack_graph_launch", "mtgr_stack_graph_destroy", "mtgr_stochastic_length",
     "mtgr_head_workspace_size", "mtgr_candidate_head_fwd", "mtgr_candidate_head_loss", "mtgr_serving_graph_create",
-    "mtgr_set_validate",
+    "mtgr_set_validate", "mtgr_hstu_attn_fwd_noalloc",
 )
 
 
@@ -97,6 +97,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.c_int),
         "mtgr_hstu_attn_fwd": ([P, P, P, I64, P, I64, P, P, P, I32, I64, I32, I32, F, F, ctypes.c_int, P, SZ, P],
                                ctypes.c_int),
+        "mtgr_hstu_attn_fwd_noalloc": ([P, P, P, I64, P, I64, P, P, P, I32, I64, I32, I32, F, F, ctypes.c_int, P],
+                                       ctypes.c_int),
         "mtgr_hstu_attn_bwd": ([P, P, P, I64, P, I64, P, P, P, I64, P, P, P, I32, I64, I32, I32, I32, F, F,
                                 ctypes.c_int, P, SZ, P], ctypes.c_int),
         "mtgr_hstu_layer_fwd": ([ctypes.POINTER(LayerParams), P, P, ctypes.POINTER(LayerSaved), P, P, P, I32,
@@ -220,6 +222,16 @@ def mtgr_hstu_attn_fwd(q, k, v, o, offsets, group_ids, timestamps, H, dh, alpha,
     _check("mtgr_hstu_attn_fwd", load_library().mtgr_hstu_attn_fwd(
         _p(q), _p(k), _p(v), _ld(q), _p(o), _ld(o), _p(offsets), _p(group_ids), _p(timestamps), B, T, H, dh,
         alpha, attn_scale, dtype_code(q.dtype), _p(ws), ws.numel(), _stream(stream)))
+
+
+def mtgr_hstu_attn_fwd_noalloc(q, k, v, o, offsets, group_ids, timestamps, H, dh, alpha, attn_scale,
+                               stream=None) -> None:
+    B = offsets.numel() - 1
+    T = q.shape[0]
+    assert _ld(q) == _ld(k) == _ld(v)
+    _check("mtgr_hstu_attn_fwd_noalloc", load_library().mtgr_hstu_attn_fwd_noalloc(
+        _p(q), _p(k), _p(v), _ld(q), _p(o), _ld(o), _p(offsets), _p(group_ids), _p(timestamps), B, T, H, dh,
+        alpha, attn_scale, dtype_code(q.dtype), _stream(stream)))
 
 
 def mtgr_hstu_attn_bwd(q, k, v, d_o, dq, dk, dv, offsets, group_ids, timestamps, H, dh, alpha, attn_scale, ws,

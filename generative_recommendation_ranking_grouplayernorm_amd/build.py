@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmtgr.so")
 
-SOURCES = ["api.cpp", "graph.cpp", "profile.cpp", "prep.hip", "sample.hip", "head.hip", "rownorm.hip", "gemm.hip", "attn.hip"]
+SOURCES = ["api.cpp", "graph.cpp", "profile.cpp", "prep.hip", "sample.hip", "head.hip", "rownorm.hip", "gemm.hip", "attn.hip",
+           "noalloc.hip"]
 HEADERS = ["common.h", "kernels.h"]
 
 # Packed-FP32 instructions are disabled: plain float code only.

@@ -337,18 +337,40 @@ int mtgr_group_layernorm_bwd(const void* dy, const void* x, const float* mean, c
                         nullptr, 0, nullptr, 0, nullptr, 0, dgamma, dbeta, workspace, S(stream));
 }
 
-static int attn_common_checks(const void* q, const void* k, const void* v, int64_t ldqkv,
-                              const int32_t* offsets, const uint8_t* g, const int64_t* ts, int32_t B,
-                              int64_t T, int32_t H, int32_t dh, int dt, void* workspace, size_t ws_bytes) {
+static int attn_arg_checks(const void* q, const void* k, const void* v, int64_t ldqkv, const int32_t* offsets,
+                           const uint8_t* g, const int64_t* ts, int32_t B, int64_t T, int32_t H, int32_t dh,
+                           int dt) {
   if (!dt_ok(dt)) return MTGR_ERR_UNSUPPORTED;
   if (!attn_shape_ok(dt, dh)) return MTGR_ERR_UNSUPPORTED;
   if (H < 1 || !jagged_ok(offsets, g, ts, B, T)) return MTGR_ERR_INVALID_ARG;
   if (ldqkv < (int64_t)H * dh) return MTGR_ERR_INVALID_ARG;
   if (T > 0 && (!q || !k || !v)) return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(q, ldqkv, dt) || !vec_ok(k, ldqkv, dt) || !vec_ok(v, ldqkv, dt)) return MTGR_ERR_INVALID_ARG;
+  return MTGR_OK;
+}
+
+static int attn_common_checks(const void* q, const void* k, const void* v, int64_t ldqkv,
+                              const int32_t* offsets, const uint8_t* g, const int64_t* ts, int32_t B,
+                              int64_t T, int32_t H, int32_t dh, int dt, void* workspace, size_t ws_bytes) {
+  const int r = attn_arg_checks(q, k, v, ldqkv, offsets, g, ts, B, T, H, dh, dt);
+  if (r) return r;
   if (ws_bytes < attn_ws(B, T) || (B > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
   return MTGR_OK;
 }
+
+}  // extern "C"
+
+int mtgr::attn_fwd_arg_checks(const void* q, const void* k, const void* v, int64_t ld_qkv, const void* o,
+                              int64_t ld_o, const int32_t* offsets, const uint8_t* group_ids,
+                              const int64_t* timestamps, int32_t B, int64_t T, int32_t H, int32_t dh, int dt) {
+  // no workspace here: the variant without one keeps its lists elsewhere
+  const int r = attn_arg_checks(q, k, v, ld_qkv, offsets, group_ids, timestamps, B, T, H, dh, dt);
+  if (r) return r;
+  if (ld_o < (int64_t)H * dh || (T > 0 && !o) || !vec_ok(o, ld_o, dt)) return MTGR_ERR_INVALID_ARG;
+  return MTGR_OK;
+}
+
+extern "C" {
 
 int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_qkv, void* o, int64_t ld_o,
                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps,

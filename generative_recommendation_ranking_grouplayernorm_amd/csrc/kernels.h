@@ -34,6 +34,11 @@ int head_fwd_run(const mtgr_head_params* p, const void* x, int64_t ld_x, const i
                  const uint8_t* group_ids, int32_t B, int64_t T, int64_t n_cand, float* logits, int dt,
                  void* workspace, size_t ws_bytes, hipStream_t stream, bool check_meta);
 
+// Host-side argument checks of mtgr_hstu_attn_fwd other than its workspace.
+int attn_fwd_arg_checks(const void* q, const void* k, const void* v, int64_t ld_qkv, const void* o, int64_t ld_o,
+                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,
+                        int64_t T, int32_t H, int32_t dh, int dt);
+
 // Host-side argument checks of mtgr_hstu_stack_fwd (MTGR_OK or a status).
 int stack_fwd_validate(const mtgr_layer_params* layers, int32_t L, const void* x_in, void* x_out,
                        const int32_t* offsets, const uint8_t* group_ids, const int64_t* timestamps, int32_t B,

@@ -280,6 +280,27 @@ int mtgr_hstu_attn_fwd(const void* q, const void* k, const void* v, int64_t ld_q
                        mtgr_stream_t stream);
 
 /*
+ * mtgr_hstu_attn_fwd for callers that cannot allocate device memory or pass
+ * a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, layout and results as
+ * mtgr_hstu_attn_fwd without `workspace` (every (query tile, head) runs as
+ * one workgroup, so results of short batches can differ from
+ * mtgr_hstu_attn_fwd's split key runs by fp32 rounding order).  Its tile
+ * lists live in a static device array of MTGR_NOALLOC_SCRATCH_BYTES per GPU,
+ * held until the process ends; the call allocates nothing.  The lists take
+ * about 48 bytes per user plus 16 bytes per 128 tokens (plus under 2 KB of
+ * alignment): every batch with B <= 16384 and T <= 4,194,304 fits; a batch
+ * that does not returns MTGR_ERR_UNSUPPORTED before any launch.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.
+ */
+#define MTGR_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
+int mtgr_hstu_attn_fwd_noalloc(const void* q, const void* k, const void* v, int64_t ld_qkv, void* o,
+                               int64_t ld_o, const int32_t* offsets, const uint8_t* group_ids,
+                               const int64_t* timestamps, int32_t B, int64_t T, int32_t H, int32_t dh,
+                               float alpha, float attn_scale, int dt, mtgr_stream_t stream);
+
+/*
  * a7 - backward of mtgr_hstu_attn_fwd.  With S = alpha q k^T,
  * A = SiLU(S) * M:  dV = c A^T dO,  dA = c dO V^T,  dS = dA * M * SiLU'(S),
  * dQ = alpha dS K,  dK = alpha dS^T Q  (c = attn_scale).  The attention
