@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="offline: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "'bench.py --copy-probe N' into profiles/traffic.json and a markdown table")
+    ap.add_argument("--counter-summary", nargs="+", metavar="PMC_DIR",
+                    help="offline: per-kernel table of rocprofv3 --pmc runs (SQ_* and GRBM_GUI_ACTIVE counters of "
+                         "'bench.py --steps 3 --warmup 1 --cpu-seconds 0') with MFMA-busy and vector-ALU fractions")
     ap.add_argument("--stats-summary", metavar="STATS_CSV",
                     help="offline: turn a rocprofv3 --stats kernel_stats.csv into a markdown table on stdout")
     ap.add_argument("--probe-mib", type=int, default=256, help="copy size used by --pmc-summary")
@@ -191,6 +194,63 @@ def pmc_summary(fetch_dir, write_dir, probe_mib):
           f"WRITE_SIZE {cw:.0f} KiB (scale {w_scale:.4f})")
 
 
+def counter_summary(dirs):
+    """Per-kernel averages of SQ_* / GRBM_GUI_ACTIVE counters from rocprofv3
+    --pmc runs, with derived fractions.  On this part the SQ and GRBM
+    counters cover half of the chip (4 of the 8 XCDs): SQ_INSTS_MFMA of the
+    UQKV projection reads exactly half of its known instruction count
+    (8 T d^2 / 32768), so instruction counts are doubled and GRBM_GUI_ACTIVE
+    (summed over the 4 counted XCDs) divided by 4 gives the clock cycles of
+    the dispatch.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (512 counted SIMDs
+    x cycles); the vector-ALU issue estimate counts 4 cycles per plain and 8
+    per transcendental wave instruction (measured issue costs of one wave)."""
+    import collections
+    import csv
+    import glob
+    import re
+
+    rows = []
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += list(csv.DictReader(open(f)))
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = collections.defaultdict(dict)
+    for r in rows:
+        # one template instance serves several products: tell them apart by grid size
+        k = (r["Kernel_Name"], int(r["Grid_Size"]))
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        dur[k][(r["Dispatch_Id"], r["Process_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+
+    def short(k):
+        name, grid = k
+        m = re.search(r"mtgr(?:\d+|::)(\w+?)(?:I|<)", name)
+        base = m.group(1) if m else name[:40]
+        e = re.search(r"(true|false), (\d), mtgr::GemmCfg", name) or re.search(r"Lb(\d)ELi(\d)ENS_7GemmCfg", name)
+        if e:
+            base += f" epi {e.group(2)}"
+        return f"{base}, grid {grid}"
+
+    print("| kernel | dispatches | avg us | clock GHz | MFMA instr | executed TFLOP/s | MFMA busy | VALU instr "
+          "(trans) | VALU issue est. | LDS instr | LDS bank-conflict cycles | wait / wave cycles |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for k in sorted(acc, key=lambda k: -sum(dur[k].values()) / len(dur[k])):
+        n = len(dur[k])
+        a = {c: v / n for c, v in acc[k].items()}
+        ns = sum(dur[k].values()) / n
+        cyc = a.get("GRBM_GUI_ACTIVE", 0) / 4
+        if cyc <= 0 or ns <= 0:
+            continue
+        mfma = 2 * a.get("SQ_INSTS_MFMA", 0)
+        valu = 2 * a.get("SQ_INSTS_VALU", 0)
+        trans = 2 * a.get("SQ_INSTS_VALU_TRANS_F32", 0)
+        busy = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (512 * cyc)
+        valu_est = ((valu - trans) * 4 + trans * 8) / (1024 * cyc)
+        wait = a.get("SQ_WAIT_ANY", 0) / a["SQ_WAVE_CYCLES"] if a.get("SQ_WAVE_CYCLES") else float("nan")
+        print(f"| `{short(k)}` | {n // 2} | {ns / 1e3:.1f} | {cyc / ns:.2f} | {mfma:.3g} | "
+              f"{mfma * 32768 / (ns * 1e-9) / 1e12:.0f} | {busy:.3f} | {valu:.3g} ({trans:.2g}) | {valu_est:.3f} | "
+              f"{2 * a.get('SQ_INSTS_LDS', 0):.3g} | {2 * a.get('SQ_LDS_BANK_CONFLICT', 0):.3g} | {wait:.3f} |")
+
+
 def stats_summary(path):
     import csv
 
@@ -273,6 +333,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.probe_mib)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.stats_summary:
         stats_summary(args.stats_summary)
