@@ -673,6 +673,25 @@ template <typename T, bool MASKED>
 __device__ __forceinline__ void silu_terms_rows_queries(const f32x16_t (&x)[2], op8 (&w)[4], uint32_t* fx, int lane,
                                                         float kexp, float alpha, int q0, int kj, int g, int s_end,
                                                         int r_end, const int64_t* tsq, int64_t tk) {
+  // Element (t, j) is query q0 + qq, qq = c + 4 g with c = 32 t + 8 (j / 4)
+  // + j % 4 a constant.  The mask's index tests become comparisons of c with
+  // per-call values: the query is real-time or later when c >= thr and sits
+  // on the key's diagonal when c == dg.  A candidate key takes thr below
+  // every c and a timestamp no query is earlier than, which leaves only the
+  // diagonal; a static key sees every query.  The empty asm keeps the
+  // compiler from rewriting the tests as q0 + c comparisons, which it would
+  // otherwise precompute for all 32 elements outside the caller's loop.
+  int thr = 0, dg = 0;
+  int64_t tke = 0;
+  bool kstat = true;
+  if (MASKED) {
+    const bool kcand = kj >= r_end;
+    kstat = kj < s_end;
+    thr = kcand ? -1024 : s_end - q0 - 4 * g;
+    dg = kj - q0 - 4 * g;
+    tke = kcand ? INT64_MAX : tk;
+    asm volatile("" : "+v"(thr), "+v"(dg));
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -687,8 +706,10 @@ __device__ __forceinline__ void silu_terms_rows_queries(const f32x16_t (&x)[2], 
         // SiLU'(y) = sigma + y sigma (1 - sigma), y = alpha s
         f[h] = __builtin_fmaf(alpha * pv[h], 1.0f - sg, sg);
         if (MASKED) {
-          const int qq = t * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-          const bool vis = visible_ts(q0 + qq, kj, s_end, r_end, tsq[qq], tk);
+          const int c = t * 32 + 8 * (j >> 2) + (j & 3);
+          // bitwise throughout: a conditional form lets the compiler put the
+          // timestamp read under a per-lane branch
+          const bool vis = kstat | ((c >= thr) & ((tke < tsq[c + 4 * g]) | (c == dg)));
           pv[h] = vis ? pv[h] : 0.f;
           f[h] = vis ? f[h] : 0.f;
         }
@@ -873,11 +894,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     int H, float kexp, float alpha, float scale, uint8_t* __restrict__ dS, int64_t ds_cap,
     const int64_t* __restrict__ tprefix) {
   constexpr int NS = DH / 16, NC = DH / 32;
+  // three stage buffers: the S side works on stage i while the dA side works
+  // on stage i - 1 and stage i + 1 is being written
   struct Smem {
-    uint16_t Qs[2][QuadRows<DH>::SIZE];
-    uint16_t Ds[2][QuadRows<DH>::SIZE];
-    uint32_t Fx[4][32 * 16 * 2];  // per group: 2 x 16 x 32 lanes
-    int64_t Tq[2][KV_BQ];         // query timestamps of the stage
+    uint16_t Qs[3][QuadRows<DH>::SIZE];
+    uint16_t Ds[3][QuadRows<DH>::SIZE];
+    uint32_t Fx[2][4][32 * 16 * 2];  // per stage parity and group: 2 x 16 x 32 lanes
+    int64_t Tq[3][KV_BQ];            // query timestamps of the stage
   };
   __shared__ __attribute__((aligned(16))) union {
     Smem m;
@@ -963,26 +986,32 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     swrite(0);
   }
   __syncthreads();
-  uint32_t* fx = Fx[grp];
   TrAddr<DH> tra;
   tra.init(lane);
-  for (int it = 0; it < nqt; ++it) {
-    const int buf = it & 1, q0 = qlo + it * KV_BQ;
-    gload(q0 + KV_BQ);  // past the query range: zeros, never used
-    // A second use of the loaded values here, under a condition that never
-    // holds (q0 is a row index, never negative) but that the compiler cannot
-    // fold, keeps the loads at the top of the stage: their real use follows
-    // the mid-stage barrier, and code sinking would otherwise move them
-    // there, a whole stage of latency hiding lost.
-    if (q0 < 0) {
+  // Iteration it (0..nqt): the S side takes stage it (S, P, f into
+  // Fx[it % 2], then dV += P^T dO), the dA side stage it - 1 (dA, dS = dA f
+  // with the f written one iteration earlier, then dK += dS^T Q), so that
+  // one wave's vector work runs beside its partner's MFMAs; one barrier per
+  // iteration.  Stage j lives in buffer j % 3: while stages it and it - 1 are
+  // read, both sides write their halves of stage it + 1 (Q rows, dO rows) to
+  // the third buffer.  Each side runs a loop of its own, so that neither
+  // carries the other's registers; both pass nqt + 1 barriers.
+  //
+  // A second use of the loaded values, under a condition that never holds
+  // (the stage row is never negative) but that the compiler cannot fold,
+  // keeps each iteration's loads at its top: their real use is the stage
+  // write at its end, and code sinking would otherwise move them there, a
+  // whole iteration of latency hiding lost.
+  auto keep_loads_early = [&](int it, int nbuf) {
+    if (qlo + it * KV_BQ < 0) {
       uint32_t any = 0;
 #pragma unroll
       for (int r = 0; r < LCH; ++r) any |= ldx[r].x | ldx[r].y | ldx[r].z | ldx[r].w;
-      Tq[buf][lane] = any;
+      Tq[nbuf][lane] = any;
     }
-    // phase 1: S (producer) or dA (consumer) for 64 queries x 32 keys
-    const uint16_t* A = producer ? Qs[buf] : Ds[buf];
-    f32x16_t x[2];
+  };
+  // phase 1: S (producer) or dA (consumer) for 64 queries x 32 keys
+  auto phase1 = [&](const uint16_t* A, f32x16_t (&x)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand_swz<DH>(A, t * 32, 0, lane), bop[0], f32x16_t{});
 #pragma unroll
@@ -990,15 +1019,49 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
 #pragma unroll
       for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand_swz<DH>(A, t * 32, s, lane), bop[s], x[t]);
     pipeline_lds_mfma<2 * NS, 8>();
-    op8 w[4];
-    if (producer) {
-      if (full)
-        silu_terms_rows_queries<T, false>(x, w, fx, lane, kexp, alpha, q0, kj, g, s_end, r_end, Tq[buf], tk);
-      else
-        silu_terms_rows_queries<T, true>(x, w, fx, lane, kexp, alpha, q0, kj, g, s_end, r_end, Tq[buf], tk);
-    }
-    __syncthreads();  // f of this stage visible to the consumers
-    if (!producer) {
+  };
+  // phase 2: dV += P^T dO (producer) or dK += dS^T Q (consumer), the B
+  // operand read transposed from the other role's row-major tile
+  auto phase2 = [&](const op8 (&w)[4], const uint16_t* Bt) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], tra.get(Bt, u, c), acc[c]);
+    pipeline_lds2_mfma<4 * NC, 8>();
+  };
+  if (producer) {
+    // one loop per mask variant, so that the mask-free loop keeps its
+    // registers to itself
+    auto run = [&](auto masked) {
+      for (int it = 0; it < nqt; ++it) {
+        const int buf = it % 3, nbuf = (it + 1) % 3, q0 = qlo + it * KV_BQ;
+        gload(q0 + KV_BQ);  // past the query range: zeros, never used
+        keep_loads_early(it, nbuf);
+        f32x16_t x[2];
+        phase1(Qs[buf], x);
+        op8 w[4];
+        silu_terms_rows_queries<T, decltype(masked)::value>(x, w, Fx[it & 1][grp], lane, kexp, alpha, q0, kj, g,
+                                                             s_end, r_end, Tq[buf], tk);
+        phase2(w, Ds[buf]);
+        swrite(nbuf);
+        __syncthreads();
+      }
+    };
+    if (full) run(std::false_type{});
+    else run(std::true_type{});
+    __syncthreads();  // the dA side's last stage
+  } else {
+    // iteration 0: only the dO rows of stage 1
+    gload(qlo + KV_BQ);
+    swrite(1);
+    __syncthreads();
+    for (int it = 1; it <= nqt; ++it) {
+      const int st = it - 1, buf = st % 3, nbuf = (it + 1) % 3, q0 = qlo + st * KV_BQ;
+      gload(qlo + (it + 1) * KV_BQ);  // past the query range: zeros, never used
+      keep_loads_early(it, nbuf);
+      f32x16_t x[2];
+      phase1(Ds[buf], x);
+      const uint32_t* fx = Fx[st & 1][grp];
       float d[2][16];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -1008,34 +1071,26 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
           d[t][2 * e] = __builtin_fmaf(x[t][2 * e], from_bits16<f16_t>((uint16_t)(fv & 0xffff)), 0.0f);
           d[t][2 * e + 1] = __builtin_fmaf(x[t][2 * e + 1], from_bits16<f16_t>((uint16_t)(fv >> 16)), 0.0f);
         }
+      op8 w[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) w[u] = pack_kstep<T>(d, u);
+      if (STORE) {
+        // Non-temporal dS stores through a resource of size zero where
+        // nothing is kept (rows beyond the dS buffer), never under a branch:
+        // the wait before the stage write then covers only this iteration's
+        // loads, not the stores, whose completion takes far longer.
+        const int qs = (q0 - lo) >> 6;  // 64-row stage of the user's rows
+        const __amdgpu_buffer_rsrc_t drs =
+            make_rsrc(ds_on ? dsb + (qs >> 1) * ds_qt_stride + (qs & 1) * 8192 : dS, ds_on ? 4096 : 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, w[u].v), drs, lane * 16 + u * 1024, 0,
+                                                 2 /* non-temporal */);
+      }
+      phase2(w, Qs[buf]);
+      swrite(nbuf);
+      __syncthreads();
     }
-    if (STORE) {
-      // Every wave issues the (non-temporal) dS stores, through a resource
-      // of size zero where nothing is kept (the S side, rows beyond the dS
-      // buffer), so that they sit in straight-line code: the wait before the
-      // next stage's LDS writes then covers only that stage's loads.  Under
-      // a branch, the wait counts merged at its join would make it cover
-      // the stores as well, whose completion takes far longer.
-      const int qs = (q0 - lo) >> 6;
-      const __amdgpu_buffer_rsrc_t drs =
-          make_rsrc(ds_on ? dsb + (qs >> 1) * ds_qt_stride + (qs & 1) * 8192 : dS, ds_on ? 4096 : 0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, w[u].v), drs, lane * 16 + u * 1024, 0,
-                                               2 /* non-temporal */);
-    }
-    // phase 2: dV += P^T dO (producer) or dK += dS^T Q (consumer), the B
-    // operand read transposed from the other role's row-major tile
-    const uint16_t* Bt = producer ? Ds[buf] : Qs[buf];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], tra.get(Bt, u, c), acc[c]);
-    pipeline_lds2_mfma<4 * NC, 8>();
-    swrite(buf ^ 1);
-    __syncthreads();
   }
   // producer holds dV, consumer dK; both scale by alpha * c
   wave_store_rows<T, NC>(sm.ep + wave * EP_FLOATS, acc, 0, lane, k0 + grp * 32, hi, alpha * scale,

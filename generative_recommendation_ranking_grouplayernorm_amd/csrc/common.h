@@ -76,8 +76,17 @@ template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi)
 // Raw buffer resource over `bytes` bytes from `base`: 16-byte loads at
 // offsets at or beyond `bytes` return zeros (hardware range check).
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// Every resource built here is wave-uniform.  The base and size are passed
+// through readfirstlane so that they stay in scalar registers even when the
+// compiler has computed them in vector registers (under scalar register
+// pressure it does); a resource it cannot prove uniform would otherwise be
+// used inside a per-lane loop around every load and store.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* b = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
   i32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
