@@ -1010,15 +1010,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
       Tq[nbuf][lane] = any;
     }
   };
-  // phase 1: S (producer) or dA (consumer) for 64 queries x 32 keys
+  // phase 1: S (producer) or dA (consumer) for 64 queries x 32 keys.  The
+  // operand reads run three k-steps ahead of the MFMAs in source order too:
+  // where register pressure makes the compiler drop the scheduling hint and
+  // keep source order, each MFMA would otherwise wait a full LDS round trip.
   auto phase1 = [&](const uint16_t* A, f32x16_t (&x)[2]) {
+    constexpr int AH = NS < 3 ? NS : 3;
+    op8 ring[AH][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand_swz<DH>(A, t * 32, 0, lane), bop[0], f32x16_t{});
+    for (int s = 0; s < AH; ++s)
 #pragma unroll
-    for (int s = 1; s < NS; ++s)
+      for (int t = 0; t < 2; ++t) ring[s][t] = row_operand_swz<DH>(A, t * 32, s, lane);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(row_operand_swz<DH>(A, t * 32, s, lane), bop[s], x[t]);
-    pipeline_lds_mfma<2 * NS, 8>();
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(ring[s % AH][t], bop[s], s == 0 ? f32x16_t{} : x[t]);
+      if (s + AH < NS) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ring[s % AH][t] = row_operand_swz<DH>(A, t * 32, s + AH, lane);
+      }
+    }
+    pipeline_lds_mfma<2 * NS, 2 * AH>();
   };
   // phase 2: dV += P^T dO (producer) or dK += dS^T Q (consumer), the B
   // operand read transposed from the other role's row-major tile
