@@ -33,7 +33,7 @@ inline bool vec_ok(const void* p, int64_t ld, int dt) {
 
 bool attn_shape_ok(int dt, int dh) {
   if (dt == MTGR_F32) return dh == 16 || dh == 32 || dh == 64 || dh == 128;
-  return dh == 64 || dh == 128;
+  return dh == 32 || dh == 64 || dh == 128;
 }
 
 size_t attn_ws(int B, int64_t T) { return prep_workspace_bytes(B, T); }

@@ -784,9 +784,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
       bop[s].v = qv ? a : u32x4_t{0, 0, 0, 0};
     }
   }
-  f32x16_t acc[NC / 2];  // half of the dQ columns per role
+  // dQ column blocks per role: producers [0, NC / 2), consumers the rest
+  // (with one block, DH = 32, the consumers take it)
+  constexpr int NCH = (NC + 1) / 2;
+  const int ncol = producer ? NC / 2 : NC - NC / 2;
+  f32x16_t acc[NCH];
 #pragma unroll
-  for (int c = 0; c < NC / 2; ++c)
+  for (int c = 0; c < NCH; ++c)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
 
@@ -858,18 +862,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
 #pragma unroll
       for (int u = 0; u < 4; ++u) da[u].v = *(const u32x4_t*)&fx[(u * 4) * 64 + lane * 4];
     }
-    // dQ += dS K: producers take column blocks [0, NC/2), consumers the rest
+    // dQ += dS K over this role's column blocks
     const int cb = producer ? 0 : NC / 2;
+    if (ncol > 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int c = 0; c < NC / 2; ++c)
-        acc[c] = mfma32<T>(da[u], vt_operand(Kt[buf], u, (cb + c) * 32, lane), acc[c]);
+        for (int c = 0; c < NCH; ++c)
+          acc[c] = mfma32<T>(da[u], vt_operand(Kt[buf], u, (cb + c) * 32, lane), acc[c]);
+    }
     if (more) swrite(buf ^ 1);
     __syncthreads();
   }
-  wave_store_rows<T, NC / 2>(sm.ep + wave * EP_FLOATS, acc, producer ? 0 : NC / 2, lane, q0 + grp * 32, hi,
-                             out_scale, dQ, lddq, hc, zq, ldz);
+  if (ncol > 0)
+    wave_store_rows<T, NCH>(sm.ep + wave * EP_FLOATS, acc, producer ? 0 : NC / 2, lane, q0 + grp * 32, hi,
+                            out_scale, dQ, lddq, hc, zq, ldz);
 }
 
 // ---------------------------------------------------------------------------
@@ -1504,10 +1511,12 @@ int launch_attn_fwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t s
   if (dt == MTGR_BF16) {
     if (a.dh == 128) fwd_mfma<bf16_t, 128>(a, pv, st);
     else if (a.dh == 64) fwd_mfma<bf16_t, 64>(a, pv, st);
+    else if (a.dh == 32) fwd_mfma<bf16_t, 32>(a, pv, st);
     else return MTGR_ERR_UNSUPPORTED;
   } else if (dt == MTGR_F16) {
     if (a.dh == 128) fwd_mfma<f16_t, 128>(a, pv, st);
     else if (a.dh == 64) fwd_mfma<f16_t, 64>(a, pv, st);
+    else if (a.dh == 32) fwd_mfma<f16_t, 32>(a, pv, st);
     else return MTGR_ERR_UNSUPPORTED;
   } else if (dt == MTGR_F32) {
     switch (a.dh) {
@@ -1529,10 +1538,12 @@ int launch_attn_bwd(int dt, const AttnArgs& a, const PrepView& pv, hipStream_t s
   if (dt == MTGR_BF16) {
     if (a.dh == 128) bwd_mfma<bf16_t, 128>(a, pv, st);
     else if (a.dh == 64) bwd_mfma<bf16_t, 64>(a, pv, st);
+    else if (a.dh == 32) bwd_mfma<bf16_t, 32>(a, pv, st);
     else return MTGR_ERR_UNSUPPORTED;
   } else if (dt == MTGR_F16) {
     if (a.dh == 128) bwd_mfma<f16_t, 128>(a, pv, st);
     else if (a.dh == 64) bwd_mfma<f16_t, 64>(a, pv, st);
+    else if (a.dh == 32) bwd_mfma<f16_t, 32>(a, pv, st);
     else return MTGR_ERR_UNSUPPORTED;
   } else if (dt == MTGR_F32) {
     switch (a.dh) {

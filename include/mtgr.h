@@ -265,7 +265,7 @@ int mtgr_group_layernorm_bwd(const void* dy, const void* x, const float* mean, c
  *   q, k, v : [T, H*dh] views with row stride ld_qkv elements (they may point
  *             into one fused [T, 4d] buffer); head h = columns h*dh..h*dh+dh-1
  *   o       : [T, H*dh] with row stride ld_o, written
- *   bf16/f16: dh in {64, 128} (MFMA kernels); f32: dh in {16, 32, 64, 128}.
+ *   bf16/f16: dh in {32, 64, 128} (MFMA kernels); f32: dh in {16, 32, 64, 128}.
  *   workspace : MTGR_OP_ATTN_FWD bytes (sized with the call's d = H*dh and
  *               H).  For 16-bit batches too short to occupy the GPU (one
  *               serving request) the key range of every query tile is split

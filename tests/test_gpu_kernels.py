@@ -129,7 +129,8 @@ def _run_attention(mb, batch, d, H, dtype, seed, alpha=1.0, with_bwd=True, max_l
 
 
 @pytest.mark.parametrize("dtype,d,H", [(torch.float32, 64, 2), (torch.bfloat16, 256, 2),
-                                       (torch.float16, 256, 2), (torch.bfloat16, 256, 4)])
+                                       (torch.float16, 256, 2), (torch.bfloat16, 256, 4),
+                                       (torch.bfloat16, 64, 2), (torch.float16, 128, 4)])
 @pytest.mark.parametrize("which", ["cfg1", "edge"])
 @pytest.mark.parametrize("ds", ["stored", "recomputed"])
 def test_attention_parity(mb, dtype, d, H, which, ds):
@@ -191,13 +192,15 @@ def test_prep_group_id_paths(mb, case):
 
 
 @pytest.mark.parametrize("ds", ["stored", "recomputed"])
-def test_attention_bf16_long_users(mb, ds):
-    """Several 128-row tiles per user, mixed tails, alpha != 1."""
+@pytest.mark.parametrize("dtype,d,H", [(torch.bfloat16, 256, 2), (torch.float16, 96, 3)])
+def test_attention_long_users(mb, ds, dtype, d, H):
+    """Several 128-row tiles per user, mixed tails, alpha != 1; head sizes
+    128 and 32."""
     rng = np.random.default_rng(12)
     lengths = [[8, 700, 40, 20], [8, 333, 64, 20], [8, 50, 3, 180], [4, 1000, 0, 20]]
     batch = make_batch_from_lengths(lengths, rng, ts_max=86400)
-    say("attention long users", batch.T, ds)
-    res = _run_attention(mb, batch, 256, 2, torch.bfloat16, seed=5, alpha=0.7,
+    say("attention long users", batch.T, ds, dtype, d, H)
+    res = _run_attention(mb, batch, d, H, dtype, seed=5, alpha=0.7,
                          max_len=None if ds == "stored" else 0)
     for name, (got, ref) in res.items():
         err = rel_l2(got, ref)

@@ -116,6 +116,17 @@ def test_layer_small_halfprec_fwd_bwd(mb, dtype, stored_ds):
     check(res, oracle_layer(batch, res, True), dtype)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_layer_cfg1_shape_halfprec_dh32(mb, dtype):
+    """The tiny configuration's shape (d 64, two 32-wide heads) through the
+    16-bit kernels."""
+    batch, params, x = config_inputs(1)
+    R = np.random.default_rng(78).normal(0, 1, size=x.shape)
+    say("layer cfg1 shape", dtype, batch.B, batch.T)
+    res = run_layer(mb, batch, params[0], x, dtype, R=R)
+    check(res, oracle_layer(batch, res, True), dtype)
+
+
 def test_layer_odd_k_steps_three_heads_f16(mb):
     """d = 192 (three 64-wide heads): the projections take an odd number of
     64-deep K steps, and three heads use the plain head-to-workgroup map."""
