@@ -429,7 +429,8 @@ def main():
 
     P = fl.visible_pairs(batch.offsets, batch.group_ids, batch.timestamps)
     attn_flops = 12 * d * P
-    attn_ms = sum(prof.get(k, (0.0, 0))[0] for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq")) / args.steps
+    attn_ms = sum(prof.get(k, (0.0, 0))[0]
+                  for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_rest")) / args.steps
     value = attn_flops / (attn_ms / 1e3) / 1e12
     layer_flops = 12 * d * P + fl.layer_gemm_flops(T, d, backward=True)
 

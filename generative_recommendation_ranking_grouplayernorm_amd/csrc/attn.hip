@@ -730,13 +730,15 @@ __device__ __forceinline__ void silu_terms_rows_queries(const f32x16_t (&x)[2], 
 // queries and forms dS = dA * f, which it hands back through LDS; each wave
 // of the pair then accumulates half of the dQ = dS K columns, so both do
 // the same number of MFMAs.
+// One (query tile, head) of the recompute dQ; the whole workgroup calls it
+// with the same arguments.
 template <typename T, int DH>
-__global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
+__device__ __forceinline__ void dq_mfma_tile(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dQ,
     int64_t lddq, const uint16_t* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
-    const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-    int H, float kexp, float alpha, float out_scale) {
+    const int64_t* __restrict__ ts, const int2* __restrict__ tiles, int H, float kexp, float alpha,
+    float out_scale, int tile, int h) {
   constexpr int KP = AttnPitch<DH>::B128;
   constexpr int NS = DH / 16, NC = DH / 32;
   struct Smem {
@@ -755,9 +757,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   auto& Kt = sm.m.Kt;
   auto& Fx = sm.m.Fx;
   auto& Tk = sm.m.Tk;
-  int tile, h;
-  xcd_tile_head(blockIdx.x, H, tile, h);
-  if (tile >= *ntiles) return;
   const int2 te = tiles[tile];
   const int b = te.x, q0 = te.y;
   const int lo = seg[b * 5 + 0], s_end = seg[b * 5 + 2], r_end = seg[b * 5 + 3], hi = seg[b * 5 + 4];
@@ -877,6 +876,54 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
   if (ncol > 0)
     wave_store_rows<T, NCH>(sm.ep + wave * EP_FLOATS, acc, producer ? 0 : NC / 2, lane, q0 + grp * 32, hi,
                             out_scale, dQ, lddq, hc, zq, ldz);
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_mfma(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dQ,
+    int64_t lddq, const uint16_t* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
+    const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+    int H, float kexp, float alpha, float out_scale) {
+  int tile, h;
+  xcd_tile_head(blockIdx.x, H, tile, h);
+  if (tile >= *ntiles) return;
+  dq_mfma_tile<T, DH>(Q, K, V, ldqkv, dO, lddo, dQ, lddq, zq, ldz, seg, ts, tiles, H, kexp, alpha, out_scale,
+                      tile, h);
+}
+
+// After the dQ stream: the (query tile, head) items of rows whose stored dS
+// did not fit its buffer (rows longer than the declared maximum), which the
+// stream skipped.  A small grid walks all items 512 at a time, one check per
+// thread, and recomputes only the flagged ones, so that the launch costs a
+// few microseconds when no row overflows.
+template <typename T, int DH>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_overflow(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dQ,
+    int64_t lddq, const uint16_t* __restrict__ zq, int64_t ldz, const int32_t* __restrict__ seg,
+    const int64_t* __restrict__ ts, const int2* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+    int H, float kexp, float alpha, float out_scale, const int64_t* __restrict__ tprefix, int64_t ds_cap) {
+  __shared__ uint8_t flag[512];
+  const int total = *ntiles * H;
+  for (int base = blockIdx.x * 512; base < total; base += gridDim.x * 512) {
+    const int item = base + (int)threadIdx.x;
+    uint8_t f = 0;
+    if (item < total) {
+      const int b = tiles[item / H].x;
+      const int nt = (seg[b * 5 + 4] - seg[b * 5 + 0] + 127) >> 7;
+      f = tprefix[b] + (int64_t)nt * nt > ds_cap;
+    }
+    __syncthreads();  // the previous pass's flags have been read
+    flag[threadIdx.x] = f;
+    if (!__syncthreads_or(f)) continue;  // the usual case: nothing to redo
+    for (int i = 0; i < 512 && base + i < total; ++i)
+      if (flag[i]) {
+        dq_mfma_tile<T, DH>(Q, K, V, ldqkv, dO, lddo, dQ, lddq, zq, ldz, seg, ts, tiles, H, kexp, alpha,
+                            out_scale, (base + i) / H, (base + i) % H);
+        __syncthreads();  // every wave's epilogue staging read before the LDS is reused
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1170,16 +1217,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_stream(
   const int nt = (hi - lo + 127) >> 7;
   const int qt = (q0 - lo) >> 7;
   const int64_t pb = tprefix[b];
-  if (pb + (int64_t)nt * nt > ds_cap) {
-    // this row's dS did not fit the buffer (a row longer than the declared
-    // maximum): its dQ is NaN rather than garbage
-    const uint16_t nan16 = bits16<T>(__builtin_nanf(""));
-    for (int i = tid; i < 128 * DH; i += 256) {
-      const int row = q0 + i / DH;
-      if (row < hi) dQ[(int64_t)row * lddq + hc + i % DH] = nan16;
-    }
-    return;
-  }
+  // a row whose dS did not fit the buffer (longer than the declared
+  // maximum) is left to the recompute kernel launched after this one
+  if (pb + (int64_t)nt * nt > ds_cap) return;
   const uint8_t* dsq = dS + (pb * H + (int64_t)h * nt * nt + (int64_t)qt * nt) * (int64_t)DS_TILE_BYTES;
   const int q_last = min(q0 + 128, hi) - 1;
   const int kv_end = key_end_for(q_last, s_end, r_end);
@@ -1463,11 +1503,22 @@ static void bwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
                          pv.k.ntiles, a.H, kexp, a.alpha, a.scale, nullptr, (int64_t)0, (const int64_t*)nullptr);
   }
   if (a.ds) {
-    ProfScope ps("attn_bwd_dq", st);
-    hipLaunchKernelGGL((attn_bwd_dq_stream<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(256), 0, st,
-                       (const uint16_t*)a.k, a.ldqkv, (const uint8_t*)a.ds, a.ds_cap, (const int64_t*)pv.tprefix,
-                       (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg, pv.q.tiles, pv.q.ntiles,
-                       a.H, a.alpha * a.scale);
+    {
+      ProfScope ps("attn_bwd_dq", st);
+      hipLaunchKernelGGL((attn_bwd_dq_stream<T, DH>), dim3(xcd_grid(pv.q.max_tiles, a.H)), dim3(256), 0, st,
+                         (const uint16_t*)a.k, a.ldqkv, (const uint8_t*)a.ds, a.ds_cap,
+                         (const int64_t*)pv.tprefix, (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz,
+                         pv.seg, pv.q.tiles, pv.q.ntiles, a.H, a.alpha * a.scale);
+    }
+    // rows longer than the declared maximum, whose dS did not fit
+    ProfScope ps("attn_bwd_dq_rest", st);
+    const int64_t items = (int64_t)pv.q.max_tiles * a.H;
+    const int grid = (int)std::min<int64_t>(256, (items + 511) / 512);
+    if (grid > 0)
+      hipLaunchKernelGGL((attn_bwd_dq_overflow<T, DH>), dim3(grid), dim3(512), 0, st, (const uint16_t*)a.q,
+                         (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv, (const uint16_t*)a.d_o, a.lddo,
+                         (uint16_t*)a.dq, a.lddqkv, (const uint16_t*)a.zq, a.ldz, pv.seg, a.ts, pv.q.tiles,
+                         pv.q.ntiles, a.H, kexp, a.alpha, a.alpha * a.scale, (const int64_t*)pv.tprefix, a.ds_cap);
     return;
   }
   ProfScope ps("attn_bwd_dq", st);

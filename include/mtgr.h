@@ -311,8 +311,9 @@ int mtgr_hstu_attn_fwd_noalloc(const void* q, const void* k, const void* v, int6
  *                  mtgr_workspace_size); in bf16/f16 with max_len > 0 the
  *                  workspace must hold MTGR_OP_ATTN_BWD bytes for that
  *                  max_len, else MTGR_ERR_WORKSPACE_TOO_SMALL.  A row longer
- *                  than max_len whose dS blocks then do not fit gets NaN in
- *                  its dq rows (never an out-of-range access).
+ *                  than max_len whose dS blocks then do not fit has its dq
+ *                  recomputed from the scores instead (slower, same result;
+ *                  never an out-of-range access).
  *   workspace    : MTGR_OP_ATTN_BWD bytes for the same B, T, max_len, H
  */
 int mtgr_hstu_attn_bwd(const void* q, const void* k, const void* v, int64_t ld_qkv,
