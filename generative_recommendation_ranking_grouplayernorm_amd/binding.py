@@ -50,7 +50,7 @@ class LayerParams(ctypes.Structure):
 
 class LayerSaved(ctypes.Structure):
     _fields_ = [("xhat", ctypes.c_void_p), ("mean1", ctypes.c_void_p), ("rstd1", ctypes.c_void_p),
-                ("z", ctypes.c_void_p), ("uqkv", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("zgrad", ctypes.c_void_p), ("uqkv", ctypes.c_void_p), ("o", ctypes.c_void_p),
                 ("mean2", ctypes.c_void_p), ("rstd2", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
@@ -253,14 +253,14 @@ def make_params(p: Dict[str, torch.Tensor], H: int, eps: float = 1e-5, alpha: fl
 
 
 def make_saved(s: Dict[str, torch.Tensor]) -> LayerSaved:
-    return LayerSaved(*(_p(s[k]) for k in ("xhat", "mean1", "rstd1", "z", "uqkv", "o", "mean2", "rstd2", "y")))
+    return LayerSaved(*(_p(s[k]) for k in ("xhat", "mean1", "rstd1", "zgrad", "uqkv", "o", "mean2", "rstd2", "y")))
 
 
 def alloc_saved(T: int, d: int, dtype: torch.dtype, device="cuda") -> Dict[str, torch.Tensor]:
     f = dict(dtype=dtype, device=device)
     s = dict(dtype=torch.float32, device=device)
     return dict(xhat=torch.empty(T, d, **f), mean1=torch.empty(T, **s), rstd1=torch.empty(T, **s),
-                z=torch.empty(T, 4 * d, **f), uqkv=torch.empty(T, 4 * d, **f), o=torch.empty(T, d, **f),
+                zgrad=torch.empty(T, 4 * d, **f), uqkv=torch.empty(T, 4 * d, **f), o=torch.empty(T, d, **f),
                 mean2=torch.empty(T, **s), rstd2=torch.empty(T, **s), y=torch.empty(T, d, **f))
 
 

@@ -485,7 +485,9 @@ static int layer_fwd_body(const mtgr_layer_params* p, const void* x_in, void* x_
   GemmEpiArgs ep = {};
   ep.kind = EPI_BIAS_SILU;
   ep.C = uqkv; ep.ldc = 4 * d; ep.bias = p->b_uqkv;
-  ep.Z = saved ? saved->z : nullptr; ep.ldz = 4 * d;
+  // the backward needs only SiLU'(z), which the epilogue forms from the
+  // sigmoid it computes anyway
+  ep.Z = saved ? saved->zgrad : nullptr; ep.ldz = 4 * d; ep.zgrad = 1;
   {
     ProfScope ps("gemm_uqkv_silu", st);
     r = launch_gemm(dt, xhat, d, true, p->W_uqkv, d, true, (int)T, 4 * d, d, ep, 1, st);
@@ -541,7 +543,7 @@ int mtgr_hstu_layer_fwd(const mtgr_layer_params* p, const void* x_in, void* x_ou
   if (T > 0 && (!x_in || !x_out)) return MTGR_ERR_INVALID_ARG;
   if (x_in == x_out && T > 0) return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(x_in, d, dt) || !vec_ok(x_out, d, dt)) return MTGR_ERR_INVALID_ARG;
-  if (saved && (!saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->z || !saved->uqkv || !saved->o ||
+  if (saved && (!saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->zgrad || !saved->uqkv || !saved->o ||
                 !saved->mean2 || !saved->rstd2 || !saved->y))
     return MTGR_ERR_INVALID_ARG;
   if (ws_bytes < layer_fwd_ws(B, T, d, p->H, dt) || (T > 0 && !workspace)) return MTGR_ERR_WORKSPACE_TOO_SMALL;
@@ -689,7 +691,7 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
   if (!grads->W_uqkv || !grads->gamma1 || !grads->beta1 || !grads->gamma2 || !grads->beta2 || !grads->W_o)
     return MTGR_ERR_INVALID_ARG;
   const int d = p->d;
-  if (T > 0 && (!x_in || !dx_out || !dx_in || !saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->z ||
+  if (T > 0 && (!x_in || !dx_out || !dx_in || !saved->xhat || !saved->mean1 || !saved->rstd1 || !saved->zgrad ||
                 !saved->uqkv || !saved->o || !saved->mean2 || !saved->rstd2 || !saved->y))
     return MTGR_ERR_INVALID_ARG;
   if (!vec_ok(x_in, d, dt) || !vec_ok(dx_out, d, dt) || !vec_ok(dx_in, d, dt)) return MTGR_ERR_INVALID_ARG;
@@ -734,7 +736,7 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
   // gradients w.r.t. SiLU(z) go to the caller's buffer when asked for,
   // otherwise straight into dz with SiLU' applied by the producers
   void* dact = want_dact ? extras->d_uqkv : ws_dz;
-  const char* zb = (const char*)saved->z;
+  const char* zb = (const char*)saved->zgrad;
   const char* ub = (const char*)saved->uqkv;
   char* db = (char*)dact;
   // a6 backward: dy = dx_out W_o ; dW_o = dx_out^T y ; db_o = colsum(dx_out)
@@ -779,7 +781,7 @@ int mtgr_hstu_layer_bwd(const mtgr_layer_params* p, const void* x_in, const mtgr
   if (want_dact) {
     if (hipMemcpyAsync(ws_dz, dact, (size_t)T * 4 * d * e, hipMemcpyDeviceToDevice, st) != hipSuccess)
       return MTGR_ERR_HIP;
-    r = launch_silu_grad_mul(dt, ws_dz, 4 * d, saved->z, 4 * d, T, 4 * d, st);
+    r = launch_silu_grad_mul(dt, ws_dz, 4 * d, saved->zgrad, 4 * d, T, 4 * d, st);
     if (r) return r;
   }
   // a3 backward: dxhat = dz W_uqkv ; dW_uqkv = dz^T xhat ; db_uqkv = colsum(dz)

@@ -318,7 +318,8 @@ __device__ __forceinline__ op8 vt_operand(const uint16_t* s, int u, int col0, in
 // ---------------------------------------------------------------------------
 // acc[b] holds column 32 (cb0 + b) + l32 (relative to col0) of rows
 // r0 + 8 (j >> 2) + 4 g + (j & 3).  out[row, col] = acc * scale, times
-// SiLU'(z[row, col]) when z is given; rows at or beyond rlim are not written.
+// z[row, col] (the SiLU derivative at the projection's pre-activation) when
+// z is given; rows at or beyond rlim are not written.
 // Two column blocks at a time pass through a wave-private LDS stage of
 // 32 x 64 floats, so that z is read and out written 16 bytes per lane (all
 // loads of a round issued before any is used) with the buffer range check
@@ -361,10 +362,7 @@ __device__ __forceinline__ void wave_store_rows(float* stage, const f32x16_t (&a
       if (z) {
         const uint32_t zw[4] = {zz[p].x, zz[p].y, zz[p].z, zz[p].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float zf = from_bits16<T>((uint16_t)(zw[e >> 1] >> (16 * (e & 1))));
-          v[e] *= silu_grad_from(zf, __builtin_amdgcn_rcpf(1.0f + __expf(-zf)));
-        }
+        for (int e = 0; e < 8; ++e) v[e] *= from_bits16<T>((uint16_t)(zw[e >> 1] >> (16 * (e & 1))));
       }
       u32x4_t o;
 #pragma unroll
@@ -1397,8 +1395,7 @@ __global__ void attn_bwd_dq_f32(const float* __restrict__ Q, const float* __rest
   for (int e = 0; e < DH; ++e) {
     float v = acc[e] * alpha * scale;
     if (zq) {
-      const float z = zq[i * ldz + hc + e];
-      v *= silu_grad_from(z, sigmoid_precise(z));
+      v *= zq[i * ldz + hc + e];
     }
     dQ[i * lddq + hc + e] = v;
   }
@@ -1442,9 +1439,8 @@ __global__ void attn_bwd_dkdv_f32(const float* __restrict__ Q, const float* __re
   for (int e = 0; e < DH; ++e) {
     float a = ak[e] * alpha * scale, bv = av[e] * scale;
     if (zk) {
-      const float z1 = zk[i * ldz + hc + e], z2 = zv[i * ldz + hc + e];
-      a *= silu_grad_from(z1, sigmoid_precise(z1));
-      bv *= silu_grad_from(z2, sigmoid_precise(z2));
+      a *= zk[i * ldz + hc + e];
+      bv *= zv[i * ldz + hc + e];
     }
     dK[i * lddkv + hc + e] = a;
     dV[i * lddkv + hc + e] = bv;

@@ -15,9 +15,6 @@
 
 namespace mtgr {
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-// 16-bit outputs: the hardware reciprocal (1 ulp) is far below the output rounding
-__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Staged epilogue of 8 consecutive outputs (m, n..n+7), N % 8 == 0.
 constexpr int G_EPI_PITCH = 72;  // floats per staged row
@@ -56,13 +53,24 @@ __device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, fl
     for (int e = 0; e < 8; ++e) v[e] += bb[e];
   }
   if (EPI == EPI_BIAS_SILU) {
-    float z[8];
-    // round z to T first so forward and backward see the same pre-activation
+    float z[8], sg[8];
+    // z rounded to T first, so that SiLU and its derivative are those of the
+    // value a consumer of z would see; 16-bit outputs take the hardware
+    // reciprocal (1 ulp), far below their rounding
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = to_f32(from_f32<T>(v[e]));
-    if (ep.Z) store8_t<T, NT>((T*)ep.Z + (int64_t)m * ep.ldz + n, z);
+    for (int e = 0; e < 8; ++e) {
+      z[e] = to_f32(from_f32<T>(v[e]));
+      sg[e] = __builtin_amdgcn_rcpf(1.0f + __expf(-z[e]));
+    }
+    if (ep.Z) {
+      float zo[8];
+      // SiLU'(z) = sigma + SiLU(z) (1 - sigma)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = silu_fast(z[e]);
+      for (int e = 0; e < 8; ++e) zo[e] = ep.zgrad ? __builtin_fmaf(z[e] * sg[e], 1.0f - sg[e], sg[e]) : z[e];
+      store8_t<T, NT>((T*)ep.Z + (int64_t)m * ep.ldz + n, zo);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] *= sg[e];
     store8_t<T, NT>((T*)ep.C + (int64_t)m * ep.ldc + n, z);
   } else if (EPI == EPI_BIAS_RESID) {
     const uint32_t w[4] = {rr.x, rr.y, rr.z, rr.w};
@@ -83,12 +91,12 @@ __device__ __forceinline__ void epi_apply(const GemmEpiArgs& ep, int m, int n, f
     ((T*)ep.C)[(int64_t)m * ep.ldc + n] = from_f32<T>(acc);
   } else if (EPI == EPI_BIAS_SILU) {
     float z = acc + (ep.bias ? to_f32(((const T*)ep.bias)[n]) : 0.f);
-    T zr = from_f32<T>(z);
-    if (ep.Z) ((T*)ep.Z)[(int64_t)m * ep.ldz + n] = zr;
-    // SiLU of the stored (rounded) pre-activation, so that forward and
-    // backward see the same z.
-    float zq = to_f32(zr);
-    ((T*)ep.C)[(int64_t)m * ep.ldc + n] = from_f32<T>(silu_f(zq));
+    // SiLU (and its derivative) of z rounded to T, the value a consumer of
+    // z would see
+    const float zq = to_f32(from_f32<T>(z));
+    const float sg = 1.0f / (1.0f + __expf(-zq));
+    if (ep.Z) ((T*)ep.Z)[(int64_t)m * ep.ldz + n] = from_f32<T>(ep.zgrad ? sg * (1.0f + zq * (1.0f - sg)) : zq);
+    ((T*)ep.C)[(int64_t)m * ep.ldc + n] = from_f32<T>(zq * sg);
   } else if (EPI == EPI_BIAS_RESID) {
     float r = acc + (ep.bias ? to_f32(((const T*)ep.bias)[n]) : 0.f) +
               to_f32(((const T*)ep.R)[(int64_t)m * ep.ldr + n]);

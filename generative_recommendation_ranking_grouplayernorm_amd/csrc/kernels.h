@@ -138,7 +138,7 @@ int launch_gln_fwd_part(int dt, const PartialRows& in, void* y, int64_t ldy, con
 // Only the sum: xs = x (in.xs must be set).
 int launch_partial_reduce(int dt, const PartialRows& in, int64_t T, int d, hipStream_t stream);
 // Backward.  Plain: dx = GLN'(dy) [+ resid].  Gate (u != NULL): the forward
-// was y = GLN(x) * u, so du = dy * GLN(x) [* SiLU'(zu) if zu != NULL] and
+// was y = GLN(x) * u, so du = dy * GLN(x) [* gu if gu != NULL, gu = SiLU'(zu)] and
 // dx = GLN'(dy * u).  dgamma/dbeta fp32 [G, d] overwritten.
 size_t gln_bwd_workspace_bytes(int64_t T, int d, int G);
 int launch_gln_bwd(int dt, const void* dy, int64_t lddy, const void* x, int64_t ldx, const float* mean,
@@ -167,6 +167,7 @@ struct GemmEpiArgs {
   const void* bias;  // [N] or NULL
   void* Z;           // pre-activation out (EPI_BIAS_SILU) or NULL
   int64_t ldz;
+  int zgrad;         // 1: Z receives SiLU'(z) instead of z
   const void* R;     // residual (EPI_BIAS_RESID)
   int64_t ldr;
   int64_t plane;     // elements between split planes (EPI_F32_PLANES)
@@ -192,8 +193,8 @@ struct AttnArgs {
   void* o; int64_t ldo;
   const void* d_o; int64_t lddo;
   void* dq; void* dk; void* dv; int64_t lddqkv;
-  // optional pre-activations: when set, the backward writes dq * SiLU'(zq)
-  // (likewise dk, dv) with zq/zk/zv at row stride ldz.
+  // optional SiLU derivatives at the pre-activations: when set, the
+  // backward writes dq * zq (likewise dk, dv), zq/zk/zv at row stride ldz.
   const void* zq; const void* zk; const void* zv; int64_t ldz;
   const int64_t* ts;
   int B; int64_t T; int H; int dh;

@@ -270,17 +270,6 @@ int launch_gln_fwd_part(int dt, const PartialRows& in, void* y, int64_t ldy, con
 constexpr int GLN_BWD_MAX_BLOCKS = 2048;
 constexpr int GLN_BWD_MIN_ROWS = 16;
 
-__device__ __forceinline__ float silu_grad_f(float z) {
-  float s = 1.0f / (1.0f + __expf(-z));
-  return s * (1.0f + z * (1.0f - s));
-}
-// 16-bit storage: the hardware reciprocal (1 ulp) is far below the output rounding
-template <typename T>
-__device__ __forceinline__ float silu_grad_t(float z) {
-  if constexpr (sizeof(T) == 4) return silu_grad_f(z);
-  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-  return s * (1.0f + z * (1.0f - s));
-}
 
 // Per block: partial[blockIdx.x][0][G][d] = dgamma part, [1][G][d] = dbeta part.
 // Each wave walks 16 consecutive rows; the group rarely changes along them,
@@ -385,10 +374,10 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
 #pragma unroll
           for (int k = 0; k < 8; ++k) duv[k] = dyv[k] * (n[i][k] * ga[k] + be[k]);
           if (zu) {
-            float zz[8];
-            R.zu[i].get(zz);
+            float gg[8];  // SiLU'(z_u)
+            R.zu[i].get(gg);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) duv[k] *= silu_grad_t<T>(zz[k]);
+            for (int k = 0; k < 8; ++k) duv[k] *= gg[k];
           }
           store8(du + row * lddu + c, duv);
 #pragma unroll
@@ -603,16 +592,16 @@ int launch_colsum(int dt, const void* X, int64_t ldx, int64_t T_, int N, float* 
   return MTGR_OK;
 }
 
+// x *= g elementwise (g: the saved SiLU derivative)
 template <typename T>
-__global__ void silu_grad_mul_kernel(T* x, int64_t ldx, const T* __restrict__ z, int64_t ldz,
+__global__ void silu_grad_mul_kernel(T* x, int64_t ldx, const T* __restrict__ g, int64_t ldg,
                                      int64_t nrows, int N) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = nrows * (int64_t)N;
   if (i >= total) return;
   const int64_t r = i / N;
   const int c = (int)(i - r * N);
-  const float zz = to_f32(z[r * ldz + c]);
-  x[r * ldx + c] = from_f32<T>(to_f32(x[r * ldx + c]) * silu_grad_f(zz));
+  x[r * ldx + c] = from_f32<T>(to_f32(x[r * ldx + c]) * to_f32(g[r * ldg + c]));
 }
 
 int launch_silu_grad_mul(int dt, void* x, int64_t ldx, const void* z, int64_t ldz, int64_t T_, int N,

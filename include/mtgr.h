@@ -346,7 +346,7 @@ typedef struct {
   void* xhat;    /* [T, d]  output of the input Group LayerNorm */
   float* mean1;  /* [T] */
   float* rstd1;  /* [T] */
-  void* z;       /* [T, 4d] pre-SiLU projection */
+  void* zgrad;   /* [T, 4d] SiLU'(z), z = xhat W^T + b the pre-SiLU projection */
   void* uqkv;    /* [T, 4d] SiLU(z): U | Q | K | V */
   void* o;       /* [T, d]  attention output */
   float* mean2;  /* [T] */

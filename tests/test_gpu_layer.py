@@ -69,7 +69,8 @@ def run_layer(mb, batch, p, x, dtype, R=None, scale=None, extras=True, stored_ds
 def oracle_layer(batch, res, with_bwd):
     q = res["_q"]
     ref, sv = orc.layer_fwd(q, res["_x"], batch.offsets, batch.group_ids, batch.timestamps, 1.0, res["_scale"])
-    want = {"x_out": ref, "xhat": sv["xhat"], "z": sv["z"], "uqkv": sv["uqkv"], "o": sv["o"], "y": sv["y"],
+    want = {"x_out": ref, "xhat": sv["xhat"], "zgrad": orc.silu_grad(sv["z"]), "uqkv": sv["uqkv"], "o": sv["o"],
+            "y": sv["y"],
             "mean1": sv["mean1"], "rstd1": sv["rstd1"], "mean2": sv["mean2"], "rstd2": sv["rstd2"]}
     if with_bwd:
         dx, gr = orc.layer_bwd(q, res["_x"], sv, res["_R"], batch.offsets, batch.group_ids, batch.timestamps, 1.0,
