@@ -412,15 +412,20 @@ __global__ __launch_bounds__(256) void gln_bwd_kernel(
       }
     }
   };
-  // two row buffers used in turn, so that no loaded register is ever copied
-  Raw ra, rb;
+  // three row buffers used in turn (no loaded register is ever copied): the
+  // rows two and three ahead are in flight while a row is computed
+  Raw ra, rb, rc;
   if (r0 < r1) load_raw(ra, r0);
-  for (int64_t row = r0; row < r1; row += 2) {
-    if (row + 1 < r1) load_raw(rb, row + 1);
+  if (r0 + 1 < r1) load_raw(rb, r0 + 1);
+  for (int64_t row = r0; row < r1; row += 3) {
+    if (row + 2 < r1) load_raw(rc, row + 2);
     process(ra, row);
     if (row + 1 >= r1) break;
-    if (row + 2 < r1) load_raw(ra, row + 2);
+    if (row + 3 < r1) load_raw(ra, row + 3);
     process(rb, row + 1);
+    if (row + 2 >= r1) break;
+    if (row + 4 < r1) load_raw(rb, row + 4);
+    process(rc, row + 2);
   }
   if (cur >= 0) flush();
   __syncthreads();
