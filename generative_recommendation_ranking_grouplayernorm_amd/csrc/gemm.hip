@@ -5,8 +5,8 @@
 //
 // bf16 / f16: 256x256 output tile per 512-thread workgroup, 8 waves in 2x4,
 // each wave 128x64 = 4x2 MFMA 32x32x16 tiles (128x128 tiles of 4 waves for
-// short batches); K staged through LDS 64 deep, double-buffered, one barrier
-// per K step.  Operands stored K-contiguous are
+// short batches); K staged through LDS 64 deep by buffer-to-LDS loads,
+// double-buffered, one barrier per K step.  Operands stored K-contiguous are
 // read with 16-byte LDS loads; operands stored M/N-contiguous (the transposed
 // products of the backward) are read with gfx950's LDS transpose load, so no
 // operand is ever transposed in memory.
@@ -111,9 +111,13 @@ __device__ __forceinline__ void epi_apply(const GemmEpiArgs& ep, int m, int n, f
 // ---------------------------------------------------------------------------
 // MFMA kernel.  Output tile BM x BN per workgroup of WAVES_M x WAVES_N waves,
 // each wave TM x TN MFMA 32x32x16 tiles; K staged 64 deep through LDS,
-// double-buffered with register prefetch, one barrier per K step.  Global
-// reads are buffer loads whose range check zero-fills rows past the matrix
-// edge; advancing a K step changes only scalar registers.
+// double-buffered, one barrier per K step.  Tiles go from memory straight to
+// LDS (buffer loads with the LDS destination), so loading the next K step
+// costs the waves no registers and no LDS write instructions: the LDS writes
+// happen while the MFMAs of the current step run (writing the tiles from
+// registers at the end of each step took 20-30% of the products' time).  The
+// range check of the buffer loads zero-fills rows past the matrix edge;
+// advancing a K step changes only scalar registers.
 //   large: 256 x 256, 8 waves as 2 x 4, 128 x 64 per wave (every batch of
 //          more than a few thousand rows);
 //   small: 128 x 128, 4 waves as 2 x 2, 64 x 64 per wave, two workgroups per
@@ -149,7 +153,8 @@ using GemmSmall = GemmCfg<128, 128, 2, 2, 2, false>;
 // its quarter-waves (4 rows x 2 chunks) 8 distinct positions modulo 8.  With
 // padded pitches (72 / ROWS + 16 elements) both kinds of reads collided, the
 // transposed ones on most accesses.  The allocation keeps the padded size,
-// which the epilogue's fp32 staging needs.
+// which the epilogue's fp32 staging needs (64 rows x 72 floats per wave,
+// NW / 4 waves per tile object).
 template <int ROWS>
 struct GTile {
   static constexpr int KC_ELEMS = ROWS * G_KC_PITCH;
@@ -172,25 +177,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const uint16_t* P, i
   return make_rsrc(P + (int64_t)k0 * ld + r0, (int)((int64_t)min(kend - k0, G_BK) * ld * 2 - (int64_t)r0 * 2));
 }
 
-// 16-byte chunk c of a K step: K-contiguous, 8 chunks per row of 64;
-// M/N-contiguous, ROWS / 8 chunks per K row.
+// Tiles reach LDS by buffer-to-LDS loads: one wave instruction fills 1 KB of
+// LDS, lane l's 16 bytes landing at byte 16 l, so the tile's 1 KB block j
+// (8 K-contiguous rows, or 1024 / (2 ROWS) M/N-contiguous K rows) is one
+// instruction, and the swizzle is applied to the global address each lane
+// reads: the lane at LDS chunk position p of row r fetches the row's chunk
+// p ^ swz(r).  The byte offset returned is relative to the step's buffer
+// resource (gemm_rsrc).
 template <bool KC, int ROWS>
-__device__ __forceinline__ int gemm_voff(int64_t ld, int c) {
-  constexpr int CPR = KC ? 8 : ROWS / 8;
-  return ((c / CPR) * (int)ld + (c % CPR) * 8) * 2;
+__device__ __forceinline__ int gemm_dma_voff(int64_t ld, int j, int lane) {
+  constexpr int CPR = KC ? 8 : ROWS / 8;  // 16-byte chunks per LDS row
+  constexpr int RPB = 64 / CPR;           // LDS rows per 1 KB block
+  const int row = j * RPB + lane / CPR, p = lane % CPR;
+  const int ch = p ^ (KC ? kc_swz(row) : mn_swz(row));
+  return (row * (int)ld + ch * 8) * 2;
 }
 
-template <bool KC, int ROWS>
-__device__ __forceinline__ void gemm_swrite(uint16_t* s, int c, uint4 v) {
-  if (KC) {
-    const int row = c / 8, ch = c % 8;
-    *(uint4*)(s + row * G_BK + 8 * (ch ^ kc_swz(row))) = v;
-  } else {
-    constexpr int CPR = ROWS / 8;
-    const int row = c / CPR, ch = c % CPR;
-    *(uint4*)(s + row * ROWS + 8 * (ch ^ mn_swz(row))) = v;
-  }
+__device__ __forceinline__ void gemm_dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds_block, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, 0, 0, 0);
 }
+
+// Wait until this wave's buffer-to-LDS loads have written LDS (vmcnt = 0;
+// gfx9 encoding with the other counters at their maxima).
+__device__ __forceinline__ void gemm_wait_dma() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
 
 // MFMA operand for 32 rows starting at r0 (within the tile), k-step ks.
 template <bool KC, int ROWS>
@@ -245,17 +254,25 @@ template <typename T, bool AK, bool BKC, int EPI, typename C>
 __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb, int M, int N, int K,
     int k_per_split, int MT, int NT, int R, GemmEpiArgs ep) {
-  constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, NTH = C::THREADS;
+  constexpr int BM = C::BM, BN = C::BN, TM = C::TM, TN = C::TN, NTH = C::THREADS, NW = NTH / 64;
   constexpr int A_ELEMS = GTile<BM>::ELEMS, B_ELEMS = GTile<BN>::ELEMS;
-  constexpr int A_LOADS = BM * G_BK / 8 / NTH, B_LOADS = BN * G_BK / 8 / NTH;
-  static_assert(A_LOADS * NTH * 8 == BM * G_BK && B_LOADS * NTH * 8 == BN * G_BK, "load split");
-  static_assert(TN == 2 && TM % 2 == 0, "epilogue stages 64 x 64 blocks");
-  static_assert((NTH / 64) * 64 * G_EPI_PITCH * 4 <= 2 * (A_ELEMS + B_ELEMS) * 2, "epilogue staging fits");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][A_ELEMS + B_ELEMS];
+  // 1 KB buffer-to-LDS blocks per wave and K step
+  constexpr int A_LOADS = BM * G_BK * 2 / 1024 / NW, B_LOADS = BN * G_BK * 2 / 1024 / NW;
+  static_assert(A_LOADS * NW * 1024 == BM * G_BK * 2 && B_LOADS * NW * 1024 == BN * G_BK * 2, "load split");
+  static_assert(TN % 2 == 0 && TM % 2 == 0, "epilogue stages 64 x 64 blocks");
+  static_assert(A_ELEMS == B_ELEMS && (NW / 4) * 64 * G_EPI_PITCH * 4 <= A_ELEMS * 2, "epilogue staging fits");
+  // The operand tiles of the two K-step buffers are separate LDS objects, so
+  // that the compiler can tell the reads of one buffer from the loads in
+  // flight into the other and need not wait for those loads before a read.
+  __shared__ __attribute__((aligned(16))) uint16_t sa0[A_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sb0[B_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sa1[A_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sb1[B_ELEMS];
   int rr, nt;
   if (!gemm_tile_of(blockIdx.x, NT, R, rr, nt)) return;
   const int mt = rr % MT, split = rr / MT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int m0 = mt * BM, n0 = nt * BN;
   const int kbeg = split * k_per_split;
@@ -273,9 +290,9 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
 
   int va[A_LOADS], vb[B_LOADS];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) va[i] = gemm_voff<AK, BM>(lda, tid + NTH * i);
+  for (int i = 0; i < A_LOADS; ++i) va[i] = gemm_dma_voff<AK, BM>(lda, i * NW + wave, lane);
 #pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) vb[i] = gemm_voff<BKC, BN>(ldb, tid + NTH * i);
+  for (int i = 0; i < B_LOADS; ++i) vb[i] = gemm_dma_voff<BKC, BN>(ldb, i * NW + wave, lane);
   auto mma = [&](const uint16_t* sa, const uint16_t* sb) {
 #pragma unroll
     for (int ks = 0; ks < G_BK / 16; ++ks) {
@@ -291,33 +308,32 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
     }
     gemm_pipeline<TM * (AK ? 1 : 2) + TN * (BKC ? 1 : 2), TM * TN>();
   };
-  auto gload_to = [&](uint4 (&ra)[A_LOADS], uint4 (&rb)[B_LOADS], int k0) {
+  // K step at k0 into one buffer (loads in flight until gemm_wait_dma)
+  auto dma = [&](uint16_t* s_a, uint16_t* s_b, int k0) {
     const __amdgpu_buffer_rsrc_t sa = gemm_rsrc<AK, BM>(A, lda, m0, M, k0, kend);
     const __amdgpu_buffer_rsrc_t sb = gemm_rsrc<BKC, BN>(B, ldb, n0, N, k0, kend);
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) ra[i] = buf_load16(sa, va[i]);
+    for (int i = 0; i < A_LOADS; ++i) gemm_dma16(sa, s_a + (i * NW + wave) * 512, va[i]);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) rb[i] = buf_load16(sb, vb[i]);
+    for (int i = 0; i < B_LOADS; ++i) gemm_dma16(sb, s_b + (i * NW + wave) * 512, vb[i]);
   };
-  auto swrite_from = [&](const uint4 (&ra)[A_LOADS], const uint4 (&rb)[B_LOADS], int buf) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) gemm_swrite<AK, BM>(smem[buf], tid + NTH * i, ra[i]);
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) gemm_swrite<BKC, BN>(smem[buf] + A_ELEMS, tid + NTH * i, rb[i]);
-  };
-  uint4 ra[A_LOADS], rb[B_LOADS];
-  if (nk > 0) {
-    gload_to(ra, rb, kbeg);
-    swrite_from(ra, rb, 0);
-  }
+  // Step it computes from one buffer while step it + 1 loads into the other
+  // (freed by the barrier that ended step it - 1); the loop is unrolled by
+  // two so that each half names its buffers statically.
+  if (nk > 0) dma(sa0, sb0, kbeg);
+  gemm_wait_dma();
   __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < nk;
-    if (more) gload_to(ra, rb, kbeg + (it + 1) * G_BK);
-    mma(smem[buf], smem[buf] + A_ELEMS);
-    if (more) swrite_from(ra, rb, buf ^ 1);
+  for (int it = 0; it < nk; it += 2) {
+    if (it + 1 < nk) dma(sa1, sb1, kbeg + (it + 1) * G_BK);
+    mma(sa0, sb0);
+    gemm_wait_dma();
     __syncthreads();
+    if (it + 1 < nk) {
+      if (it + 2 < nk) dma(sa0, sb0, kbeg + (it + 2) * G_BK);
+      mma(sa1, sb1);
+      gemm_wait_dma();
+      __syncthreads();
+    }
   }
   if constexpr (EPI == EPI_F32_STORE || EPI == EPI_F32_ATOMIC || EPI == EPI_F32_PLANES) {
     float* planeC = (float*)ep.C + (EPI == EPI_F32_PLANES ? (int64_t)split * ep.plane : 0);
@@ -340,45 +356,55 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
     // and residual values a lane needs are loaded before any store: the
     // compiler cannot move a load past a store that may alias it, so loads
     // inside the store loop would each wait a full memory round trip.
-    float* st = (float*)&smem[0][0] + wave * (64 * G_EPI_PITCH);
+    const int sq = wave / (NW / 4);
+    uint16_t* const sbase = sq == 0 ? sa0 : sq == 1 ? sb0 : sq == 2 ? sa1 : sb1;
+    float* st = (float*)sbase + (wave % (NW / 4)) * (64 * G_EPI_PITCH);
     const int wr0 = m0 + wm * (TM * 32), wc0 = n0 + wn * (TN * 32);
     const int cc = (lane & 7) * 8;
-    const int n = wc0 + cc;
-    float bb[8];
+    // 64-column blocks of the wave's tile
+    float bb[TN / 2][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bb[e] = 0.f;
-    if ((EPI == EPI_BIAS_SILU || EPI == EPI_BIAS_RESID) && ep.bias && n < N) load8_t<T>((const T*)ep.bias + n, bb);
+    for (int cb = 0; cb < TN / 2; ++cb) {
+      const int n = wc0 + cb * 64 + cc;
 #pragma unroll
-    for (int half = 0; half < TM / 2; ++half) {
-      uint4 rr[8];
+      for (int e = 0; e < 8; ++e) bb[cb][e] = 0.f;
+      if ((EPI == EPI_BIAS_SILU || EPI == EPI_BIAS_RESID) && ep.bias && n < N) load8_t<T>((const T*)ep.bias + n, bb[cb]);
+    }
 #pragma unroll
-      for (int pass = 0; pass < 8; ++pass) {
-        rr[pass] = make_uint4(0, 0, 0, 0);
-        if (EPI == EPI_BIAS_RESID) {
-          const int m = wr0 + half * 64 + pass * 8 + (lane >> 3);
-          if (m < M && n < N) rr[pass] = *(const uint4*)((const T*)ep.R + (int64_t)m * ep.ldr + n);
-        }
-      }
+    for (int cb = 0; cb < TN / 2; ++cb) {
+      const int n = wc0 + cb * 64 + cc;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int half = 0; half < TM / 2; ++half) {
+        uint4 rr[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int r = tt * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-            st[r * G_EPI_PITCH + u * 32 + (lane & 31)] = acc[2 * half + tt][u][j];
+        for (int pass = 0; pass < 8; ++pass) {
+          rr[pass] = make_uint4(0, 0, 0, 0);
+          if (EPI == EPI_BIAS_RESID) {
+            const int m = wr0 + half * 64 + pass * 8 + (lane >> 3);
+            if (m < M && n < N) rr[pass] = *(const uint4*)((const T*)ep.R + (int64_t)m * ep.ldr + n);
           }
-      // lane -> 8 consecutive columns of one row; 8 rows per pass
+        }
 #pragma unroll
-      for (int pass = 0; pass < 8; ++pass) {
-        const int r = pass * 8 + (lane >> 3);
-        const int m = wr0 + half * 64 + r;
-        if (m < M && n < N) {
-          float v[8];
-          const float4 a = *(const float4*)&st[r * G_EPI_PITCH + cc];
-          const float4 b = *(const float4*)&st[r * G_EPI_PITCH + cc + 4];
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-          epi_row8<T, EPI, C::STREAM_OUT>(ep, m, n, v, bb, rr[pass]);
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int r = tt * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+              st[r * G_EPI_PITCH + u * 32 + (lane & 31)] = acc[2 * half + tt][2 * cb + u][j];
+            }
+        // lane -> 8 consecutive columns of one row; 8 rows per pass
+#pragma unroll
+        for (int pass = 0; pass < 8; ++pass) {
+          const int r = pass * 8 + (lane >> 3);
+          const int m = wr0 + half * 64 + r;
+          if (m < M && n < N) {
+            float v[8];
+            const float4 a = *(const float4*)&st[r * G_EPI_PITCH + cc];
+            const float4 b = *(const float4*)&st[r * G_EPI_PITCH + cc + 4];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            epi_row8<T, EPI, C::STREAM_OUT>(ep, m, n, v, bb[cb], rr[pass]);
+          }
         }
       }
     }
