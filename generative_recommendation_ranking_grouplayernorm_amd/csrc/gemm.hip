@@ -54,17 +54,20 @@ __device__ __forceinline__ void epi_row8(const GemmEpiArgs& ep, int m, int n, fl
   }
   if (EPI == EPI_BIAS_SILU) {
     float z[8], sg[8];
-    // z rounded to T first, so that SiLU and its derivative are those of the
-    // value a consumer of z would see; 16-bit outputs take the hardware
-    // reciprocal (1 ulp), far below their rounding
+    // z rounded to T first (two values per conversion), so that SiLU and its
+    // derivative are those of the value a consumer of z would see; 16-bit
+    // outputs take the hardware reciprocal (1 ulp), far below their rounding
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      z[e] = to_f32(from_f32<T>(v[e]));
-      sg[e] = __builtin_amdgcn_rcpf(1.0f + __expf(-z[e]));
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t w = pack2<T>(v[e], v[e + 1]);
+      z[e] = from_bits16<T>((uint16_t)(w & 0xffff));
+      z[e + 1] = from_bits16<T>((uint16_t)(w >> 16));
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sg[e] = __builtin_amdgcn_rcpf(1.0f + __expf(-z[e]));
     if (ep.Z) {
       float zo[8];
-      // SiLU'(z) = sigma + SiLU(z) (1 - sigma)
+      // z itself, or SiLU'(z) = sigma + SiLU(z) (1 - sigma)
 #pragma unroll
       for (int e = 0; e < 8; ++e) zo[e] = ep.zgrad ? __builtin_fmaf(z[e] * sg[e], 1.0f - sg[e], sg[e]) : z[e];
       store8_t<T, NT>((T*)ep.Z + (int64_t)m * ep.ldz + n, zo);

@@ -154,7 +154,7 @@ int launch_gln_bwd(int dt, const void* dy, int64_t lddy, const void* x, int64_t 
 //   b_kcontig: B(n,k) = B[n*ldb + k], else B[k*ldb + n]
 enum GemmEpi {
   EPI_STORE = 0,       // C = acc                                  (dtype dt)
-  EPI_BIAS_SILU = 1,   // z = acc + bias; Z = z (if given); C = SiLU(z)
+  EPI_BIAS_SILU = 1,   // z = acc + bias; Z = z or SiLU'(z) (if given); C = SiLU(z)
   EPI_BIAS_RESID = 2,  // C = acc + bias + R
   EPI_F32_STORE = 3,   // Cf = acc (fp32)
   EPI_F32_ATOMIC = 4,  // Cf += acc (fp32, for split-K)
