@@ -946,13 +946,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     int H, float kexp, float alpha, float scale, uint8_t* __restrict__ dS, int64_t ds_cap,
     const int64_t* __restrict__ tprefix) {
   constexpr int NS = DH / 16, NC = DH / 32;
-  // three stage buffers: the S side works on stage i while the dA side works
-  // on stage i - 1 and stage i + 1 is being written
+  // Stage buffers: in iteration it the S side works on stage it, the dA side
+  // on stage it - 1 (dA, dS) and on stage it - 2 (its dK product, which
+  // reads that stage's Q rows), while stage it + 1 is being written.  So Q
+  // rows (and their timestamps) of stage j live in buffer j % 4, dO rows in
+  // buffer j % 3.
   struct Smem {
-    uint16_t Qs[3][QuadRows<DH>::SIZE];
+    uint16_t Qs[4][QuadRows<DH>::SIZE];
     uint16_t Ds[3][QuadRows<DH>::SIZE];
     uint32_t Fx[2][4][32 * 16 * 2];  // per stage parity and group: 2 x 16 x 32 lanes
-    int64_t Tq[3][KV_BQ];            // query timestamps of the stage
+    int64_t Tq[4][KV_BQ];            // query timestamps of the stage
   };
   __shared__ __attribute__((aligned(16))) union {
     Smem m;
@@ -1040,14 +1043,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   __syncthreads();
   TrAddr<DH> tra;
   tra.init(lane);
-  // Iteration it (0..nqt): the S side takes stage it (S, P, f into
-  // Fx[it % 2], then dV += P^T dO), the dA side stage it - 1 (dA, dS = dA f
-  // with the f written one iteration earlier, then dK += dS^T Q), so that
-  // one wave's vector work runs beside its partner's MFMAs; one barrier per
-  // iteration.  Stage j lives in buffer j % 3: while stages it and it - 1 are
-  // read, both sides write their halves of stage it + 1 (Q rows, dO rows) to
-  // the third buffer.  Each side runs a loop of its own, so that neither
-  // carries the other's registers; both pass nqt + 1 barriers.
+  // Iteration it (0..nqt + 1): the S side takes stage it (S, P, f into
+  // Fx[it % 2], then dV += P^T dO); the dA side first finishes stage it - 2
+  // (dK += dS^T Q with the dS it formed one iteration earlier), then forms
+  // dA and dS = dA f for stage it - 1 (with the f written one iteration
+  // earlier).  Each SIMD then runs one wave's MFMAs beside the other wave's
+  // vector work in every phase: S products beside the dK product, the SiLU
+  // terms beside dA, dV beside dS.  One barrier per iteration; both sides
+  // write their halves of stage it + 1 (Q rows, dO rows).  Each side runs a
+  // loop of its own, so that neither carries the other's registers; both
+  // pass nqt + 2 barriers after the first.
   //
   // A second use of the loaded values, under a condition that never holds
   // (the stage row is never negative) but that the compiler cannot fold,
@@ -1098,31 +1103,34 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     // registers to itself
     auto run = [&](auto masked) {
       for (int it = 0; it < nqt; ++it) {
-        const int buf = it % 3, nbuf = (it + 1) % 3, q0 = qlo + it * KV_BQ;
+        const int qb = it & 3, nqb = (it + 1) & 3, q0 = qlo + it * KV_BQ;
         gload(q0 + KV_BQ);  // past the query range: zeros, never used
-        keep_loads_early(it, nbuf);
+        keep_loads_early(it, nqb);
         f32x16_t x[2];
-        phase1(Qs[buf], x);
+        phase1(Qs[qb], x);
         op8 w[4];
         silu_terms_rows_queries<T, decltype(masked)::value>(x, w, Fx[it & 1][grp], lane, kexp, alpha, q0, kj, g,
-                                                             s_end, r_end, Tq[buf], tk);
-        phase2(w, Ds[buf]);
-        swrite(nbuf);
+                                                             s_end, r_end, Tq[qb], tk);
+        phase2(w, Ds[it % 3]);
+        swrite(nqb);
         __syncthreads();
       }
     };
     if (full) run(std::false_type{});
     else run(std::true_type{});
     __syncthreads();  // the dA side's last stage
+    __syncthreads();  // its last dK product
   } else {
     // iteration 0: only the dO rows of stage 1
     gload(qlo + KV_BQ);
     swrite(1);
     __syncthreads();
+    op8 wp[4];  // dS operands of the previous stage, for its dK product
     for (int it = 1; it <= nqt; ++it) {
       const int st = it - 1, buf = st % 3, nbuf = (it + 1) % 3, q0 = qlo + st * KV_BQ;
       gload(qlo + (it + 1) * KV_BQ);  // past the query range: zeros, never used
       keep_loads_early(it, nbuf);
+      if (it >= 2) phase2(wp, Qs[(st - 1) & 3]);
       f32x16_t x[2];
       phase1(Ds[buf], x);
       const uint32_t* fx = Fx[st & 1][grp];
@@ -1151,10 +1159,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, w[u].v), drs, lane * 16 + u * 1024, 0,
                                                  2 /* non-temporal */);
       }
-      phase2(w, Qs[buf]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) wp[u] = w[u];
       swrite(nbuf);
       __syncthreads();
     }
+    if (nqt >= 1) phase2(wp, Qs[(nqt - 1) & 3]);
+    __syncthreads();  // every read of the stage tiles done before the epilogue reuses the LDS
   }
   // producer holds dV, consumer dK; both scale by alpha * c
   wave_store_rows<T, NC>(sm.ep + wave * EP_FLOATS, acc, 0, lane, k0 + grp * 32, hi, alpha * scale,
