@@ -1050,15 +1050,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   // earlier).  Each SIMD then runs one wave's MFMAs beside the other wave's
   // vector work in every phase: S products beside the dK product, the SiLU
   // terms beside dA, dV beside dS.  One barrier per iteration; both sides
-  // write their halves of stage it + 1 (Q rows, dO rows).  Each side runs a
-  // loop of its own, so that neither carries the other's registers; both
-  // pass nqt + 2 barriers after the first.
+  // write their halves of stage it + 1 (Q rows, dO rows) mid-iteration, the
+  // S side before its dV product and the dA side before its dS, rather than
+  // just before the barrier (dK/dV 0.81 -> 0.79 ms).  Each side runs a loop
+  // of its own, so that neither carries the other's registers; both pass
+  // nqt + 2 barriers after the first.
   //
   // A second use of the loaded values, under a condition that never holds
   // (the stage row is never negative) but that the compiler cannot fold,
   // keeps each iteration's loads at its top: their real use is the stage
-  // write at its end, and code sinking would otherwise move them there, a
-  // whole iteration of latency hiding lost.
+  // write later on, and code sinking would otherwise move them there, the
+  // latency hiding lost.
   auto keep_loads_early = [&](int it, int nbuf) {
     if (qlo + it * KV_BQ < 0) {
       uint32_t any = 0;
@@ -1111,8 +1113,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
         op8 w[4];
         silu_terms_rows_queries<T, decltype(masked)::value>(x, w, Fx[it & 1][grp], lane, kexp, alpha, q0, kj, g,
                                                              s_end, r_end, Tq[qb], tk);
-        phase2(w, Ds[it % 3]);
         swrite(nqb);
+        phase2(w, Ds[it % 3]);
         __syncthreads();
       }
     };
@@ -1133,6 +1135,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
       if (it >= 2) phase2(wp, Qs[(st - 1) & 3]);
       f32x16_t x[2];
       phase1(Ds[buf], x);
+      swrite(nbuf);
       const uint32_t* fx = Fx[st & 1][grp];
       float d[2][16];
 #pragma unroll
@@ -1161,7 +1164,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) wp[u] = w[u];
-      swrite(nbuf);
       __syncthreads();
     }
     if (nqt >= 1) phase2(wp, Qs[(nqt - 1) & 3]);
