@@ -351,7 +351,9 @@ __device__ __forceinline__ void wave_store_rows(float* stage, const f32x16_t (&a
     uint4 zz[NP];
     if (z) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) zz[p] = buf_load16(rz, ((p * RPP + pr) * (int)ldz + colb) * 2);
+      for (int p = 0; p < NP; ++p)  // read once: non-temporal
+        zz[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rz, ((p * RPP + pr) * (int)ldz + colb) * 2,
+                                                                                0, 2 /* non-temporal */));
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {

@@ -384,7 +384,10 @@ __global__ __launch_bounds__(C::THREADS, C::MIN_BLOCKS) void gemm_mfma_kernel(
           rr[pass] = make_uint4(0, 0, 0, 0);
           if (EPI == EPI_BIAS_RESID) {
             const int m = wr0 + half * 64 + pass * 8 + (lane >> 3);
-            if (m < M && n < N) rr[pass] = *(const uint4*)((const T*)ep.R + (int64_t)m * ep.ldr + n);
+            if (m < M && n < N) {  // read once: non-temporal
+            const u32x4_t t = __builtin_nontemporal_load((const u32x4_t*)((const T*)ep.R + (int64_t)m * ep.ldr + n));
+            rr[pass] = make_uint4(t[0], t[1], t[2], t[3]);
+          }
           }
         }
 #pragma unroll

@@ -28,6 +28,20 @@ __device__ __forceinline__ void load8_16(const H* p, float* o) {
     o[2 * i + 1] = from_bits16<H>((uint16_t)(w[i] >> 16));
   }
 }
+// Streaming (non-temporal) variant for rows read once: cached reads of them
+// push the next kernel's inputs out of the caches.
+template <typename H>
+__device__ __forceinline__ void load8_16_nt(const H* p, float* o) {
+  const u32x4_t r = __builtin_nontemporal_load((const u32x4_t*)p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = from_bits16<H>((uint16_t)(r[i] & 0xffff));
+    o[2 * i + 1] = from_bits16<H>((uint16_t)(r[i] >> 16));
+  }
+}
+__device__ __forceinline__ void load8_nt(const float* p, float* o) { load8(p, o); }
+__device__ __forceinline__ void load8_nt(const bf16_t* p, float* o) { load8_16_nt(p, o); }
+__device__ __forceinline__ void load8_nt(const f16_t* p, float* o) { load8_16_nt(p, o); }
 __device__ __forceinline__ void load8(const bf16_t* p, float* o) { load8_16(p, o); }
 __device__ __forceinline__ void load8(const f16_t* p, float* o) { load8_16(p, o); }
 
@@ -127,7 +141,7 @@ __global__ __launch_bounds__(256) void gln_fwd_kernel(
     const int c = lane * 8 + i * 512;
     if (c < d) {
       if (PART) partial_row8<T>(pr, row, c, v[i]);
-      else load8(x + row * ldx + c, v[i]);
+      else load8_nt(x + row * ldx + c, v[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += v[i][e];
     } else {
@@ -165,7 +179,7 @@ __global__ __launch_bounds__(256) void gln_fwd_kernel(
       for (int e = 0; e < 8; ++e) out[e] = (v[i][e] - mean) * rstd * ga[e] + be[e];
       if (GATE) {
         float uu[8];
-        load8(u + row * ldu + c, uu);
+        load8_nt(u + row * ldu + c, uu);
 #pragma unroll
         for (int e = 0; e < 8; ++e) out[e] *= uu[e];
       }
