@@ -669,7 +669,7 @@ __device__ __forceinline__ void silu_grad_rows_keys(const f32x16_t (&x)[2], uint
 // Tile with rows = queries qq of the stage at q0, lane = key kj:
 // P = SiLU(alpha s) / alpha packed as the A operands w of P^T dO, and
 // f = M * SiLU'(alpha s) to the exchange buffer fx as f16 pairs.
-template <typename T, bool MASKED>
+template <typename T, bool MASKED, bool A1 = false>
 __device__ __forceinline__ void silu_terms_rows_queries(const f32x16_t (&x)[2], op8 (&w)[4], uint32_t* fx, int lane,
                                                         float kexp, float alpha, int q0, int kj, int g, int s_end,
                                                         int r_end, const int64_t* tsq, int64_t tk) {
@@ -704,7 +704,8 @@ __device__ __forceinline__ void silu_terms_rows_queries(const f32x16_t (&x)[2], 
         const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sr * kexp));
         pv[h] = sr * sg;
         // SiLU'(y) = sigma + y sigma (1 - sigma), y = alpha s
-        f[h] = __builtin_fmaf(alpha * pv[h], 1.0f - sg, sg);
+        // (A1: alpha is 1 and the multiply is skipped, same bits)
+        f[h] = __builtin_fmaf(A1 ? pv[h] : alpha * pv[h], 1.0f - sg, sg);
         if (MASKED) {
           const int c = t * 32 + 8 * (j >> 2) + (j & 3);
           // bitwise throughout: a conditional form lets the compiler put the
@@ -938,7 +939,7 @@ constexpr int KV_BK = 128;    // keys per workgroup (4 groups of 32)
 constexpr int KV_BQ = 64;     // queries per LDS stage
 constexpr int F_PITCH = 64;   // f16 exchange tile: [key group][64 queries][32 keys]
 
-template <typename T, int DH, bool STORE>
+template <typename T, int DH, bool STORE, bool A1 = false>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int64_t ldqkv, const uint16_t* __restrict__ dO, int64_t lddo, uint16_t* __restrict__ dK,
@@ -1113,7 +1114,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
         f32x16_t x[2];
         phase1(Qs[qb], x);
         op8 w[4];
-        silu_terms_rows_queries<T, decltype(masked)::value>(x, w, Fx[it & 1][grp], lane, kexp, alpha, q0, kj, g,
+        silu_terms_rows_queries<T, decltype(masked)::value, A1>(x, w, Fx[it & 1][grp], lane, kexp, alpha, q0, kj, g,
                                                              s_end, r_end, Tq[qb], tk);
         swrite(nqb);
         phase2(w, Ds[it % 3]);
@@ -1499,7 +1500,16 @@ static void bwd_mfma(const AttnArgs& a, const PrepView& pv, hipStream_t st) {
   const float kexp = -a.alpha * 1.4426950408889634f;
   {
     ProfScope ps("attn_bwd_dkdv", st);
-    if (a.ds)
+    // alpha = 1 (the layer's default) saves one multiply per score of the
+    // S side's vector work, which bounds the kernel (1-2% of its time)
+    if (a.ds && a.alpha == 1.0f)
+      hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH, true, true>), dim3(xcd_grid(pv.k.max_tiles, a.H)), dim3(512), 0,
+                         st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
+                         (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv,
+                         (const uint16_t*)a.zk, (const uint16_t*)a.zv, a.ldz, pv.seg, a.ts, pv.k.tiles,
+                         pv.k.ntiles, a.H, kexp, a.alpha, a.scale, (uint8_t*)a.ds, a.ds_cap,
+                         (const int64_t*)pv.tprefix);
+    else if (a.ds)
       hipLaunchKernelGGL((attn_bwd_dkdv_mfma<T, DH, true>), dim3(xcd_grid(pv.k.max_tiles, a.H)), dim3(512), 0,
                          st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.ldqkv,
                          (const uint16_t*)a.d_o, a.lddo, (uint16_t*)a.dk, (uint16_t*)a.dv, a.lddqkv,
