@@ -1076,20 +1076,36 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   // operand reads run three k-steps ahead of the MFMAs in source order too:
   // where register pressure makes the compiler drop the scheduling hint and
   // keep source order, each MFMA would otherwise wait a full LDS round trip.
+  // element offsets of the phase-1 operand reads inside a tile, whole (row
+  // and swizzled chunk): the compiler would otherwise keep the parts apart
+  // and spend two vector instructions per read on joining them
+  int p1off[NS][2];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      p1off[s][t] = QuadRows<DH>::off(t * 32 + l32, 2 * s + g);
+      asm volatile("" : "+v"(p1off[s][t]));
+    }
+  auto p1read = [&](const uint16_t* A, int s, int t) {
+    op8 o;
+    o.v = *(const u32x4_t*)(A + p1off[s][t]);
+    return o;
+  };
   auto phase1 = [&](const uint16_t* A, f32x16_t (&x)[2]) {
     constexpr int AH = NS < 3 ? NS : 3;
     op8 ring[AH][2];
 #pragma unroll
     for (int s = 0; s < AH; ++s)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) ring[s][t] = row_operand_swz<DH>(A, t * 32, s, lane);
+      for (int t = 0; t < 2; ++t) ring[s][t] = p1read(A, s, t);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) x[t] = mfma32<T>(ring[s % AH][t], bop[s], s == 0 ? f32x16_t{} : x[t]);
       if (s + AH < NS) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) ring[s % AH][t] = row_operand_swz<DH>(A, t * 32, s + AH, lane);
+        for (int t = 0; t < 2; ++t) ring[s % AH][t] = p1read(A, s + AH, t);
       }
     }
     pipeline_lds_mfma<2 * NS, 2 * AH>();
