@@ -1076,20 +1076,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   // operand reads run three k-steps ahead of the MFMAs in source order too:
   // where register pressure makes the compiler drop the scheduling hint and
   // keep source order, each MFMA would otherwise wait a full LDS round trip.
-  // element offsets of the phase-1 operand reads inside a tile, whole (row
-  // and swizzled chunk): the compiler would otherwise keep the parts apart
-  // and spend two vector instructions per read on joining them
+  // byte offsets of the phase-1 operand reads inside a tile, whole (row and
+  // swizzled chunk, scaled to bytes): the compiler would otherwise keep the
+  // parts apart, or the element offset, and spend vector instructions on
+  // every read joining or scaling them
   int p1off[NS][2];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      p1off[s][t] = QuadRows<DH>::off(t * 32 + l32, 2 * s + g);
+      p1off[s][t] = 2 * QuadRows<DH>::off(t * 32 + l32, 2 * s + g);
       asm volatile("" : "+v"(p1off[s][t]));
     }
   auto p1read = [&](const uint16_t* A, int s, int t) {
     op8 o;
-    o.v = *(const u32x4_t*)(A + p1off[s][t]);
+    o.v = *(const u32x4_t*)((const char*)A + p1off[s][t]);
     return o;
   };
   auto phase1 = [&](const uint16_t* A, f32x16_t (&x)[2]) {
