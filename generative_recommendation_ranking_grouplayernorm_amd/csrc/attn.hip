@@ -271,14 +271,16 @@ struct VtLoad {
 };
 
 // Global loads of one 64-key V tile for V^T: 4 rows (keys 4kq..4kq+3) x 16
-// bytes (dh 8c..8c+7).
+// bytes (dh 8c..8c+7).  tid < 256 (four waves), so c < 16: with DH = 128
+// every thread has a chunk, which is stated at compile time so that the
+// loads are not wrapped in lane-masked branches.
 template <int DH>
 __device__ __forceinline__ void vt_gload(VtLoad<DH>& L, const uint16_t* __restrict__ V, int64_t ld, int k0,
                                          int rlim, int col0, int tid) {
   const int lane = tid & 63, w = tid >> 6;
   L.kq = lane & 15;
   L.c = 4 * w + 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
-  L.on = L.c < DH / 8;
+  L.on = DH / 8 >= 16 || L.c < DH / 8;
   const __amdgpu_buffer_rsrc_t rs = rows_rsrc(V, ld, k0, rlim, col0);
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -955,8 +957,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   // rows (and their timestamps) of stage j live in buffer j % 4, dO rows in
   // buffer j % 3.
   struct Smem {
-    uint16_t Qs[4][QuadRows<DH>::SIZE];
     uint16_t Ds[3][QuadRows<DH>::SIZE];
+    uint16_t Qs[4][QuadRows<DH>::SIZE];
     uint32_t Fx[2][4][32 * 16 * 2];  // per stage parity and group: 2 x 16 x 32 lanes
     int64_t Tq[4][KV_BQ];            // query timestamps of the stage
   };
@@ -1120,6 +1122,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
       for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], tra.get(Bt, u, c), acc[c]);
     pipeline_lds2_mfma<4 * NC, 8>();
   };
+  // Stage buffer j of a tile array as a byte offset the compiler cannot see
+  // through: otherwise it strength-reduces the rotating buffer index into
+  // per-lane base registers that it advances by one more vector add each
+  // per iteration.
+  auto stage_tile = [&](const uint16_t* t0, int j) {
+    int off = j * (int)(QuadRows<DH>::SIZE * sizeof(uint16_t));
+    asm volatile("" : "+s"(off));
+    return (const uint16_t*)((const char*)t0 + off);
+  };
   if (producer) {
     // one loop per mask variant, so that the mask-free loop keeps its
     // registers to itself
@@ -1134,7 +1145,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
         silu_terms_rows_queries<T, decltype(masked)::value, A1>(x, w, Fx[it & 1][grp], lane, kexp, alpha, q0, kj, g,
                                                              s_end, r_end, Tq[qb], tk);
         swrite(nqb);
-        phase2(w, Ds[it % 3]);
+        phase2(w, stage_tile(Ds[0], it % 3));
         __syncthreads();
       }
     };
@@ -1152,7 +1163,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
       const int st = it - 1, buf = st % 3, nbuf = (it + 1) % 3, q0 = qlo + st * KV_BQ;
       gload(qlo + (it + 1) * KV_BQ);  // past the query range: zeros, never used
       keep_loads_early(it, nbuf);
-      if (it >= 2) phase2(wp, Qs[(st - 1) & 3]);
+      if (it >= 2) phase2(wp, stage_tile(Qs[0], (st - 1) & 3));
       f32x16_t x[2];
       phase1(Ds[buf], x);
       swrite(nbuf);
