@@ -87,7 +87,7 @@ def kernel_work(T, d, P, ds_bytes):
     return {
         "attn_fwd": ("mfma", 4 * d * P),
         "attn_bwd_dkdv": ("mfma", 6 * d * P),   # dV, dA = dO V^T, dK
-        # dQ = dS K from stored dS: streams dS, reads K and the Q pre-activation, writes dQ
+        # dQ = dS K from stored dS: streams dS, reads K and the SiLU' factor of Q, writes dQ
         "attn_bwd_dq": ("hbm", ds_bytes + 3 * T * d * e),
         "gemm_uqkv_silu": ("mfma", 8 * T * d * d),
         "gemm_out_resid": ("mfma", 2 * T * d * d),
