@@ -138,12 +138,21 @@ def _per_dispatch(rows, counter):
     return out
 
 
-def attn_source_hash():
-    """Hash of the attention kernels' source: counters taken on other code are stale."""
+def code_hash(text):
+    """SHA-256 of C++ source with comments and whitespace removed: an edit to
+    a comment leaves it unchanged, an edit to the code does not."""
     import hashlib
+    import re
 
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
+def attn_source_hash():
+    """Hash of the attention kernels' code: counters taken on other code are stale."""
     path = os.path.join(ROOT, "generative_recommendation_ranking_grouplayernorm_amd", "csrc", "attn.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    return code_hash(open(path).read())
 
 
 def pmc_summary(fetch_dir, write_dir, probe_mib):

@@ -955,7 +955,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
   // on stage it - 1 (dA, dS) and on stage it - 2 (its dK product, which
   // reads that stage's Q rows), while stage it + 1 is being written.  So Q
   // rows (and their timestamps) of stage j live in buffer j % 4, dO rows in
-  // buffer j % 3.
+  // buffer j % 3.  The dO tiles come first: with DH = 128 the three dO and
+  // four Q tiles end at 48 and 112 KB, so the constant part of every operand
+  // address (a tile's base plus the 16-row steps of the transposed reads,
+  // up to 63 KB) fits the 16-bit offset field of the LDS instructions.
   struct Smem {
     uint16_t Ds[3][QuadRows<DH>::SIZE];
     uint16_t Qs[4][QuadRows<DH>::SIZE];
@@ -1122,10 +1125,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_mfma(
       for (int c = 0; c < NC; ++c) acc[c] = mfma32<T>(w[u], tra.get(Bt, u, c), acc[c]);
     pipeline_lds2_mfma<4 * NC, 8>();
   };
-  // Stage buffer j of a tile array as a byte offset the compiler cannot see
-  // through: otherwise it strength-reduces the rotating buffer index into
-  // per-lane base registers that it advances by one more vector add each
-  // per iteration.
+  // Stage buffer j of a tile array, offset by a scalar byte count the
+  // compiler cannot see through: otherwise it strength-reduces the rotating
+  // buffer index into per-lane base registers and spends a vector add per
+  // register and iteration advancing them.
   auto stage_tile = [&](const uint16_t* t0, int j) {
     int off = j * (int)(QuadRows<DH>::SIZE * sizeof(uint16_t));
     asm volatile("" : "+s"(off));
