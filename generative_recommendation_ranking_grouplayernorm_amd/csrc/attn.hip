@@ -383,7 +383,22 @@ __device__ __forceinline__ void wave_store_rows(float* stage, const f32x16_t (&a
 constexpr int F_BQ = 128;
 constexpr int F_BK = 64;
 
-template <typename T, int DH, bool MASKED>
+// As pipeline_lds_mfma, with NV vector-memory loads (the next tile's rows)
+// issued one after each of the first MFMAs, so that the load issue overlaps
+// the MFMAs instead of holding the wave at the top of the tile.
+template <int N, int AHEAD, int NV>
+__device__ __forceinline__ void pipeline_lds_mfma_vmem() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+template <typename T, int DH, bool MASKED, int NV = 0>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt, const int64_t* tsk,
                                          const op8 (&qop)[DH / 16], f32x16_t (&oacc)[DH / 32], int k0, int qi,
                                          int64_t tq, int s_end, int r_end, float kexp, int lane) {
@@ -396,7 +411,8 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vt,
   for (int s = 1; s < DH / 16; ++s)
 #pragma unroll
     for (int t = 0; t < 2; ++t) sacc[t] = mfma32<T>(row_operand<KP>(Ks, t * 32, s, lane), qop[s], sacc[t]);
-  pipeline_lds_mfma<DH / 8, 8>();
+  if (NV > 0) pipeline_lds_mfma_vmem<DH / 8, 8, NV>();
+  else pipeline_lds_mfma<DH / 8, 8>();
   float p[2][16];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -492,7 +508,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   auto gload = [&](int k0) {
     tile_gload_rows<DH, F_BK>(rk, K, ldqkv, k0, hi, hc, tid);
     vt_gload<DH>(rv, V, ldqkv, k0, hi, hc, tid);
-    if (wave == 0) rt = ts_load(ts, k0, hi, lane);
+    rt = ts_load(ts, k0, hi, lane);  // every wave: no branch before the MFMAs
   };
   auto swrite = [&](int buf) {
     tile_swrite_rows<DH, F_BK, KP>(Ks[buf], rk, tid);
@@ -508,10 +524,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(
   const int mid = max(it0, min(it1, nfull));
   for (int it = it0; it < mid; ++it) {
     const int buf = (it - it0) & 1, k0 = lo + it * F_BK;
-    const bool more = it + 1 < it1;
-    if (more) gload(lo + kr.tile(it + 1) * F_BK);
-    fwd_tile<T, DH, false>(Ks[buf], Vt[buf], Tk[buf], qop, oacc, k0, qi, tq, s_end, r_end, kexp, lane);
-    if (more) swrite(buf ^ 1);
+    // unconditional, so that the loads share the MFMAs' scheduling region
+    // and issue between them: past the run they fetch a tile nobody reads
+    // (rows at or beyond the row end read as zero), written to the idle
+    // buffer
+    gload(lo + kr.tile(it + 1) * F_BK);
+    fwd_tile<T, DH, false, 9>(Ks[buf], Vt[buf], Tk[buf], qop, oacc, k0, qi, tq, s_end, r_end, kexp, lane);
+    swrite(buf ^ 1);
     __syncthreads();
   }
   for (int it = mid; it < it1; ++it) {
